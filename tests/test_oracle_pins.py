@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each checks the oracle against an
+independent construction (a recursion, a hand-worked example, an identity, a
+special case with a known answer, or brute force), chosen so that a dropped
+term, a wrong sign or index, or a transposed operand fails one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import rq_oracle as o
+import workloads
+
+
+def _rows(path):
+    out = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            out.append([p.strip() for p in line.split("|")])
+    return out
+
+
+# ---------------------------------------------------------------- Hadamard
+
+def _sylvester(n):
+    """Independent construction: H_1 = [1], H_2n = [[H, H], [H, -H]] / sqrt(2)."""
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]]) / math.sqrt(2.0)
+    return h
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 256, 1024])
+def test_hadamard_matches_sylvester_recursion(n):
+    np.testing.assert_allclose(o.hadamard(n), _sylvester(n), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n", [4, 64, 256, 4096])
+def test_hadamard_orthogonal_symmetric_involution(n):
+    h = o.hadamard(n)
+    eye = np.eye(n)
+    assert np.abs(h @ h.T - eye).max() < 1e-12          # R R^T = I  (SpinQuant OpenReview Q2/A2)
+    assert np.array_equal(h, h.T)
+    assert np.abs(h @ h - eye).max() < 1e-12
+
+
+def test_hadamard_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        o.hadamard(12)
+
+
+def test_hadamard_worked_example(golden_dir):
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "worked_examples.txt"))}
+    x = np.array(rows["hadamard4"][1].split(), float)
+    want = np.array(rows["hadamard4"][2].split(), float)
+    np.testing.assert_array_equal(x @ o.hadamard(4), want)
+
+
+def test_hadamard_special_cases():
+    n = 256
+    h = o.hadamard(n)
+    # e_i . H = row i: every entry +-1/sqrt(n), so min-max codes are all +-7
+    e = np.zeros((1, n)); e[0, 37] = 1.0
+    q, s, _ = o.quantize_sym(e @ h)
+    assert np.all(np.abs(q) == 7) and np.isclose(s[0], np.float32(1 / 16 / 7))
+    # c * ones . H = c sqrt(n) e_0: one code +-7, the rest 0
+    c = 3.0
+    q, s, _ = o.quantize_sym(np.full((1, n), c) @ h)
+    assert q[0, 0] == 7 and not np.any(q[0, 1:])
+    # a single outlier of size m spreads to +-m/sqrt(n) on every channel
+    m = 50.0
+    x = np.zeros((1, n)); x[0, 5] = m
+    np.testing.assert_allclose(np.abs(x @ h), m / 16.0, rtol=0, atol=1e-12)
+
+
+def test_rotation_preserves_norm_and_rmsnorm_invariance():
+    """||x R|| = ||x|| and RMSNorm(X) = RMSNorm(X Q^T) Q ("QuaRot & SpinQuant"
+    blog, section 1, with RMSNorm taken as x / ||x|| per row)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((8, 256)) * 3
+    x[:, 7] *= 40
+
+    def rmsnorm(a, eps=0.0):
+        return a / np.sqrt(np.sum(a * a, axis=1, keepdims=True) + eps)
+
+    for q in (o.hadamard(256), o.gsr_rotation(256, 64)):
+        np.testing.assert_allclose(np.linalg.norm(x @ q, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+        np.testing.assert_allclose(rmsnorm(x), rmsnorm(x @ q.T) @ q, rtol=0, atol=1e-13)
+    # a non-orthogonal transform breaks the invariance (FlatQuant's affine is
+    # not a rotation, so it is never relied on there)
+    wl = workloads.get("flat")
+    p1, p2, s = workloads.make_affine(wl, np.random.default_rng(0), 16, 16)
+    r = o.kron_affine(p1, p2, s)
+    assert np.abs(rmsnorm(x) - rmsnorm(x @ np.linalg.inv(r)) @ r).max() > 1e-3
+
+
+# ---------------------------------------------------------------- Walsh / GSR
+
+def test_walsh8_matches_hand_table(golden_dir):
+    table = _rows(os.path.join(golden_dir, "walsh8_sequency.txt"))
+    want = np.array([r[1].split() for r in table], float) / math.sqrt(8)
+    np.testing.assert_allclose(o.walsh_sequency(8), want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 256])
+def test_walsh_sign_changes_are_a_permutation(n):
+    w = o.walsh_sequency(n)
+    assert list(o.sign_changes(w)) == list(range(n))
+    assert np.abs(w @ w.T - np.eye(n)).max() < 1e-12
+
+
+def _bitrev(v, bits):
+    r = 0
+    for _ in range(bits):
+        r = (r << 1) | (v & 1)
+        v >>= 1
+    return r
+
+
+@pytest.mark.parametrize("n", [8, 64])
+def test_walsh_rows_follow_bitreversed_gray_code(n):
+    """Textbook map from sequency s to natural Hadamard index: bitrev(gray(s))."""
+    bits = n.bit_length() - 1
+    w = o.walsh_sequency(n)
+    h = o.hadamard(n)
+    for s in range(n):
+        np.testing.assert_array_equal(w[s], h[_bitrev(s ^ (s >> 1), bits)])
+
+
+def test_gsr_is_block_local():
+    r = o.gsr_rotation(256, 64)
+    x = np.zeros((1, 256)); x[0, 64:128] = np.arange(64) + 1.0
+    y = x @ r
+    assert not np.any(y[0, :64]) and not np.any(y[0, 128:])
+    np.testing.assert_allclose(y[0, 64:128], (np.arange(64) + 1.0) @ o.walsh_sequency(64), atol=1e-12)
+    with pytest.raises(ValueError):
+        o.gsr_rotation(100, 64)
+
+
+# ---------------------------------------------------------------- Kronecker affine
+
+def test_kron_matches_elementwise_definition_and_matrix_form():
+    rng = np.random.default_rng(3)
+    n1, n2 = 4, 8
+    p1 = rng.standard_normal((n1, n1)); p2 = rng.standard_normal((n2, n2))
+    s = rng.uniform(0.5, 2, n1 * n2)
+    x = rng.standard_normal((3, n1 * n2))
+    y = x @ o.kron_affine(p1, p2, s)
+    # brute force: y[j1*n2+j2] = sum_{i1,i2} x[i1*n2+i2] s[.] P1[i1,j1] P2[i2,j2]
+    for t in range(3):
+        for j1 in range(n1):
+            for j2 in range(n2):
+                acc = 0.0
+                for i1 in range(n1):
+                    for i2 in range(n2):
+                        acc += x[t, i1 * n2 + i2] * s[i1 * n2 + i2] * p1[i1, j1] * p2[i2, j2]
+                assert abs(y[t, j1 * n2 + j2] - acc) < 1e-12
+        # per-token matrix form: reshape row-major, P1^T M P2
+        m = (x[t] * s).reshape(n1, n2)
+        np.testing.assert_allclose(y[t], (p1.T @ m @ p2).reshape(-1), atol=1e-12)
+
+
+def test_kron_full_size_matrix_form_and_inverse():
+    inp = workloads.make_inputs("flat", T=8, with_weights=False)
+    p1, p2, s = inp["p1"], inp["p2"], inp["s"]
+    r = o.kron_affine(p1, p2, s)
+    x = inp["x"].astype(np.float64)
+    y = x @ r
+    for t in range(8):
+        m = (x[t] * s.astype(np.float64)).reshape(64, 64)
+        np.testing.assert_allclose(y[t], (p1.astype(np.float64).T @ m @ p2.astype(np.float64)).reshape(-1),
+                                   rtol=1e-12, atol=1e-9)
+    k = np.kron(p1.astype(np.float64), p2.astype(np.float64))
+    kinv = np.kron(np.linalg.inv(p1.astype(np.float64)), np.linalg.inv(p2.astype(np.float64)))
+    assert np.abs(k @ kinv - np.eye(4096)).max() < 1e-10
+    for p in (p1, p2):
+        assert np.linalg.cond(p.astype(np.float64)) <= 1.5
+
+
+@pytest.mark.parametrize("kind", ["hadamard", "gsr", "kron", "none"])
+def test_weight_transform_keeps_the_product(kind):
+    """(X R)(W G)^T = X W^T: computational invariance ("QuaRot & SpinQuant"
+    blog, section 1) and its affine form (FlatQuant article, section 2.3)."""
+    rng = np.random.default_rng(5)
+    K = 256
+    x = rng.standard_normal((6, K)); w = rng.standard_normal((10, K))
+    kw = {}
+    if kind == "gsr":
+        kw = {"block": 64}
+    if kind == "kron":
+        wl = workloads.get("flat")
+        p1, p2, s = workloads.make_affine(wl, rng, 16, 16)
+        kw = {"p1": p1, "p2": p2, "chan_scale": s}
+    r = o.rotation(kind, K, **kw)
+    g = o.weight_transform(kind, K, **kw)
+    ref = x @ w.T
+    got = (x @ r) @ (w @ g).T
+    assert np.abs(got - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- quantizers
+
+def test_symmetric_quantizer_worked_examples(golden_dir):
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "worked_examples.txt"))}
+    for name in ("symq_after_h4", "symq_ties"):
+        x = np.array([rows[name][1].split()], float)
+        want = np.array(rows[name][2].split(), int)
+        q, s, _ = o.quantize_sym(x)
+        np.testing.assert_array_equal(q[0], want)
+    q, s, _ = o.quantize_sym(np.array([[5.0, -1, -2, 0]]))
+    assert s[0] == np.float32(5.0 / 7.0)
+
+
+def test_symmetric_quantizer_properties():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 512)) * rng.uniform(0.01, 100, (64, 1))
+    q, s, pre = o.quantize_sym(x)
+    assert q.min() >= -7 and q.max() <= 7
+    assert np.all(np.abs(q).max(axis=1) == 7)               # min-max uses the full range
+    assert np.abs(pre).max() <= 7 + 1e-6                      # no clamp needed at clip = 1
+    err = np.abs(x - q * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2 * (1 + 1e-6))
+    # clipped: codes saturate at +-7 and the unclipped part keeps the s/2 bound
+    q9, s9, pre9 = o.quantize_sym(x, clip=0.9)
+    np.testing.assert_allclose(s9, (np.float64(np.float32(0.9)) * np.abs(x).max(1) / 7).astype(np.float32))
+    assert q9.min() >= -7 and q9.max() <= 7 and np.abs(pre9).max() > 7
+    inside = np.abs(pre9) <= 7
+    assert np.all(np.abs(x - q9 * s9.astype(np.float64)[:, None])[inside]
+                  <= np.broadcast_to(s9.astype(np.float64)[:, None] / 2 * (1 + 1e-6), x.shape)[inside])
+    # zero row: scale 0, codes 0, no NaN
+    qz, sz, _ = o.quantize_sym(np.zeros((2, 16)))
+    assert not qz.any() and not sz.any()
+
+
+def test_crafted_ties_through_the_rotation():
+    """Rows built as y . H with half-integer y: H is an involution, so the
+    rotated row is y again and the quantizer sees exact .5 ties."""
+    n = 256
+    y = np.zeros((1, n))
+    y[0, :6] = [7.0, 0.5, 1.5, 2.5, -2.5, -3.5]
+    x = y @ o.hadamard(n)
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x)         # exact in fp16
+    r = o.rotate_quant(x16, "hadamard")
+    assert r["scale"][0] == np.float32(1.0)
+    np.testing.assert_array_equal(r["q"][0, :6], [7, 0, 2, 2, -2, -4])
+    assert not r["q"][0, 6:].any()
+
+
+def test_asymmetric_quantizer_worked_and_properties(golden_dir):
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "worked_examples.txt"))}
+    x = np.array([rows["asymq"][1].split()], float)
+    q, s, z, _, _ = o.quantize_asym(x)
+    np.testing.assert_array_equal(q[0], np.array(rows["asymq"][2].split(), int))
+    assert z[0] == 5 and s[0] == np.float32(0.2)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((32, 300)) * 5 + rng.uniform(-3, 3, (32, 1))
+    x[3] = np.abs(x[3])            # all >= 0: lo = 0 -> zero point 0
+    x[4] = -np.abs(x[4])           # all <= 0: hi = 0 -> zero point 15
+    q, s, z, pre, zpre = o.quantize_asym(x)
+    assert q.min() >= 0 and q.max() <= 15 and z.min() >= 0 and z.max() <= 15
+    assert z[3] == 0 and z[4] == 15
+    deq = (q.astype(np.float64) - z[:, None]) * s.astype(np.float64)[:, None]
+    assert np.all(np.abs(deq - x) <= s.astype(np.float64)[:, None] * (1.0 + 1e-6))
+    qz, sz, zz, _, _ = o.quantize_asym(np.zeros((1, 8)))
+    assert not qz.any() and not sz.any() and not zz.any()
+
+
+# ---------------------------------------------------------------- packing, GEMM
+
+def test_pack_worked_example_and_roundtrip(golden_dir):
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "worked_examples.txt"))}
+    q = np.array([rows["pack"][1].split()], int)
+    np.testing.assert_array_equal(o.pack_int4(q)[0], np.array(rows["pack"][2].split(), int))
+    rng = np.random.default_rng(1)
+    qs = rng.integers(-8, 8, (5, 64))
+    np.testing.assert_array_equal(o.unpack_int4(o.pack_int4(qs), signed=True), qs)
+    qu = rng.integers(0, 16, (5, 64))
+    np.testing.assert_array_equal(o.unpack_int4(o.pack_int4(qu), signed=False), qu)
+
+
+def test_int_gemm_matches_bruteforce(golden_dir):
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "worked_examples.txt"))}
+    a, b = [np.array([p.split()], int) for p in rows["dot"][1].split(";")]
+    assert o.int_gemm(a, b)[0, 0] == int(rows["dot"][2])
+    rng = np.random.default_rng(2)
+    for K in (64, 256, 1000):
+        a = rng.integers(-7, 8, (9, K)); b = rng.integers(-7, 8, (13, K))
+        np.testing.assert_array_equal(o.int_gemm(a, b), o.int_gemm_bruteforce(a, b))
+        au = rng.integers(0, 16, (9, K))
+        np.testing.assert_array_equal(o.int_gemm(au, b), o.int_gemm_bruteforce(au, b))
+    big = np.full((1, 4), 2 ** 20);
+    with pytest.raises(OverflowError):
+        o.int_gemm(big, big)
+
+
+def _grid_layer(kind, T=5, N=7, K=256, seed=0):
+    """Inputs that quantize losslessly: rotated rows are integer codes times a
+    power-of-two scale, so the whole pipeline must reproduce X W^T exactly."""
+    rng = np.random.default_rng(seed)
+    kw = {"block": 64} if kind == "gsr" else {}
+    r = o.rotation(kind, K, **kw)
+    qx = rng.integers(-7, 8, (T, K)); qx[:, 0] = 7
+    qw = rng.integers(-7, 8, (N, K)); qw[:, 1] = -7
+    sx = 2.0 ** rng.integers(-4, 2, T); sw = 2.0 ** rng.integers(-8, -4, N)
+    x = (qx * sx[:, None]) @ r.T          # x R = qx sx  (R orthogonal)
+    w = (qw * sw[:, None]) @ r.T          # w R = qw sw
+    return x, w, qx, qw, sx, sw
+
+
+@pytest.mark.parametrize("kind", ["hadamard", "gsr", "none"])
+def test_lossless_pipeline_reproduces_dense_product(kind):
+    x, w, qx, qw, sx, sw = _grid_layer(kind)
+    x16, w16 = x.astype(np.float16), w.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x) and np.array_equal(w16.astype(np.float64), w)
+    kw = {"block": 64} if kind == "gsr" else {}
+    xq = o.rotate_quant(x16, kind, **kw)
+    wq = o.prepare_weights(w16, kind, **kw)
+    np.testing.assert_array_equal(xq["q"], qx)
+    np.testing.assert_array_equal(wq["q"], qw)
+    y = o.linear(xq, wq)["y"]
+    np.testing.assert_array_equal(y, (x @ w.T).astype(np.float16))
+
+
+def test_dequant_equals_product_of_dequantized_operands():
+    rng = np.random.default_rng(4)
+    qx = rng.integers(-7, 8, (6, 128)); qw = rng.integers(-7, 8, (9, 128))
+    sx = rng.uniform(0.1, 2, 6).astype(np.float32); sw = rng.uniform(1e-3, 1e-2, 9).astype(np.float32)
+    dense = (qx * sx.astype(np.float64)[:, None]) @ (qw * sw.astype(np.float64)[:, None]).T
+    np.testing.assert_array_equal(o.dequant_sym(o.int_gemm(qx, qw), sx, sw), dense.astype(np.float16))
+
+
+# ---------------------------------------------------------------- QUIK split
+
+def test_quik_split_identity_and_zero_point_correction():
+    rng = np.random.default_rng(8)
+    K, n_out = 512, 16
+    x = rng.integers(-50, 50, (4, K)).astype(np.float64)
+    w = rng.integers(-50, 50, (6, K)).astype(np.float64)
+    idx = np.sort(rng.choice(K, n_out, replace=False))
+    xn, xo = o.split_outliers(x, idx); wn, wo = o.split_outliers(w, idx)
+    assert xn.shape == (4, K - n_out) and xo.shape == (4, n_out)
+    np.testing.assert_array_equal(xn @ wn.T + xo @ wo.T, x @ w.T)
+    keep = np.setdiff1d(np.arange(K), idx)
+    np.testing.assert_array_equal(xn, x[:, keep])
+    # asymmetric codes: sum_k (q - z) qw = acc - z * rowsum (brute force)
+    q = rng.integers(0, 16, (4, 64)); z = rng.integers(0, 16, 4)
+    qw = rng.integers(-7, 8, (6, 64))
+    brute = o.int_gemm_bruteforce(q - z[:, None], qw)
+    acc = o.int_gemm(q, qw).astype(np.int64)
+    np.testing.assert_array_equal(acc - z[:, None] * qw.sum(1)[None, :], brute)
+
+
+def test_quik_mixed_pipeline_small():
+    """Asymmetric INT4 part + FP16 outlier part against the dense product,
+    within the quantization error bound of the INT4 part."""
+    inp = workloads.make_inputs("quik_prefill", T=24, K=512, N=40)
+    x, w, idx = inp["x"], inp["w"], inp["outlier_ch"][:32]
+    xq = o.rotate_quant(x, "none", asym=True, outlier_idx=idx)
+    wq = o.prepare_weights(w, "none", outlier_idx=idx)
+    y = o.linear(xq, wq)["y"].astype(np.float64)
+    xn, xo = o.split_outliers(x.astype(np.float64), idx)
+    wn, wo = o.split_outliers(w.astype(np.float64), idx)
+    xd = (xq["q"].astype(np.float64) - xq["zero"][:, None]) * xq["scale"].astype(np.float64)[:, None]
+    wd = wq["q"] * wq["scale"].astype(np.float64)[:, None]
+    exact = xd @ wd.T + xo @ wo.T
+    np.testing.assert_allclose(y, exact, rtol=1e-3, atol=1e-3)
+    # the quantization error of each operand is bounded by half a step
+    assert np.all(np.abs(xd - xn) <= xq["scale"].astype(np.float64)[:, None] * 0.5 * (1 + 1e-6) + 1e-12)
+    assert np.all(np.abs(wd - wn) <= wq["scale"].astype(np.float64)[:, None] * 0.5 * (1 + 1e-6) + 1e-12)
+
+
+def test_outlier_selection_recovers_generator_columns():
+    inp = workloads.make_inputs("quik_prefill", T=64, with_weights=False)
+    np.testing.assert_array_equal(o.select_outlier_columns(inp["x"], 256), inp["outlier_ch"])
+
+
+# ---------------------------------------------------------------- statistical sanity
+
+def test_rotation_flattens_outliers_and_quip_bound():
+    inp = workloads.make_inputs("llama7b", T=64, N=64)
+    x = inp["x"].astype(np.float64)
+    xr = x @ o.hadamard(4096)
+
+    def ratio(a):
+        return np.max(np.abs(a), axis=1) / np.sqrt(np.mean(a * a, axis=1))
+    assert np.all(ratio(xr) < ratio(x))
+    # QuIP# incoherence bound quoted in the SpinQuant OpenReview discussion:
+    # max |W_ij| <= mu ||W||_F / sqrt(mn), mu = 2 log(4 mn / delta)
+    w = inp["w"].astype(np.float64) @ o.hadamard(4096)
+    m, n = w.shape
+    delta = 0.01
+    mu = 2 * math.log(4 * m * n / delta)
+    assert np.abs(w).max() <= mu * np.linalg.norm(w) / math.sqrt(m * n)
+
+
+def test_affine_pipeline_small():
+    """FlatQuant path end to end: codes dequantize to X R and W R^{-T} within
+    half a step (clipped entries aside), and (X R)(W R^{-T})^T = X W^T."""
+    inp = workloads.make_inputs("flat", T=12, K=256, N=20, n1=16, n2=16)
+    x, w = inp["x"], inp["w"]
+    kw = dict(p1=inp["p1"], p2=inp["p2"], chan_scale=inp["s"])
+    xq = o.rotate_quant(x, "kron", clip=0.95, **kw)
+    wq = o.prepare_weights(w, "kron", **kw)
+    xr = x.astype(np.float64) @ o.rotation("kron", 256, **kw)
+    wr = w.astype(np.float64) @ o.weight_transform("kron", 256, **kw)
+    np.testing.assert_allclose(xq["xr"], xr, rtol=1e-13, atol=1e-12)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(xr @ wr.T - ref).max() <= 1e-10 * np.abs(ref).max()
+    sx = xq["scale"].astype(np.float64)[:, None]
+    inside = np.abs(xq["pre"]) <= 7
+    assert np.all((np.abs(xq["q"] * sx - xr) <= sx / 2 * (1 + 1e-6))[inside])
+    assert np.all(np.abs(xq["q"][~inside]) == 7)
+    sw = wq["scale"].astype(np.float64)[:, None]
+    assert np.all(np.abs(wq["q"] * sw - wr) <= sw / 2 * (1 + 1e-6))
+    y = o.linear(xq, wq)["y"]
+    np.testing.assert_array_equal(y, ((xq["q"] * sx) @ (wq["q"] * sw).T).astype(np.float16))
