@@ -1,0 +1,178 @@
+/*
+ * rq.h -- C ABI of the online-rotation + W4A4 linear library for MI355X (gfx950).
+ *
+ * The library computes the quantized linear layer that the rotation-based
+ * 4-bit methods share:
+ *
+ *     Y = dequant( Q(X . R) . Q(W . R^{-T})^T )   [+ X_out . W_out^T]
+ *
+ * R is an online per-token transform: a normalized Walsh-Hadamard transform
+ * ("QuaRot & SpinQuant" blog, section 2), a block-diagonal sequency-ordered
+ * Walsh rotation ("Grouped Sequency-arranged Rotation" abstract), or a
+ * Kronecker affine transform with channel scaling and clipping (FlatQuant
+ * article, section 2.3).  Q is per-token INT4 quantization; the product is an
+ * INT4 x INT4 GEMM with INT32 accumulation, then per-token x per-channel
+ * dequantization, with QUIK's FP16 outlier columns added (QUIK blog, "QUIK
+ * quantization" parts 1 and 4).
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronizes; each call only enqueues
+ *     kernels on `stream` (a hipStream_t passed as void*, NULL = default).
+ *   - Arguments are checked on the host before anything is launched.  A
+ *     failed check returns an error code, launches nothing and writes nothing.
+ *     Kernel launch failures return RQ_EHIP.  rq_last_error() then holds a
+ *     message (thread-local).  No exception or abort crosses the ABI.
+ *   - Matrices are row-major.  fp16 is IEEE binary16.  Packed INT4 rows hold
+ *     two codes per byte: element 2j in the low nibble, 2j+1 in the high
+ *     nibble.  Symmetric codes are 4-bit two's complement in [-7, 7];
+ *     asymmetric codes are unsigned in [0, 15].
+ *   - Data pointers must be 16-byte aligned (fp32/int32 vectors: 4-byte).
+ *   - Rounding is round-half-to-even throughout.
+ *   - Calls on one stream run in order; the library keeps no state between
+ *     calls except the thread-local error string.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RQ_ABI_VERSION 1
+
+typedef enum {
+  RQ_OK = 0,
+  RQ_EINVAL = 1, /* null pointer, unknown enum value, negative size, bad ratio */
+  RQ_ESHAPE = 2, /* size or transform the library does not support           */
+  RQ_EALIGN = 3, /* pointer or leading dimension not aligned / too small       */
+  RQ_EHIP = 4    /* a HIP launch or runtime call failed                        */
+} rq_status;
+
+typedef enum {
+  RQ_ROT_NONE = 0,     /* identity (QUIK: no rotation)                        */
+  RQ_ROT_HADAMARD = 1, /* full normalized Walsh-Hadamard over K, natural order */
+  RQ_ROT_GSR = 2,      /* blockdiag of sequency-ordered Walsh blocks           */
+  RQ_ROT_KRON = 3      /* diag(s) . (P1 kron P2)                               */
+} rq_rot_kind;
+
+/* Online transform R, applied to each row on the right: x' = x . R.
+ *   HADAMARD  R = H_K, H[i][j] = (-1)^popcount(i&j) / sqrt(K).
+ *             K a power of two, 64 <= K <= 32768.
+ *   GSR       R = blockdiag(Wal_b, ..., Wal_b), Wal_b row s = the H_b row
+ *             with exactly s sign changes.  b = `block`, a power of two,
+ *             2 <= b <= 256, K % b == 0, K <= 32768.
+ *   KRON      R = diag(chan_scale) . (P1 kron P2) with numpy's Kronecker
+ *             index convention; per row, x' reshaped [n1, n2] = P1^T M P2 with
+ *             M = (x * chan_scale) reshaped row-major.  K == n1 * n2,
+ *             1 <= n1, n2 <= 64.  p1: fp32 [n1, n1], p2: fp32 [n2, n2],
+ *             chan_scale: fp32 [K] or NULL (all ones).
+ * Rotations (kind != NONE) require n_out == 0 in the quantizer descriptor. */
+typedef struct {
+  int32_t kind;
+  int32_t block;
+  int32_t n1, n2;
+  const float *p1;
+  const float *p2;
+  const float *chan_scale;
+} rq_rot_desc;
+
+/* Per-row quantizer.
+ *   asymmetric == 0: scale = fp32(clip_ratio * max|x'| / 7),
+ *                    code = clamp(rne(x'/scale), -7, 7)
+ *                    (SpinQuant OpenReview, first reviewer Q1/A1: min-max onto
+ *                    +-(2^{N-1}-1); FlatQuant article section 2.3: clipping).
+ *   asymmetric == 1: lo = min(min x, 0), hi = max(max x, 0),
+ *                    scale = fp32((hi - lo) / 15), zero = clamp(rne(-lo/scale), 0, 15),
+ *                    code = clamp(rne(x/scale) + zero, 0, 15)
+ *                    (QUIK blog part 1: asymmetric per-token dynamic).
+ *                    clip_ratio must be 1.
+ *   A row whose range is 0 gets scale 0, zero 0 and all codes 0.
+ *   outlier_idx: device int32 [n_out], the columns kept in fp16 (QUIK blog
+ *   parts 1 and 3).  Must be distinct and in [0, K); order does not matter:
+ *   outlier columns are emitted in ascending column order, the other K - n_out
+ *   columns keep their relative order.  Violating this gives unspecified
+ *   values but never an out-of-bounds access.  n_out = 0: no split. */
+typedef struct {
+  int32_t asymmetric;
+  float clip_ratio;
+  const int32_t *outlier_idx;
+  int32_t n_out;
+} rq_quant_desc;
+
+/* rq_rotate_quant -- online transform + per-token INT4 quantization + packing.
+ *   x        fp16 [T, ldx] (row t starts at x + t*ldx elements; ldx >= K, ldx % 8 == 0)
+ *   q        out uint8 [T, (K - n_out)/2] packed codes (dense rows)
+ *   scale    out fp32 [T]
+ *   zero     out int32 [T] (asymmetric only; NULL for symmetric)
+ *   code_sum out int32 [T] sum of each row's codes (NULL to skip); the
+ *            weight side uses it for the asymmetric zero-point correction
+ *   x_out    out fp16 [T, n_out] outlier columns (NULL iff n_out == 0)
+ * T == 0 is a no-op.  (K - n_out) must be a positive multiple of 64 (QUIK's
+ * 8192 - 256 = 7936 qualifies). */
+rq_status rq_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx,
+                          const rq_rot_desc *rot, const rq_quant_desc *qd,
+                          uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum,
+                          void *x_out, void *stream);
+
+/* rq_prepare_weights -- the offline weight side: W' = W . R^{-T}, then
+ * per-output-channel symmetric INT4 (FlatQuant article section 3: per-channel
+ * symmetric weights; "QuaRot & SpinQuant" blog section 1: the rotation folds
+ * into the weights).  For HADAMARD/GSR/NONE, R^{-T} = R.  For KRON,
+ * R^{-T} = diag(1/s) . (P1^{-T} kron P2^{-T}); the inverses are computed on
+ * the GPU in fp64 (Gauss-Jordan, partial pivoting) into `workspace`.
+ *   w        fp16 [N, ldw], qd: symmetric only, clip_ratio as for activations,
+ *            outlier_idx/n_out select the fp16 columns (written to w_out [N, n_out])
+ *   qw       out uint8 [N, (K - n_out)/2], sw out fp32 [N],
+ *   w_rowsum out int32 [N] sum of each row's codes (NULL to skip)
+ *   workspace device buffer of rq_prepare_weights_workspace_bytes(rot) bytes
+ *            (may be NULL when that is 0).  A singular factor yields
+ *            unspecified (non-finite) values, not an error. */
+int64_t rq_prepare_weights_workspace_bytes(const rq_rot_desc *rot);
+rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw,
+                             const rq_rot_desc *rot, const rq_quant_desc *qd,
+                             uint8_t *qw, float *sw, int32_t *w_rowsum, void *w_out,
+                             void *workspace, int64_t workspace_bytes, void *stream);
+
+/* rq_w4a4_linear -- y[t][n] = fp16( acc[t][n] * sx[t] * sw[n] ),
+ * acc = sum_k qx[t][k] * qw[n][k] in INT32 (QUIK blog part 4), symmetric codes.
+ *   qx uint8 [T, K/2], sx fp32 [T], qw uint8 [N, K/2], sw fp32 [N],
+ *   y fp16 [T, ldy] (ldy >= N, ldy % 8 == 0).  K % 64 == 0, K > 0, N >= 1.
+ * The scale product is formed in fp32 and rounded once to fp16. */
+rq_status rq_w4a4_linear(const uint8_t *qx, const float *sx, int64_t T, int64_t K,
+                         const uint8_t *qw, const float *sw, int64_t N,
+                         void *y, int64_t ldy, void *stream);
+
+/* rq_mixed_outlier_linear -- QUIK's mixed-precision linear (QUIK blog part 1):
+ *   y[t][n] = fp16( (acc[t][n] - zx[t]*w_rowsum[n]) * sx[t] * sw[n]
+ *                   + sum_j x_out[t][j] * w_out[n][j] )
+ *   qx uint8 [T, K_int/2] asymmetric codes (zx int32 [T]); if zx is NULL the
+ *   codes are symmetric and w_rowsum may be NULL.  qw/sw/w_rowsum as written by
+ *   rq_prepare_weights.  x_out fp16 [T, n_out], w_out fp16 [N, n_out]
+ *   (n_out % 32 == 0, may be 0 with NULL pointers).  The outlier product
+ *   accumulates in fp32 on FP16 matrix cores; one fp16 rounding at the end. */
+rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int32_t *zx,
+                                  int64_t T, int64_t K_int,
+                                  const uint8_t *qw, const float *sw, const int32_t *w_rowsum,
+                                  int64_t N, const void *x_out, const void *w_out, int32_t n_out,
+                                  void *y, int64_t ldy, void *stream);
+
+/* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
+ * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
+ * otherwise signed.  acc int32 [T, ldacc], ldacc >= N, ldacc % 4 == 0. */
+rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K,
+                           const uint8_t *qw, int64_t N, int32_t *acc, int64_t ldacc,
+                           void *stream);
+
+const char *rq_status_string(rq_status s);
+const char *rq_last_error(void);
+int rq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */

@@ -1,0 +1,219 @@
+"""Online rotation + W4A4 linear for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over librq.so (the C ABI in include/rq.h).  It only
+marshals arguments: torch supplies device memory and the current HIP stream,
+every computation runs in the library's HIP kernels.  There is no fallback:
+if librq.so is missing or a tensor is not on the GPU, the call raises.
+
+Entry points carry the C names:
+    rq_rotate_quant, rq_prepare_weights, rq_w4a4_linear,
+    rq_mixed_outlier_linear, rq_w4a4_gemm_i32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librq.so")
+
+RQ_OK, RQ_EINVAL, RQ_ESHAPE, RQ_EALIGN, RQ_EHIP = range(5)
+ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
+
+__all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
+           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_w4a4_gemm_i32",
+           "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
+
+# Every symbol include/rq.h declares.
+EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
+           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_w4a4_gemm_i32",
+           "rq_status_string", "rq_last_error", "rq_abi_version")
+
+
+class RqError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class _RotDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("block", ctypes.c_int32), ("n1", ctypes.c_int32),
+                ("n2", ctypes.c_int32), ("p1", ctypes.c_void_p), ("p2", ctypes.c_void_p),
+                ("chan_scale", ctypes.c_void_p)]
+
+
+class _QuantDesc(ctypes.Structure):
+    _fields_ = [("asymmetric", ctypes.c_int32), ("clip_ratio", ctypes.c_float),
+                ("outlier_idx", ctypes.c_void_p), ("n_out", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librq.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m online_rotation_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.rq_rotate_quant.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
+                                      ctypes.POINTER(_QuantDesc), vp, vp, vp, vp, vp, vp]
+        L.rq_prepare_weights_workspace_bytes.argtypes = [ctypes.POINTER(_RotDesc)]
+        L.rq_prepare_weights_workspace_bytes.restype = i64
+        L.rq_prepare_weights.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
+                                         ctypes.POINTER(_QuantDesc), vp, vp, vp, vp, vp, i64, vp]
+        L.rq_w4a4_linear.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i64, vp]
+        L.rq_mixed_outlier_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp,
+                                              i32, vp, i64, vp]
+        L.rq_w4a4_gemm_i32.argtypes = [vp, i32, i64, i64, vp, i64, vp, i64, vp]
+        for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear",
+                   "rq_mixed_outlier_linear", "rq_w4a4_gemm_i32"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.rq_status_string.argtypes = [ctypes.c_int]
+        L.rq_status_string.restype = ctypes.c_char_p
+        L.rq_last_error.restype = ctypes.c_char_p
+        L.rq_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def rq_status_string(s: int) -> str:
+    return lib().rq_status_string(s).decode()
+
+
+def rq_last_error() -> str:
+    return lib().rq_last_error().decode()
+
+
+def rq_abi_version() -> int:
+    return lib().rq_abi_version()
+
+
+def _check(status: int, fn: str):
+    if status != RQ_OK:
+        raise RqError(status, fn, rq_last_error() or rq_status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("rq: tensors must live on the GPU (no CPU path exists)")
+
+
+@dataclass
+class Rotation:
+    """Online transform descriptor (tensors are kept alive by this object)."""
+    kind: str = "none"
+    block: int = 0
+    p1: object = None          # fp32 [n1, n1] device tensor (kron)
+    p2: object = None          # fp32 [n2, n2] device tensor (kron)
+    chan_scale: object = None  # fp32 [K] device tensor or None (kron)
+
+    def desc(self) -> _RotDesc:
+        n1 = int(self.p1.shape[0]) if self.p1 is not None else 0
+        n2 = int(self.p2.shape[0]) if self.p2 is not None else 0
+        return _RotDesc(ROT_KINDS[self.kind], int(self.block), n1, n2, _ptr(self.p1),
+                        _ptr(self.p2), _ptr(self.chan_scale))
+
+
+def _qdesc(asym: bool, clip: float, outlier_idx):
+    n_out = 0 if outlier_idx is None else int(outlier_idx.numel())
+    return _QuantDesc(1 if asym else 0, float(clip), _ptr(outlier_idx), n_out), n_out
+
+
+def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
+                    outlier_idx=None, code_sum: bool = False, out: dict | None = None) -> dict:
+    """x fp16 [T, K] (row stride x.stride(0)) -> dict(q, scale, zero, code_sum, x_out)."""
+    import torch
+    _gpu(x, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
+    T, K = x.shape
+    qd, n_out = _qdesc(asym, clip, outlier_idx)
+    dev = x.device
+    o = dict(out or {})
+    o.setdefault("q", torch.empty((T, (K - n_out) // 2), dtype=torch.uint8, device=dev))
+    o.setdefault("scale", torch.empty((T,), dtype=torch.float32, device=dev))
+    o.setdefault("zero", torch.empty((T,), dtype=torch.int32, device=dev) if asym else None)
+    o.setdefault("code_sum", torch.empty((T,), dtype=torch.int32, device=dev) if code_sum else None)
+    o.setdefault("x_out", torch.empty((T, n_out), dtype=torch.float16, device=dev) if n_out else None)
+    rd = rot.desc()
+    st = lib().rq_rotate_quant(_ptr(x), T, K, x.stride(0), ctypes.byref(rd), ctypes.byref(qd),
+                               _ptr(o["q"]), _ptr(o["scale"]), _ptr(o["zero"]),
+                               _ptr(o["code_sum"]), _ptr(o["x_out"]), _stream(dev))
+    _check(st, "rq_rotate_quant")
+    return o
+
+
+def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None) -> dict:
+    """w fp16 [N, K] -> dict(q, scale, rowsum, w_out): rotated, per-channel INT4."""
+    import torch
+    _gpu(w, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
+    N, K = w.shape
+    qd, n_out = _qdesc(False, clip, outlier_idx)
+    dev = w.device
+    rd = rot.desc()
+    ws_bytes = lib().rq_prepare_weights_workspace_bytes(ctypes.byref(rd))
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    o = {"q": torch.empty((N, (K - n_out) // 2), dtype=torch.uint8, device=dev),
+         "scale": torch.empty((N,), dtype=torch.float32, device=dev),
+         "rowsum": torch.empty((N,), dtype=torch.int32, device=dev),
+         "w_out": torch.empty((N, n_out), dtype=torch.float16, device=dev) if n_out else None}
+    st = lib().rq_prepare_weights(_ptr(w), N, K, w.stride(0), ctypes.byref(rd), ctypes.byref(qd),
+                                  _ptr(o["q"]), _ptr(o["scale"]), _ptr(o["rowsum"]),
+                                  _ptr(o["w_out"]), _ptr(ws), ws_bytes, _stream(dev))
+    _check(st, "rq_prepare_weights")
+    o["_workspace"] = ws   # keep alive until the stream has consumed it
+    return o
+
+
+def rq_w4a4_linear(qx, sx, qw, sw, out=None):
+    """fp16 y [T, N] = acc * sx[t] * sw[n] from packed symmetric codes."""
+    import torch
+    _gpu(qx, sx, qw, sw)
+    T, Kb = qx.shape
+    N = qw.shape[0]
+    y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=qx.device)
+    st = lib().rq_w4a4_linear(_ptr(qx), _ptr(sx), T, 2 * Kb, _ptr(qw), _ptr(sw), N, _ptr(y),
+                              y.stride(0), _stream(qx.device))
+    _check(st, "rq_w4a4_linear")
+    return y
+
+
+def rq_mixed_outlier_linear(qx, sx, zx, qw, sw, w_rowsum, x_out=None, w_out=None, out=None):
+    """QUIK mixed linear: dequantized INT4 part + fp16 outlier product."""
+    import torch
+    _gpu(qx, sx, zx, qw, sw, w_rowsum, x_out, w_out)
+    T, Kb = qx.shape
+    N = qw.shape[0]
+    n_out = 0 if x_out is None else int(x_out.shape[1])
+    y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=qx.device)
+    st = lib().rq_mixed_outlier_linear(_ptr(qx), _ptr(sx), _ptr(zx), T, 2 * Kb, _ptr(qw),
+                                       _ptr(sw), _ptr(w_rowsum), N, _ptr(x_out), _ptr(w_out),
+                                       n_out, _ptr(y), y.stride(0), _stream(qx.device))
+    _check(st, "rq_mixed_outlier_linear")
+    return y
+
+
+def rq_w4a4_gemm_i32(qx, qw, x_unsigned: bool = False, out=None):
+    """Raw INT32 accumulator [T, N] (for bit-exact tests)."""
+    import torch
+    _gpu(qx, qw)
+    T, Kb = qx.shape
+    N = qw.shape[0]
+    acc = out if out is not None else torch.empty((T, N), dtype=torch.int32, device=qx.device)
+    st = lib().rq_w4a4_gemm_i32(_ptr(qx), 1 if x_unsigned else 0, T, 2 * Kb, _ptr(qw), N,
+                                _ptr(acc), acc.stride(0), _stream(qx.device))
+    _check(st, "rq_w4a4_gemm_i32")
+    return acc

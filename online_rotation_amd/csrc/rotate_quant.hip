@@ -1,0 +1,541 @@
+// rotate_quant.hip -- online transform + per-token INT4 quantization (gfx950).
+//
+// Kernels:
+//   fwht4096_quant   one wavefront per 4096-wide row: Walsh-Hadamard
+//                    butterflies ("QuaRot & SpinQuant" blog, section 2) over
+//                    the full row or within sequency-ordered Walsh blocks
+//                    ("Grouped Sequency-arranged Rotation" abstract), min-max
+//                    symmetric INT4 (SpinQuant OpenReview, Q1/A1), packing.
+//   rowlds_quant     one workgroup per row, the row staged in LDS: any
+//                    power-of-two Hadamard / GSR span, the identity with
+//                    QUIK's fp16 outlier split and asymmetric per-token codes
+//                    (QUIK blog, "QUIK quantization" parts 1 and 3).
+//   kron_quant       FlatQuant's Kronecker affine transform with channel
+//                    scaling and clipping (FlatQuant article, section 2.3).
+//   kron_inverse_t   fp64 Gauss-Jordan inverse-transpose of a Kronecker
+//                    factor, for the weight side of the affine transform.
+#include "rq_device.h"
+#include "rq_kernels.h"
+
+namespace rq {
+
+// ---------------------------------------------------------------------------
+// fwht4096_quant
+//
+// Index bits of a 4096-element row are split between the 64 lanes and the 64
+// registers of each lane.  Loads are coalesced (lane l, vector v holds
+// elements v*512 + l*8 + e), so registers first cover bits {0,1,2,9,10,11};
+// one LDS transpose moves bits {3..8} into registers for the remaining
+// butterflies, a second transpose brings the row back to the load layout for
+// quantization and contiguous packed stores.
+//
+// LDS word address of element i: bit 2 is flipped by bit 5 and every 512
+// elements are padded by 8 words, which makes the 128-bit row accesses and
+// the 32-bit transposed accesses free of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int kF4096Waves = 4;
+constexpr int kF4096Words = 4096 + 8 * 8;
+
+__device__ __forceinline__ int f4096_addr(int i) {
+  return (i ^ (((i >> 5) & 1) << 2)) + ((i >> 9) << 3);
+}
+
+// Butterfly along register-index bit `rb` of a[64].
+template <int RB>
+__device__ __forceinline__ void reg_stage(float *a) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (i & (1 << RB)) continue;
+    const float u = a[i], w = a[i | (1 << RB)];
+    a[i] = u + w;
+    a[i | (1 << RB)] = u - w;
+  }
+}
+
+__device__ __forceinline__ int bitrev(int v, int bits) {
+  return (int)(__builtin_bitreverse32((uint32_t)v) >> (32 - bits));
+}
+
+template <bool GSR>
+__global__ __launch_bounds__(256) void fwht4096_quant(const __half *__restrict__ x, int64_t T,
+                                                      int64_t ldx, uint8_t *__restrict__ q,
+                                                      float *__restrict__ scale,
+                                                      int32_t *__restrict__ code_sum, float clip,
+                                                      int span_log2, float norm) {
+  __shared__ __align__(16) float lds[kF4096Waves][kF4096Words];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kF4096Waves + wave;
+  if (t >= T) return;  // whole wavefront leaves; no workgroup barrier below
+  float *L = lds[wave];
+  const __half *row = x + t * ldx;
+
+  float a[64];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(row + v * 512 + lane * 8);
+    h8_to_f32(raw, a + v * 8);
+  }
+  // phase 1: idx bits 0,1,2 (register bits 0..2) and 9,10,11 (register bits 3..5)
+  if (span_log2 > 0) reg_stage<0>(a);
+  if (span_log2 > 1) reg_stage<1>(a);
+  if (span_log2 > 2) reg_stage<2>(a);
+  if (span_log2 > 9) reg_stage<3>(a);
+  if (span_log2 > 10) reg_stage<4>(a);
+  if (span_log2 > 11) reg_stage<5>(a);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+#pragma unroll
+    for (int e0 = 0; e0 < 8; e0 += 4) {
+      const int i = v * 512 + lane * 8 + e0;
+      *reinterpret_cast<float4 *>(L + f4096_addr(i)) =
+          make_float4(a[v * 8 + e0], a[v * 8 + e0 + 1], a[v * 8 + e0 + 2], a[v * 8 + e0 + 3]);
+    }
+  }
+  wave_lds_sync();
+  // phase 2: idx bits 3..8 in registers; lane holds bits {0,1,2} and {9,10,11}
+  const int base2 = ((lane >> 3) << 9) | (lane & 7);
+#pragma unroll
+  for (int r = 0; r < 64; ++r) a[r] = L[f4096_addr(base2 | (r << 3))];
+  if (span_log2 > 3) reg_stage<0>(a);
+  if (span_log2 > 4) reg_stage<1>(a);
+  if (span_log2 > 5) reg_stage<2>(a);
+  if (span_log2 > 6) reg_stage<3>(a);
+  if (span_log2 > 7) reg_stage<4>(a);
+  if (span_log2 > 8) reg_stage<5>(a);
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {
+    a[r] *= norm;
+    amax = fmaxf(amax, fabsf(a[r]));
+  }
+#pragma unroll
+  for (int r = 0; r < 64; ++r) L[f4096_addr(base2 | (r << 3))] = a[r];
+  amax = wave_max(amax);
+  float s, inv;
+  sym_scale(amax, clip, s, inv);
+  wave_lds_sync();
+  // phase 3: back to the load layout (output position j = v*512 + lane*8 + e)
+  if (!GSR) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+#pragma unroll
+      for (int e0 = 0; e0 < 8; e0 += 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(L + f4096_addr(v * 512 + lane * 8 + e0));
+        a[v * 8 + e0] = f.x;
+        a[v * 8 + e0 + 1] = f.y;
+        a[v * 8 + e0 + 2] = f.z;
+        a[v * 8 + e0 + 3] = f.w;
+      }
+    }
+  } else {
+    // x . Wal_b: the sequency-ordered Walsh block is symmetric and equals the
+    // Hadamard block with rows permuted by sigma(s) = bitrev(gray(s)), so
+    // output j of a block reads butterfly result sigma(j).
+    const int bmask = (1 << span_log2) - 1;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = v * 512 + lane * 8 + e;
+        const int s_ = j & bmask;
+        const int nat = (j & ~bmask) | bitrev(s_ ^ (s_ >> 1), span_log2);
+        a[v * 8 + e] = L[f4096_addr(nat)];
+      }
+    }
+  }
+  uint8_t *qrow = q + t * 2048;
+  int csum = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    int c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      c[e] = quant_sym(a[v * 8 + e], inv, 7.0f);
+      csum += c[e];
+    }
+    *reinterpret_cast<uint32_t *>(qrow + v * 256 + lane * 4) = pack8(c);
+  }
+  if (code_sum) csum = wave_sum(csum);
+  if (lane == 0) {
+    scale[t] = s;
+    if (code_sum) code_sum[t] = csum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rowlds_quant: one workgroup (256 threads) per row, grid-stride over rows.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 256;
+
+struct RowArgs {
+  const __half *x;
+  int64_t T, K, ldx;
+  int span_log2;      // 0: no transform
+  int gsr;            // output permutation within each 2^span_log2 block
+  float norm;
+  int asym;
+  float clip;
+  const int32_t *outlier_idx;
+  int n_out;
+  uint8_t *q;
+  float *scale;
+  int32_t *zero;
+  int32_t *code_sum;
+  __half *x_out;
+};
+
+__device__ __forceinline__ float block_reduce_max(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_reduce_min(float v, float *red) {
+  v = wave_min(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
+}
+
+__device__ __forceinline__ int block_reduce_sum(int v, int *red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Dynamic LDS: vals fp32 [K] | ncol int32 [K] | ocol int32 [K] | mask u32 [W] | wpre int32 [W],
+// W = ceil(K/32) (the last four only when n_out > 0).
+__global__ __launch_bounds__(kRowThreads) void rowlds_quant(RowArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int K = (int)p.K;
+  const int Kn = K - p.n_out;
+  float *vals = reinterpret_cast<float *>(smem);
+  int32_t *ncol = reinterpret_cast<int32_t *>(vals + K);
+  int32_t *ocol = ncol + K;
+  const int W = (K + 31) / 32;
+  uint32_t *mask = reinterpret_cast<uint32_t *>(ocol + K);
+  int32_t *wpre = reinterpret_cast<int32_t *>(mask + W);
+  const int tid = threadIdx.x;
+
+  if (p.n_out > 0) {
+    // Column classes, built once per workgroup: bit mask of outlier columns,
+    // per-word exclusive prefix counts, then the compacted column maps.
+    for (int w = tid; w < W; w += kRowThreads) mask[w] = 0u;
+    for (int j = tid; j < p.n_out; j += kRowThreads) ocol[j] = 0;  // defined even for bad index lists
+    __syncthreads();
+    for (int j = tid; j < p.n_out; j += kRowThreads) {
+      const int c = p.outlier_idx[j];
+      if (c >= 0 && c < K) atomicOr(&mask[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int w = 0; w < W; ++w) {
+        wpre[w] = run;
+        run += __popc(mask[w]);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < K; c += kRowThreads) {
+      const uint32_t m = mask[c >> 5];
+      const int before = wpre[c >> 5] + __popc(m & ((1u << (c & 31)) - 1u));
+      if ((m >> (c & 31)) & 1u) {
+        if (before < p.n_out) ocol[before] = c;
+      } else {
+        const int pos = c - before;
+        if (pos < Kn) ncol[pos] = c;
+      }
+    }
+    __syncthreads();
+  }
+
+  for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
+    const __half *row = p.x + t * p.ldx;
+    for (int c8 = tid; c8 < K / 8; c8 += kRowThreads) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(row + c8 * 8);
+      float f[8];
+      h8_to_f32(raw, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vals[c8 * 8 + i] = f[i];
+    }
+    __syncthreads();
+    for (int lh = 0; lh < p.span_log2; ++lh) {
+      const int h = 1 << lh;
+      for (int pr = tid; pr < K / 2; pr += kRowThreads) {
+        const int i = ((pr >> lh) << (lh + 1)) | (pr & (h - 1));
+        const float u = vals[i], w = vals[i + h];
+        vals[i] = u + w;
+        vals[i + h] = u - w;
+      }
+      __syncthreads();
+    }
+    // value at compacted (normal) position pos
+    auto value_at = [&](int pos) -> float {
+      int c = p.n_out > 0 ? ncol[pos] : pos;
+      if (p.gsr) {
+        const int bm = (1 << p.span_log2) - 1;
+        const int s_ = c & bm;
+        c = (c & ~bm) | (int)(__builtin_bitreverse32((uint32_t)(s_ ^ (s_ >> 1))) >> (32 - p.span_log2));
+      }
+      return vals[c] * p.norm;
+    };
+    float s, inv;
+    int zero = 0;
+    if (p.asym) {
+      float mn = INFINITY, mx = -INFINITY;
+      for (int pos = tid; pos < Kn; pos += kRowThreads) {
+        const float v = value_at(pos);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      mn = block_reduce_min(mn, redf);
+      mx = block_reduce_max(mx, redf);
+      asym_params(mn, mx, s, inv, zero);
+    } else {
+      float amax = 0.0f;
+      for (int pos = tid; pos < Kn; pos += kRowThreads) amax = fmaxf(amax, fabsf(value_at(pos)));
+      amax = block_reduce_max(amax, redf);
+      sym_scale(amax, p.clip, s, inv);
+    }
+    const float zf = (float)zero;
+    int csum = 0;
+    uint8_t *qrow = p.q + t * (int64_t)(Kn / 2);
+    for (int pb = tid; pb < Kn / 2; pb += kRowThreads) {
+      const float v0 = value_at(2 * pb), v1 = value_at(2 * pb + 1);
+      int c0, c1;
+      if (p.asym) {
+        c0 = quant_asym(v0, inv, zf);
+        c1 = quant_asym(v1, inv, zf);
+      } else {
+        c0 = quant_sym(v0, inv, 7.0f);
+        c1 = quant_sym(v1, inv, 7.0f);
+      }
+      csum += c0 + c1;
+      qrow[pb] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+    }
+    if (p.n_out > 0) {
+      const unsigned short *rh = reinterpret_cast<const unsigned short *>(row);
+      unsigned short *xo = reinterpret_cast<unsigned short *>(p.x_out) + t * (int64_t)p.n_out;
+      for (int j = tid; j < p.n_out; j += kRowThreads) xo[j] = rh[ocol[j]];
+    }
+    if (p.code_sum) csum = block_reduce_sum(csum, redi);
+    if (tid == 0) {
+      p.scale[t] = s;
+      if (p.asym) p.zero[t] = zero;
+      if (p.code_sum) p.code_sum[t] = csum;
+    }
+    __syncthreads();  // vals is reused by the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kron_quant: per row, M = (x * s) reshaped [n1, n2] (or x / s on the weight
+// side), x' = A^T . M . B reshaped back, then symmetric INT4.
+// Activations use A = P1, B = P2; the weight side passes A = P1^{-T},
+// B = P2^{-T} and divides by s.
+// ---------------------------------------------------------------------------
+constexpr int kKronPad = 65;
+
+__global__ __launch_bounds__(256) void kron_quant(const __half *__restrict__ x, int64_t T, int64_t ldx,
+                                                  int n1, int n2, const float *__restrict__ fa,
+                                                  const float *__restrict__ fb,
+                                                  const float *__restrict__ chan_scale, int divide,
+                                                  float clip, uint8_t *__restrict__ q,
+                                                  float *__restrict__ scale,
+                                                  int32_t *__restrict__ code_sum) {
+  __shared__ float A[64 * kKronPad];
+  __shared__ float B[64 * kKronPad];
+  __shared__ float M[64 * kKronPad];
+  __shared__ float U[64 * kKronPad];
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int tid = threadIdx.x;
+  const int K = n1 * n2;
+  for (int i = tid; i < n1 * n1; i += 256) A[(i / n1) * kKronPad + i % n1] = fa[i];
+  for (int i = tid; i < n2 * n2; i += 256) B[(i / n2) * kKronPad + i % n2] = fb[i];
+  __syncthreads();
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const __half *row = x + t * ldx;
+    for (int c = tid; c < K; c += 256) {
+      float v = __half2float(row[c]);
+      if (chan_scale) v = divide ? v / chan_scale[c] : v * chan_scale[c];
+      M[(c / n2) * kKronPad + c % n2] = v;
+    }
+    __syncthreads();
+    // U = A^T . M : U[j1][i2] = sum_i1 A[i1][j1] M[i1][i2]
+    for (int o = tid; o < K; o += 256) {
+      const int j1 = o / n2, i2 = o % n2;
+      float acc = 0.0f;
+      for (int i1 = 0; i1 < n1; ++i1) acc = fmaf(A[i1 * kKronPad + j1], M[i1 * kKronPad + i2], acc);
+      U[j1 * kKronPad + i2] = acc;
+    }
+    __syncthreads();
+    // x' = U . B : x'[j1][j2] = sum_i2 U[j1][i2] B[i2][j2]   (stored in M)
+    float amax = 0.0f;
+    for (int o = tid; o < K; o += 256) {
+      const int j1 = o / n2, j2 = o % n2;
+      float acc = 0.0f;
+      for (int i2 = 0; i2 < n2; ++i2) acc = fmaf(U[j1 * kKronPad + i2], B[i2 * kKronPad + j2], acc);
+      M[j1 * kKronPad + j2] = acc;
+      amax = fmaxf(amax, fabsf(acc));
+    }
+    amax = block_reduce_max(amax, redf);  // includes a barrier after the M writes
+    float s, inv;
+    sym_scale(amax, clip, s, inv);
+    int csum = 0;
+    uint8_t *qrow = q + t * (int64_t)(K / 2);
+    for (int pb = tid; pb < K / 2; pb += 256) {
+      const int o0 = 2 * pb, o1 = 2 * pb + 1;
+      const int c0 = quant_sym(M[(o0 / n2) * kKronPad + o0 % n2], inv, 7.0f);
+      const int c1 = quant_sym(M[(o1 / n2) * kKronPad + o1 % n2], inv, 7.0f);
+      csum += c0 + c1;
+      qrow[pb] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+    }
+    if (code_sum) csum = block_reduce_sum(csum, redi);
+    if (tid == 0) {
+      scale[t] = s;
+      if (code_sum) code_sum[t] = csum;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kron_inverse_t: out_k = (P_k^{-1})^T in fp32, P_k fp32 [n_k, n_k], n_k <= 64.
+// fp64 Gauss-Jordan elimination with partial pivoting on [P | I]; block k
+// handles factor k.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kron_inverse_t(const float *__restrict__ p1, int n1,
+                                                      float *__restrict__ o1,
+                                                      const float *__restrict__ p2, int n2,
+                                                      float *__restrict__ o2) {
+  __shared__ double aug[64][129];
+  __shared__ int piv;
+  const float *P = blockIdx.x == 0 ? p1 : p2;
+  float *O = blockIdx.x == 0 ? o1 : o2;
+  const int n = blockIdx.x == 0 ? n1 : n2;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n * 2 * n; i += 256) {
+    const int r = i / (2 * n), c = i % (2 * n);
+    aug[r][c] = c < n ? (double)P[r * n + c] : (c - n == r ? 1.0 : 0.0);
+  }
+  __syncthreads();
+  for (int col = 0; col < n; ++col) {
+    if (tid == 0) {
+      int best = col;
+      double bv = fabs(aug[col][col]);
+      for (int r = col + 1; r < n; ++r) {
+        const double v = fabs(aug[r][col]);
+        if (v > bv) {
+          bv = v;
+          best = r;
+        }
+      }
+      piv = best;
+    }
+    __syncthreads();
+    const int pr = piv;
+    if (pr != col) {
+      for (int c = tid; c < 2 * n; c += 256) {
+        const double tmp = aug[col][c];
+        aug[col][c] = aug[pr][c];
+        aug[pr][c] = tmp;
+      }
+    }
+    __syncthreads();
+    const double d = aug[col][col];
+    __syncthreads();
+    for (int c = tid; c < 2 * n; c += 256) aug[col][c] /= d;
+    __syncthreads();
+    for (int i = tid; i < n * 2 * n; i += 256) {
+      const int r = i / (2 * n), c = i % (2 * n);
+      if (r != col && c != col) aug[r][c] -= aug[r][col] * aug[col][c];
+    }
+    __syncthreads();
+    for (int r = tid; r < n; r += 256)
+      if (r != col) aug[r][col] = 0.0;
+    __syncthreads();
+  }
+  // inverse is aug[:, n:2n]; write its transpose
+  for (int i = tid; i < n * n; i += 256) {
+    const int r = i / n, c = i % n;
+    O[r * n + c] = (float)aug[c][n + r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called by the C ABI after validation).
+// ---------------------------------------------------------------------------
+hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int span_log2,
+                           float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
+                           hipStream_t st) {
+  const int64_t blocks = (T + kF4096Waves - 1) / kF4096Waves;
+  if (gsr)
+    fwht4096_quant<true><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        (const __half *)x, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+  else
+    fwht4096_quant<false><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        (const __half *)x, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+  return hipGetLastError();
+}
+
+size_t rowlds_smem_bytes(int64_t K, int n_out) {
+  size_t b = (size_t)K * 4;
+  if (n_out > 0) b += (size_t)K * 8 + (size_t)((K + 31) / 32) * 8;
+  return b;
+}
+
+hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int span_log2, bool gsr,
+                         float norm, bool asym, float clip, const int32_t *outlier_idx, int n_out,
+                         uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum, void *x_out,
+                         hipStream_t st) {
+  RowArgs p;
+  p.x = (const __half *)x;
+  p.T = T;
+  p.K = K;
+  p.ldx = ldx;
+  p.span_log2 = span_log2;
+  p.gsr = gsr ? 1 : 0;
+  p.norm = norm;
+  p.asym = asym ? 1 : 0;
+  p.clip = clip;
+  p.outlier_idx = outlier_idx;
+  p.n_out = n_out;
+  p.q = q;
+  p.scale = scale;
+  p.zero = zero;
+  p.code_sum = code_sum;
+  p.x_out = (__half *)x_out;
+  const size_t smem = rowlds_smem_bytes(K, n_out);
+  hipError_t e = hipFuncSetAttribute((const void *)rowlds_quant,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int64_t grid = T < 8192 ? T : 8192;
+  rowlds_quant<<<dim3((unsigned)grid), dim3(kRowThreads), smem, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, const float *fa,
+                       const float *fb, const float *chan_scale, bool divide, float clip,
+                       uint8_t *q, float *scale, int32_t *code_sum, hipStream_t st) {
+  const int64_t grid = T < 8192 ? T : 8192;
+  kron_quant<<<dim3((unsigned)grid), dim3(256), 0, st>>>((const __half *)x, T, ldx, n1, n2, fa, fb,
+                                                         chan_scale, divide ? 1 : 0, clip, q, scale,
+                                                         code_sum);
+  return hipGetLastError();
+}
+
+hipError_t launch_kron_inverse_t(const float *p1, int n1, float *o1, const float *p2, int n2,
+                                 float *o2, hipStream_t st) {
+  kron_inverse_t<<<dim3(2), dim3(256), 0, st>>>(p1, n1, o1, p2, n2, o2);
+  return hipGetLastError();
+}
+
+}  // namespace rq

@@ -1,0 +1,43 @@
+// rq_kernels.h -- launchers of the gfx950 kernels (internal; the C ABI in
+// rq_api.cpp validates arguments and then calls these).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rq {
+
+struct GemmArgs {
+  const uint8_t *qx;     // [T, Kb] packed codes
+  const uint8_t *qw;     // [N, Kb] packed codes (signed)
+  int64_t T, N, Kb;      // Kb = K / 2 bytes per row
+  const float *sx;       // [T]
+  const float *sw;       // [N]
+  const int32_t *zx;     // [T] or null
+  const int32_t *rowsum; // [N] or null
+  const __half *xo;      // [T, n_out] or null
+  const __half *wo;      // [N, n_out] or null
+  int n_out;
+  void *out;             // int32 or fp16 [T, ldo]
+  int64_t ldo;
+};
+
+hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int span_log2,
+                           float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
+                           hipStream_t st);
+size_t rowlds_smem_bytes(int64_t K, int n_out);
+hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int span_log2, bool gsr,
+                         float norm, bool asym, float clip, const int32_t *outlier_idx, int n_out,
+                         uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum, void *x_out,
+                         hipStream_t st);
+hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, const float *fa,
+                       const float *fb, const float *chan_scale, bool divide, float clip,
+                       uint8_t *q, float *scale, int32_t *code_sum, hipStream_t st);
+hipError_t launch_kron_inverse_t(const float *p1, int n1, float *o1, const float *p2, int n2,
+                                 float *o2, hipStream_t st);
+// mode 0: raw int32 accumulator; 1: symmetric fp16 output; 2: mixed fp16 output
+hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
+
+}  // namespace rq

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/rq.h declares, and its host-side validation rejects bad arguments
+with the documented status codes before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_rotation_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rq.LIB_PATH),
+                                reason="librq.so not built (run python -m online_rotation_amd.build)")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(rq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rq.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert rq.rq_abi_version() == 1
+    assert rq.rq_status_string(0) == "RQ_OK"
+    for s in range(1, 5):
+        assert rq.rq_status_string(s).startswith("RQ_E")
+
+
+def _rot(kind="hadamard", block=0, n1=0, n2=0, p1=None, p2=None, cs=None):
+    return rq._RotDesc(rq.ROT_KINDS[kind], block, n1, n2, p1, p2, cs)
+
+
+def _qd(asym=0, clip=1.0, idx=None, n_out=0):
+    return rq._QuantDesc(asym, clip, idx, n_out)
+
+
+def _rotate_quant(T, K, ldx, rot, qd, x=FAKE, q=FAKE, scale=FAKE, zero=None, x_out=None):
+    return rq.lib().rq_rotate_quant(x, T, K, ldx, ctypes.byref(rot), ctypes.byref(qd), q, scale,
+                                    zero, None, x_out, None)
+
+
+@pytest.mark.parametrize("T,K,ldx,rot,qd,want", [
+    (4, 4096, 4096, _rot("hadamard"), _qd(clip=0.0), rq.RQ_EINVAL),           # clip out of range
+    (4, 4096, 4096, _rot("hadamard"), _qd(clip=1.5), rq.RQ_EINVAL),
+    (-1, 4096, 4096, _rot("hadamard"), _qd(), rq.RQ_EINVAL),                  # negative T
+    (4, 3000, 3000, _rot("hadamard"), _qd(), rq.RQ_ESHAPE),                   # not a power of two
+    (4, 65536, 65536, _rot("hadamard"), _qd(), rq.RQ_ESHAPE),                 # too large
+    (4, 4096, 4096, _rot("gsr", block=48), _qd(), rq.RQ_ESHAPE),              # block not pow2
+    (4, 4096, 4096, _rot("gsr", block=512), _qd(), rq.RQ_ESHAPE),             # block too large
+    (4, 4096, 4096, _rot("kron", n1=64, n2=32, p1=FAKE, p2=FAKE), _qd(), rq.RQ_ESHAPE),  # K != n1*n2
+    (4, 4096, 4096, _rot("kron", n1=64, n2=64), _qd(), rq.RQ_EINVAL),         # null factors
+    (4, 4096, 4096, _rot("hadamard"), _qd(asym=1), rq.RQ_ESHAPE),             # asym + rotation
+    (4, 4096, 4096, _rot("hadamard"), _qd(idx=FAKE, n_out=64), rq.RQ_ESHAPE),  # split + rotation
+    (4, 8192, 8192, _rot("none"), _qd(idx=FAKE, n_out=100), rq.RQ_ESHAPE),    # K - n_out % 64
+    (4, 8192, 8192, _rot("none"), _qd(n_out=256), rq.RQ_EINVAL),              # null idx
+    (4, 4096, 4000, _rot("hadamard"), _qd(), rq.RQ_EALIGN),                   # ldx < K
+    (4, 4096, 4100, _rot("hadamard"), _qd(), rq.RQ_EALIGN),                   # ldx % 8
+    (4, 4096, 4096, _rot("none"), _qd(asym=1, clip=0.9), rq.RQ_EINVAL),       # asym takes clip 1
+    (4, 4104, 4104, _rot("none"), _qd(), rq.RQ_ESHAPE),                       # K % 64 with no split
+    (4, 32768, 32768, _rot("none"), _qd(idx=FAKE, n_out=64 * 3 + 128), rq.RQ_ESHAPE),  # LDS
+])
+def test_rotate_quant_validation(T, K, ldx, rot, qd, want):
+    assert _rotate_quant(T, K, ldx, rot, qd, x_out=FAKE) == want
+    assert rq.rq_last_error() != ""
+
+
+def test_rotate_quant_alignment_and_nulls():
+    rot, qd = _rot("hadamard"), _qd()
+    assert _rotate_quant(4, 4096, 4096, rot, qd, x=FAKE + 2) == rq.RQ_EALIGN
+    assert _rotate_quant(4, 4096, 4096, rot, qd, q=None) == rq.RQ_EINVAL
+    assert _rotate_quant(4, 8192, 8192, _rot("none"), _qd(asym=1), zero=None) == rq.RQ_EINVAL
+    assert _rotate_quant(4, 8448, 8448, _rot("none"), _qd(idx=FAKE, n_out=256)) == rq.RQ_EINVAL  # x_out
+    L = rq.lib()
+    assert L.rq_rotate_quant(FAKE, 4, 4096, 4096, None, ctypes.byref(qd), FAKE, FAKE, None, None,
+                             None, None) == rq.RQ_EINVAL
+    bad = _rot("hadamard"); bad.kind = 9
+    assert _rotate_quant(4, 4096, 4096, bad, qd) == rq.RQ_EINVAL
+
+
+def test_empty_batch_is_a_no_op():
+    # T == 0 passes validation and launches nothing, so it is safe without a GPU
+    assert _rotate_quant(0, 4096, 4096, _rot("hadamard"), _qd(), x=None, q=None, scale=None) == rq.RQ_OK
+    L = rq.lib()
+    assert L.rq_w4a4_linear(None, None, 0, 4096, None, None, 16, None, 16, None) == rq.RQ_OK
+    assert L.rq_w4a4_gemm_i32(None, 0, 0, 4096, None, 16, None, 16, None) == rq.RQ_OK
+
+
+def test_gemm_validation():
+    L = rq.lib()
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 100, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_ESHAPE  # K % 64
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 0, FAKE, 16, None) == rq.RQ_EINVAL  # N
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 12, None) == rq.RQ_EALIGN  # ldy < N
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 20, None) == rq.RQ_EALIGN  # ldy % 8
+    assert L.rq_w4a4_linear(FAKE + 8, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_EALIGN
+    assert L.rq_w4a4_linear(FAKE, None, 8, 4096, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_EINVAL
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 131072, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_ESHAPE
+    assert L.rq_w4a4_gemm_i32(FAKE, 0, 8, 4096, FAKE, 16, FAKE, 18, None) == rq.RQ_EALIGN     # ldacc % 4
+    assert L.rq_mixed_outlier_linear(FAKE, FAKE, FAKE, 8, 7936, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                     100, FAKE, 16, None) == rq.RQ_ESHAPE                    # n_out % 32
+    assert L.rq_mixed_outlier_linear(FAKE, FAKE, FAKE, 8, 7936, FAKE, FAKE, None, 16, FAKE, FAKE,
+                                     256, FAKE, 16, None) == rq.RQ_EINVAL                    # rowsum
+    assert L.rq_mixed_outlier_linear(FAKE, FAKE, None, 8, 7936, FAKE, FAKE, None, 16, None, None,
+                                     256, FAKE, 16, None) == rq.RQ_EINVAL                    # outliers
+
+
+def test_prepare_weights_validation_and_workspace():
+    L = rq.lib()
+    kron = _rot("kron", n1=64, n2=64, p1=FAKE, p2=FAKE)
+    assert L.rq_prepare_weights_workspace_bytes(ctypes.byref(kron)) == 2 * 64 * 64 * 4
+    assert L.rq_prepare_weights_workspace_bytes(ctypes.byref(_rot("hadamard"))) == 0
+    assert L.rq_prepare_weights_workspace_bytes(None) == 0
+    qd = _qd()
+    # KRON without a workspace
+    assert L.rq_prepare_weights(FAKE, 8, 4096, 4096, ctypes.byref(kron), ctypes.byref(qd), FAKE, FAKE,
+                                None, None, None, 0, None) == rq.RQ_EINVAL
+    # asymmetric weights are not a thing
+    assert L.rq_prepare_weights(FAKE, 8, 4096, 4096, ctypes.byref(_rot("none")), ctypes.byref(_qd(asym=1)),
+                                FAKE, FAKE, None, None, None, 0, None) == rq.RQ_EINVAL
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 4096), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        rq.rq_rotate_quant(x, rq.Rotation("hadamard"))

@@ -1,0 +1,390 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test prints its case before touching the GPU.  Inputs come from the
+seeded generators in `workloads`; expected values come from `oracle` only.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import rq_oracle as o
+from parity_utils import (check_asym_quant, check_scales, check_sym_quant, check_y, dev,
+                          flip_allowance, host, note)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+rq = pytest.importorskip("online_rotation_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rq.lib()  # raises if librq.so is missing: no silent fallback
+
+
+def _rot_args(kind, block=0, inp=None):
+    kw = {}
+    if kind == "gsr":
+        kw["block"] = block
+    if kind == "kron":
+        kw.update(p1=inp["p1"], p2=inp["p2"], chan_scale=inp["s"])
+    return kw
+
+
+def _gpu_rot(kind, block=0, inp=None):
+    if kind == "kron":
+        return rq.Rotation("kron", p1=dev(inp["p1"]), p2=dev(inp["p2"]), chan_scale=dev(inp["s"]))
+    return rq.Rotation(kind, block=block)
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+QUANT_CASES = [
+    # name, workload, T, K, kind, block, clip, n1
+    ("tiny-full", "tiny", None, None, "hadamard", 0, 1.0, 0),
+    ("had4096-ragged", "llama7b", 301, 4096, "hadamard", 0, 1.0, 0),
+    ("gsr64-4096-clip", "gsr", 301, 4096, "gsr", 64, 0.9, 0),
+    ("gsr16-4096", "gsr", 37, 4096, "gsr", 16, 1.0, 0),
+    ("gsr256-4096", "gsr", 37, 4096, "gsr", 256, 1.0, 0),
+    ("gsr64-1024-rowlds", "gsr", 41, 1024, "gsr", 64, 0.9, 0),
+    ("had64-rowlds", "llama7b", 33, 64, "hadamard", 0, 1.0, 0),
+    ("had1024-rowlds", "llama7b", 33, 1024, "hadamard", 0, 1.0, 0),
+    ("had8192-rowlds", "llama7b", 9, 8192, "hadamard", 0, 1.0, 0),
+    ("had32768-rowlds-max", "llama7b", 3, 32768, "hadamard", 0, 1.0, 0),
+    ("kron64x64", "flat", 37, 4096, "kron", 0, 0.95, 64),
+    ("kron16x16", "flat", 21, 256, "kron", 0, 0.95, 16),
+    ("none-sym-512", "llama7b", 19, 512, "none", 0, 1.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_rotate_quant_matches_oracle(case):
+    name, wl, T, K, kind, block, clip, n1 = case
+    note(f"[rotate_quant] {name}")
+    inp = workloads.make_inputs(wl, T=T, K=K, with_weights=False, n1=n1 or None, n2=n1 or None)
+    x = inp["x"]
+    ref = o.rotate_quant(x, kind, clip=clip, **_rot_args(kind, block, inp))
+    out = rq.rq_rotate_quant(dev(x), _gpu_rot(kind, block, inp), clip=clip, code_sum=True)
+    torch.cuda.synchronize()
+    check_sym_quant(host(out["q"]), host(out["scale"]), ref)
+    q_gpu = o.unpack_int4(host(out["q"]), signed=True).astype(np.int64)
+    assert np.array_equal(host(out["code_sum"]), q_gpu.sum(axis=1))
+
+
+def test_rotate_quant_strided_rows():
+    note("[rotate_quant] strided ldx")
+    inp = workloads.make_inputs("llama7b", T=13, K=4096, with_weights=False)
+    x = inp["x"]
+    big = np.zeros((13, 4096 + 64), np.float16)
+    big[:, :4096] = x
+    ref = o.rotate_quant(x, "hadamard")
+    xt = dev(big)[:, :4096]
+    assert xt.stride(0) == 4160
+    out = rq.rq_rotate_quant(xt, rq.Rotation("hadamard"))
+    torch.cuda.synchronize()
+    check_sym_quant(host(out["q"]), host(out["scale"]), ref)
+    inp2 = workloads.make_inputs("tiny", T=5, with_weights=False)
+    big2 = np.zeros((5, 256 + 8), np.float16)
+    big2[:, :256] = inp2["x"]
+    out2 = rq.rq_rotate_quant(dev(big2)[:, :256], rq.Rotation("hadamard"))
+    torch.cuda.synchronize()
+    check_sym_quant(host(out2["q"]), host(out2["scale"]), o.rotate_quant(inp2["x"], "hadamard"))
+
+
+@pytest.mark.parametrize("T,K,n_out", [(37, 8192, 256), (5, 8192, 0), (3, 1024, 64)])
+def test_asymmetric_outlier_split_matches_oracle(T, K, n_out):
+    note(f"[rotate_quant] asym T={T} K={K} n_out={n_out}")
+    inp = workloads.make_inputs("quik_prefill", T=T, K=K, with_weights=False)
+    x, idx = inp["x"], inp["outlier_ch"][:n_out]
+    ref = o.rotate_quant(x, "none", asym=True, outlier_idx=idx if n_out else None)
+    out = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True,
+                             outlier_idx=dev(idx) if n_out else None)
+    torch.cuda.synchronize()
+    check_asym_quant(host(out["q"]), host(out["scale"]), host(out["zero"]), ref)
+    if n_out:
+        assert np.array_equal(host(out["x_out"]).view(np.uint16), ref["x_out"].view(np.uint16))
+        # the order of the index list does not matter
+        perm = np.random.default_rng(0).permutation(n_out)
+        out2 = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True,
+                                  outlier_idx=dev(idx[perm].copy()))
+        torch.cuda.synchronize()
+        for k in ("q", "scale", "zero", "x_out"):
+            assert torch.equal(out[k], out2[k]), k
+
+
+# ----------------------------------------------------------------------------- weights
+
+WEIGHT_CASES = [
+    ("had4096", "llama7b", 200, 4096, "hadamard", 0, 0),
+    ("gsr64", "gsr", 130, 4096, "gsr", 64, 0),
+    ("kron64", "flat", 70, 4096, "kron", 0, 0),
+    ("tiny", "tiny", None, None, "hadamard", 0, 0),
+    ("quik-split", "quik_prefill", 100, 8192, "none", 0, 256),
+]
+
+
+@pytest.mark.parametrize("case", WEIGHT_CASES, ids=[c[0] for c in WEIGHT_CASES])
+def test_prepare_weights_matches_oracle(case):
+    name, wl, N, K, kind, block, n_out = case
+    note(f"[prepare_weights] {name}")
+    inp = workloads.make_inputs(wl, T=4, K=K, N=N)
+    w = inp["w"]
+    idx = inp["outlier_ch"][:n_out] if n_out else None
+    ref = o.prepare_weights(w, kind, outlier_idx=idx, **_rot_args(kind, block, inp))
+    out = rq.rq_prepare_weights(dev(w), _gpu_rot(kind, block, inp),
+                                outlier_idx=dev(idx) if n_out else None)
+    torch.cuda.synchronize()
+    check_sym_quant(host(out["q"]), host(out["scale"]), ref, what="w")
+    q_gpu = o.unpack_int4(host(out["q"]), signed=True).astype(np.int64)
+    assert np.array_equal(host(out["rowsum"]), q_gpu.sum(axis=1))
+    if n_out:
+        assert np.array_equal(host(out["w_out"]).view(np.uint16), ref["w_out"].view(np.uint16))
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
+               (8, 300, 8192)]
+
+
+@pytest.mark.parametrize("unsigned_x", [False, True])
+@pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
+def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
+    note(f"[gemm_i32] T={T} N={N} K={K} unsigned_x={unsigned_x}")
+    rng = np.random.default_rng(T * 7 + N * 3 + K)
+    qx = rng.integers(0, 16, (T, K)) if unsigned_x else rng.integers(-8, 8, (T, K))
+    qw = rng.integers(-8, 8, (N, K))
+    acc = rq.rq_w4a4_gemm_i32(dev(o.pack_int4(qx)), dev(o.pack_int4(qw)), x_unsigned=unsigned_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), o.int_gemm(qx, qw))
+
+
+@pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968)])
+def test_linear_epilogue_on_oracle_codes(T, N, K):
+    note(f"[w4a4_linear] T={T} N={N} K={K}")
+    rng = np.random.default_rng(K + T)
+    qx = rng.integers(-7, 8, (T, K)); qw = rng.integers(-7, 8, (N, K))
+    sx = rng.uniform(0.01, 40, T).astype(np.float32); sw = rng.uniform(1e-4, 5e-3, N).astype(np.float32)
+    y = rq.rq_w4a4_linear(dev(o.pack_int4(qx)), dev(sx), dev(o.pack_int4(qw)), dev(sw))
+    torch.cuda.synchronize()
+    check_y(host(y), o.dequant_sym(o.int_gemm(qx, qw), sx, sw))
+
+
+@pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False)])
+def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
+    note(f"[mixed_linear] T={T} N={N} n_out={n_out} asym={asym}")
+    K = 7936
+    rng = np.random.default_rng(n_out + T)
+    qx = rng.integers(0, 16, (T, K)) if asym else rng.integers(-7, 8, (T, K))
+    zx = rng.integers(0, 16, T).astype(np.int32) if asym else None
+    qw = rng.integers(-7, 8, (N, K))
+    rowsum = qw.sum(axis=1).astype(np.int32)
+    sx = rng.uniform(0.01, 2, T).astype(np.float32); sw = rng.uniform(1e-4, 5e-3, N).astype(np.float32)
+    xo = (rng.standard_normal((T, n_out)) * 40).astype(np.float16)
+    wo = (rng.standard_normal((N, n_out)) * 0.02).astype(np.float16)
+    y = rq.rq_mixed_outlier_linear(dev(o.pack_int4(qx)), dev(sx), dev(zx) if asym else None,
+                                   dev(o.pack_int4(qw)), dev(sw), dev(rowsum) if asym else None,
+                                   dev(xo) if n_out else None, dev(wo) if n_out else None)
+    torch.cuda.synchronize()
+    ref = o.dequant_mixed(o.int_gemm(qx, qw), sx, zx if asym else np.zeros(T, np.int32), sw, rowsum,
+                          xo, wo)
+    check_y(host(y), ref)
+
+
+# ----------------------------------------------------------------------------- end to end
+
+E2E_CASES = [
+    # name, workload, T, K, N, kind, block, clip, n1
+    ("tiny-full", "tiny", None, None, None, "hadamard", 0, 1.0, 0),
+    ("llama7b-small", "llama7b", 300, 4096, 200, "hadamard", 0, 1.0, 0),
+    ("gsr-small", "gsr", 150, 4096, 260, "gsr", 64, 0.9, 0),
+    ("flat-small", "flat", 70, 4096, 130, "kron", 0, 0.95, 64),
+]
+
+
+def _e2e(inp, kind, block, clip, x_rows=None, w_rows=None):
+    """GPU full pipeline; returns GPU results on the requested rows."""
+    x, w = inp["x"], inp["w"]
+    rot = _gpu_rot(kind, block, inp)
+    xd, wd = dev(x), dev(w)
+    xq = rq.rq_rotate_quant(xd, rot, clip=clip)
+    wq = rq.rq_prepare_weights(wd, rot)
+    y = rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"])
+    torch.cuda.synchronize()
+    return xq, wq, y
+
+
+@pytest.mark.parametrize("case", E2E_CASES, ids=[c[0] for c in E2E_CASES])
+def test_end_to_end_matches_oracle(case):
+    name, wl, T, K, N, kind, block, clip, n1 = case
+    note(f"[e2e] {name}")
+    inp = workloads.make_inputs(wl, T=T, K=K, N=N, n1=n1 or None, n2=n1 or None)
+    kw = _rot_args(kind, block, inp)
+    xr = o.rotate_quant(inp["x"], kind, clip=clip, **kw)
+    wr = o.prepare_weights(inp["w"], kind, **kw)
+    yr = o.linear(xr, wr)["y"]
+    xq, wq, y = _e2e(inp, kind, block, clip)
+    fx = check_sym_quant(host(xq["q"]), host(xq["scale"]), xr)
+    fw = check_sym_quant(host(wq["q"]), host(wq["scale"]), wr, what="w")
+    check_y(host(y), yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw, qmax_x=7))
+
+
+def test_end_to_end_quik_small():
+    note("[e2e] quik small")
+    inp = workloads.make_inputs("quik_prefill", T=40, K=8192, N=130)
+    x, w, idx = inp["x"], inp["w"], inp["outlier_ch"]
+    xr = o.rotate_quant(x, "none", asym=True, outlier_idx=idx)
+    wr = o.prepare_weights(w, "none", outlier_idx=idx)
+    yr = o.linear(xr, wr)["y"]
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=dev(idx))
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=dev(idx))
+    y = rq.rq_mixed_outlier_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"],
+                                   wq["rowsum"], xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    fx = check_asym_quant(host(xq["q"]), host(xq["scale"]), host(xq["zero"]), xr)
+    fw = check_sym_quant(host(wq["q"]), host(wq["scale"]), wr, what="w")
+    check_y(host(y), yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw))
+
+
+# ----------------------------------------------------------------------------- full size, sampled
+
+FULL_CASES = [
+    # name, workload, kind, block, clip
+    ("llama7b", "llama7b", "hadamard", 0, 1.0),
+    ("gsr", "gsr", "gsr", 64, 0.9),
+    ("flat", "flat", "kron", 0, 0.95),
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_full_size_sampled(case):
+    name, wl, kind, block, clip = case
+    note(f"[full] {name}")
+    inp = workloads.make_inputs(wl)
+    x, w = inp["x"], inp["w"]
+    T, N = x.shape[0], w.shape[0]
+    rng = np.random.default_rng(99)
+    ts = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 45, replace=False)]))
+    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 254, replace=False)]))
+    kw = _rot_args(kind, block, inp)
+    xr = o.rotate_quant(x[ts], kind, clip=clip, **kw)
+    wr = o.prepare_weights(w[ns], kind, **kw)
+    yr = o.linear(xr, wr)["y"]
+    xq, wq, y = _e2e(inp, kind, block, clip)
+    fx = check_sym_quant(host(xq["q"])[ts], host(xq["scale"])[ts], xr)
+    fw = check_sym_quant(host(wq["q"])[ns], host(wq["scale"])[ns], wr, what="w")
+    check_y(host(y)[np.ix_(ts, ns)], yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw, qmax_x=7))
+
+
+@pytest.mark.parametrize("wl", ["quik_prefill", "quik_decode"])
+def test_full_size_quik_sampled(wl):
+    note(f"[full] {wl}")
+    inp = workloads.make_inputs(wl)
+    x, w, idx = inp["x"], inp["w"], inp["outlier_ch"]
+    T, N = x.shape[0], w.shape[0]
+    rng = np.random.default_rng(7)
+    ts = np.unique(np.concatenate([[0, T - 1], rng.choice(T, min(T, 30), replace=False)]))
+    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 254, replace=False)]))
+    xr = o.rotate_quant(x[ts], "none", asym=True, outlier_idx=idx)
+    wr = o.prepare_weights(w[ns], "none", outlier_idx=idx)
+    yr = o.linear(xr, wr)["y"]
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=dev(idx))
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=dev(idx))
+    y = rq.rq_mixed_outlier_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"],
+                                   wq["rowsum"], xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    fx = check_asym_quant(host(xq["q"])[ts], host(xq["scale"])[ts], host(xq["zero"])[ts], xr)
+    fw = check_sym_quant(host(wq["q"])[ns], host(wq["scale"])[ns], wr, what="w")
+    check_y(host(y)[np.ix_(ts, ns)], yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw))
+
+
+@pytest.mark.parametrize("T,N,K", [(2048, 4096, 4096), (4096, 28672, 7936)])
+def test_full_size_gemm_int32_sampled(T, N, K):
+    """The bench's GEMM launch shape, on random codes, bit-exact on sampled outputs."""
+    note(f"[full gemm_i32] T={T} N={N} K={K}")
+    rng = np.random.default_rng(5)
+    qx = rng.integers(-8, 8, (T, K), dtype=np.int8)
+    qw = rng.integers(-8, 8, (N, K), dtype=np.int8)
+    acc = host(rq.rq_w4a4_gemm_i32(dev(o.pack_int4(qx)), dev(o.pack_int4(qw))))
+    ts = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 40, replace=False)]))
+    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 300, replace=False)]))
+    assert np.array_equal(acc[np.ix_(ts, ns)], o.int_gemm(qx[ts], qw[ns]))
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_edge_rows_zero_constant_onehot_and_ties():
+    note("[edge] crafted rows")
+    K = 4096
+    h = o.hadamard(K)
+    rows = np.zeros((8, K))
+    rows[1] = 3.0                                   # constant -> one nonzero code
+    rows[2, 17] = 5.0                               # one-hot -> all codes +-7
+    y = np.zeros(K); y[:6] = [7.0, 0.5, 1.5, 2.5, -2.5, -3.5]
+    rows[3] = y @ h                                 # exact ties after rotation
+    rows[4] = -rows[3]
+    rows[5, :] = 1e-3                               # tiny values
+    rows[6] = np.where(np.arange(K) % 2, 1.0, -1.0) * 65504.0 / 64  # large, exact
+    rows[7, 4095] = -2.0
+    x = rows.astype(np.float16)
+    assert np.array_equal(x[3].astype(np.float64), rows[3])
+    for kind, block, clip in (("hadamard", 0, 1.0), ("gsr", 64, 1.0), ("hadamard", 0, 0.9)):
+        ref = o.rotate_quant(x, kind, clip=clip, block=block)
+        out = rq.rq_rotate_quant(dev(x), rq.Rotation(kind, block=block), clip=clip)
+        torch.cuda.synchronize()
+        check_sym_quant(host(out["q"]), host(out["scale"]), ref)
+        qg = o.unpack_int4(host(out["q"]), signed=True)
+        assert not qg[0].any() and host(out["scale"])[0] == 0.0
+        if kind == "hadamard" and clip == 1.0:
+            np.testing.assert_array_equal(qg[3, :6], [7, 0, 2, 2, -2, -4])
+            np.testing.assert_array_equal(qg[4, :6], [-7, 0, -2, -2, 2, 4])
+    # zero activation row gives a zero output row
+    inp = workloads.make_inputs("llama7b", T=4, K=K, N=64)
+    xz = inp["x"].copy(); xz[2] = 0
+    xq = rq.rq_rotate_quant(dev(xz), rq.Rotation("hadamard"))
+    wq = rq.rq_prepare_weights(dev(inp["w"]), rq.Rotation("hadamard"))
+    yy = host(rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"]))
+    assert not yy[2].any()
+
+
+def test_edge_asymmetric_rows():
+    note("[edge] asymmetric rows")
+    K = 1024
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, K))
+    x[0] = np.abs(x[0])          # zero point 0
+    x[1] = -np.abs(x[1])         # zero point 15
+    x[2] = 0.0                   # zero row
+    x[3] = 2.5                   # constant positive row
+    x16 = x.astype(np.float16)
+    ref = o.rotate_quant(x16, "none", asym=True)
+    out = rq.rq_rotate_quant(dev(x16), rq.Rotation("none"), asym=True)
+    torch.cuda.synchronize()
+    check_asym_quant(host(out["q"]), host(out["scale"]), host(out["zero"]), ref)
+    assert host(out["zero"])[0] == 0 and host(out["zero"])[1] == 15 and host(out["scale"])[2] == 0
+
+
+def test_empty_and_single_row():
+    note("[edge] T=0 and T=1")
+    x0 = torch.empty((0, 4096), dtype=torch.float16, device="cuda")
+    out = rq.rq_rotate_quant(x0, rq.Rotation("hadamard"))
+    assert out["q"].shape == (0, 2048)
+    inp = workloads.make_inputs("llama7b", T=1, K=4096, N=130)
+    xr = o.rotate_quant(inp["x"], "hadamard"); wr = o.prepare_weights(inp["w"], "hadamard")
+    xq, wq, y = _e2e(inp, "hadamard", 0, 1.0)
+    fx = check_sym_quant(host(xq["q"]), host(xq["scale"]), xr)
+    fw = check_sym_quant(host(wq["q"]), host(wq["scale"]), wr, what="w")
+    check_y(host(y), o.linear(xr, wr)["y"], extra=flip_allowance(xr["scale"], wr["scale"], fx, fw, qmax_x=7))
+    y0 = rq.rq_w4a4_linear(xq["q"][:0], xq["scale"][:0], wq["q"], wq["scale"])
+    torch.cuda.synchronize()
+    assert y0.shape == (0, 130)
+
+
+def test_deterministic_reruns():
+    note("[edge] determinism")
+    inp = workloads.make_inputs("gsr", T=64, K=4096, N=256)
+    a = _e2e(inp, "gsr", 64, 0.9)
+    b = _e2e(inp, "gsr", 64, 0.9)
+    assert torch.equal(a[0]["q"], b[0]["q"]) and torch.equal(a[2], b[2])
