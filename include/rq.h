@@ -27,7 +27,8 @@
  *     two codes per byte: element 2j in the low nibble, 2j+1 in the high
  *     nibble.  Symmetric codes are 4-bit two's complement in [-7, 7];
  *     asymmetric codes are unsigned in [0, 15].
- *   - Data pointers must be 16-byte aligned (fp32/int32 vectors: 4-byte).
+ *   - Input matrices must be 16-byte aligned; outputs and fp32/int32
+ *     vectors need the alignment of their element type.
  *   - Rounding is round-half-to-even throughout.
  *   - Calls on one stream run in order; the library keeps no state between
  *     calls except the thread-local error string.
@@ -140,7 +141,8 @@ rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw,
 /* rq_w4a4_linear -- y[t][n] = fp16( acc[t][n] * sx[t] * sw[n] ),
  * acc = sum_k qx[t][k] * qw[n][k] in INT32 (QUIK blog part 4), symmetric codes.
  *   qx uint8 [T, K/2], sx fp32 [T], qw uint8 [N, K/2], sw fp32 [N],
- *   y fp16 [T, ldy] (ldy >= N, ldy % 8 == 0).  K % 64 == 0, K > 0, N >= 1.
+ *   y fp16 [T, ldy] (ldy >= N).  K % 64 == 0, 0 < K <= 65536, N >= 1,
+ *   ceil(T/128) <= 65535.
  * The scale product is formed in fp32 and rounded once to fp16. */
 rq_status rq_w4a4_linear(const uint8_t *qx, const float *sx, int64_t T, int64_t K,
                          const uint8_t *qw, const float *sw, int64_t N,
@@ -162,7 +164,7 @@ rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int3
 
 /* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
  * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
- * otherwise signed.  acc int32 [T, ldacc], ldacc >= N, ldacc % 4 == 0. */
+ * otherwise signed.  acc int32 [T, ldacc], ldacc >= N. */
 rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K,
                            const uint8_t *qw, int64_t N, int32_t *acc, int64_t ldacc,
                            void *stream);

@@ -166,22 +166,23 @@ rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw, c
 }
 
 static rq_status check_gemm(const uint8_t *qx, int64_t T, int64_t K, const uint8_t *qw, int64_t N,
-                            const void *out, int64_t ldo, int64_t ld_multiple) {
+                            const void *out, int64_t ldo, size_t out_elem) {
   if (T < 0 || K <= 0 || N < 1) return fail(RQ_EINVAL, "need T >= 0, K > 0, N >= 1");
   if (K % 64) return fail(RQ_ESHAPE, "K=%lld must be a multiple of 64", (long long)K);
   if (K > kMaxK) return fail(RQ_ESHAPE, "K=%lld exceeds %lld", (long long)K, (long long)kMaxK);
-  if ((T + 127) / 128 > 65535 || (N + 127) / 128 > 2147483647LL) return fail(RQ_ESHAPE, "T=%lld exceeds the grid limit", (long long)T);
+  if ((T + 127) / 128 > 65535) return fail(RQ_ESHAPE, "T=%lld exceeds the grid limit", (long long)T);
   if (T > 0) {
     if (!qx || !qw || !out) return fail(RQ_EINVAL, "qx, qw and the output are required");
-    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(out, 16)) return fail(RQ_EALIGN, "qx, qw and the output must be 16-byte aligned");
-    if (ldo < N || ldo % ld_multiple) return fail(RQ_EALIGN, "leading dimension %lld must be >= N and a multiple of %lld", (long long)ldo, (long long)ld_multiple);
+    if (!aligned(qx, 16) || !aligned(qw, 16)) return fail(RQ_EALIGN, "qx and qw must be 16-byte aligned");
+    if (!aligned(out, out_elem)) return fail(RQ_EALIGN, "the output must be aligned to its element size");
+    if (ldo < N) return fail(RQ_EALIGN, "leading dimension %lld must be >= N=%lld", (long long)ldo, (long long)N);
   }
   return ok();
 }
 
 rq_status rq_w4a4_linear(const uint8_t *qx, const float *sx, int64_t T, int64_t K, const uint8_t *qw,
                          const float *sw, int64_t N, void *y, int64_t ldy, void *stream) {
-  rq_status s = check_gemm(qx, T, K, qw, N, y, ldy, 8);
+  rq_status s = check_gemm(qx, T, K, qw, N, y, ldy, 2);
   if (s != RQ_OK) return s;
   if (T == 0) return ok();
   if (!sx || !sw || !aligned(sx, 4) || !aligned(sw, 4)) return fail(RQ_EINVAL, "sx and sw are required (4-byte aligned)");
@@ -194,7 +195,7 @@ rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int3
                                   const int32_t *w_rowsum, int64_t N, const void *x_out,
                                   const void *w_out, int32_t n_out, void *y, int64_t ldy,
                                   void *stream) {
-  rq_status s = check_gemm(qx, T, K_int, qw, N, y, ldy, 8);
+  rq_status s = check_gemm(qx, T, K_int, qw, N, y, ldy, 2);
   if (s != RQ_OK) return s;
   if (n_out < 0 || n_out % 32) return fail(RQ_ESHAPE, "n_out=%d must be a non-negative multiple of 32", n_out);
   if (T == 0) return ok();

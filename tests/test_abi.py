@@ -105,11 +105,12 @@ def test_gemm_validation():
     assert L.rq_w4a4_linear(FAKE, FAKE, 8, 100, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_ESHAPE  # K % 64
     assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 0, FAKE, 16, None) == rq.RQ_EINVAL  # N
     assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 12, None) == rq.RQ_EALIGN  # ldy < N
-    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 20, None) == rq.RQ_EALIGN  # ldy % 8
+    assert L.rq_w4a4_linear(FAKE, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE + 1, 16, None) == rq.RQ_EALIGN  # fp16 y
     assert L.rq_w4a4_linear(FAKE + 8, FAKE, 8, 4096, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_EALIGN
     assert L.rq_w4a4_linear(FAKE, None, 8, 4096, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_EINVAL
     assert L.rq_w4a4_linear(FAKE, FAKE, 8, 131072, FAKE, FAKE, 16, FAKE, 16, None) == rq.RQ_ESHAPE
-    assert L.rq_w4a4_gemm_i32(FAKE, 0, 8, 4096, FAKE, 16, FAKE, 18, None) == rq.RQ_EALIGN     # ldacc % 4
+    assert L.rq_w4a4_gemm_i32(FAKE, 0, 8, 4096, FAKE, 16, FAKE + 2, 16, None) == rq.RQ_EALIGN  # int32 acc
+    assert L.rq_w4a4_gemm_i32(FAKE, 0, 65535 * 128 + 1, 4096, FAKE, 16, FAKE, 16, None) == rq.RQ_ESHAPE
     assert L.rq_mixed_outlier_linear(FAKE, FAKE, FAKE, 8, 7936, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
                                      100, FAKE, 16, None) == rq.RQ_ESHAPE                    # n_out % 32
     assert L.rq_mixed_outlier_linear(FAKE, FAKE, FAKE, 8, 7936, FAKE, FAKE, None, 16, FAKE, FAKE,
