@@ -19,6 +19,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA accumulators in VGPRs (no AGPR copies)
     "-Wall", "-Wno-unused-function",
 ]
 

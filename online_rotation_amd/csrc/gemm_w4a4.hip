@@ -13,16 +13,33 @@
 // (signed) or 15*128 (unsigned), so the INT32 sum cannot overflow for the
 // K <= 65536 the C ABI accepts.
 //
-// Tile: 128 (tokens) x 128 (output channels) per 256-thread workgroup, k-step
-// 128 codes (64 bytes) staged in LDS with double buffering; each wavefront
-// owns a 64 x 64 sub-tile = 2 x 2 MFMA 32x32x32 blocks.
+// Tile: (64*WMB) x (64*WNB) per 256-thread workgroup (2 x 2 wavefronts, each
+// owning WMB x WNB MFMA 32x32x32 blocks).  Each k-step of 128 codes (64 bytes
+// per row) goes global -> registers -> LDS -> registers:
+//   - global loads run kDepth k-steps ahead in a register ring;
+//   - LDS holds three k-steps; during step kb a wavefront multiplies the
+//     fragments of step kb (already in registers), reads step kb+1's
+//     fragments from LDS and stores step kb+2 into LDS;
+//   - one workgroup barrier per step: a buffer is read one step after it
+//     was stored and overwritten two steps after it was read.
 #include "rq_device.h"
 #include "rq_kernels.h"
 
+#include <stdlib.h>
+
 namespace rq {
 
-constexpr int kBM = 128, kBN = 128, kBKB = 64;  // tile rows, cols, k-step bytes
-constexpr int kLdsRow = kBKB + 16;              // padded LDS row (bytes)
+
+constexpr int kBKB = 64;              // k-step: 128 codes = 64 bytes per row
+constexpr int kDepth = 3;             // global prefetch distance in k-steps
+
+// LDS tile rows are 64 bytes (four 16-byte chunks) with the chunk index
+// XOR-swizzled by the row, so that both the cooperative 16-byte stores (four
+// lanes per row) and the per-lane 16-byte fragment reads (one row per lane)
+// touch distinct banks within every group of 8 or 16 lanes.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kBKB + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+}
 
 __device__ __forceinline__ v4i widen_signed(uint32_t w0, uint32_t w1) {
   v4i r;
@@ -42,98 +59,166 @@ __device__ __forceinline__ v4i widen_unsigned(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-template <bool XU, int MODE>
-__global__ __launch_bounds__(256) void gemm_w4a4(GemmArgs p) {
-  __shared__ __align__(16) uint8_t As[2][kBM * kLdsRow];
-  __shared__ __align__(16) uint8_t Bs[2][kBN * kLdsRow];
+// Workgroup id -> output tile.  Consecutive ids go round-robin to the 8
+// XCDs; remapping gives each XCD a contiguous range of positions, and the
+// grouped order walks 8 row-tiles against consecutive column tiles, so the
+// workgroups resident on one XCD share rows and columns in its L2.
+__device__ __forceinline__ void map_tile(int bid, int nt_m, int nt_n, int &tm, int &tn) {
+  const int nt = nt_m * nt_n;
+  int pos = bid;
+  if ((nt & 7) == 0) pos = (bid & 7) * (nt >> 3) + (bid >> 3);
+  constexpr int G = 8;
+  const int group = pos / (G * nt_n);
+  const int first = group * G;
+  const int gsz = min(G, nt_m - first);
+  const int in = pos - group * G * nt_n;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+template <int WMB, int WNB, bool XU, int MODE>
+__global__ __launch_bounds__(256) void gemm_w4a4(GemmArgs p, int nt_m, int nt_n) {
+  constexpr int BM = 64 * WMB, BN = 64 * WNB;
+  constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte chunks per thread per k-step
+  __shared__ __align__(16) uint8_t As[3][BM * kBKB];
+  __shared__ __align__(16) uint8_t Bs[3][BN * kBKB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  int tm, tn;
+  map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t Kb = p.Kb;
-  const int nk = (int)((Kb + kBKB - 1) / kBKB);
+  const int nfull = (int)(Kb / kBKB);               // full 64-byte k-steps
+  const int nsteps = nfull + ((Kb % kBKB) ? 1 : 0);  // plus a last 32-byte half step
 
-  uint4 ra[2], rb[2];
-  auto gload = [&](int kb) {
+  // tile bases are uniform; per-thread 32-bit offsets (rows clamped)
+  const uint8_t *abase = p.qx + m0 * Kb;
+  const uint8_t *bbase = p.qw + n0 * Kb;
+  uint32_t aoff[LA], boff[LB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256, row = c >> 2, cc = c & 3;
-      const int64_t off = (int64_t)kb * kBKB + cc * 16;
-      const int64_t gm = m0 + row, gn = n0 + row;
-      ra[i] = (gm < p.T && off < Kb) ? *reinterpret_cast<const uint4 *>(p.qx + gm * Kb + off)
-                                     : make_uint4(0, 0, 0, 0);
-      rb[i] = (gn < p.N && off < Kb) ? *reinterpret_cast<const uint4 *>(p.qw + gn * Kb + off)
-                                     : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < LA; ++i) {
+    const int c = tid + i * 256;
+    aoff[i] = (uint32_t)((min(m0 + (c >> 2), p.T - 1) - m0) * Kb) + (c & 3) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int c = tid + i * 256;
+    boff[i] = (uint32_t)((min(n0 + (c >> 2), p.N - 1) - n0) * Kb) + (c & 3) * 16;
+  }
+  uint4 ra[kDepth][LA], rb[kDepth][LB];
+  auto gload = [&](int slot, int kb) {
+    const uint8_t *a = abase + (int64_t)kb * kBKB, *b = bbase + (int64_t)kb * kBKB;
+    if (kb < nfull) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ra[slot][i] = *reinterpret_cast<const uint4 *>(a + aoff[i]);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[slot][i] = *reinterpret_cast<const uint4 *>(b + boff[i]);
+    } else {  // half step: chunks 0 and 1 are data, 2 and 3 are zero
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        ra[slot][i] = ((tid + i * 256) & 2) ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4 *>(a + aoff[i]);
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        rb[slot][i] = ((tid + i * 256) & 2) ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4 *>(b + boff[i]);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int slot) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256, row = c >> 2, cc = c & 3;
-      *reinterpret_cast<uint4 *>(&As[buf][row * kLdsRow + cc * 16]) = ra[i];
-      *reinterpret_cast<uint4 *>(&Bs[buf][row * kLdsRow + cc * 16]) = rb[i];
+    for (int i = 0; i < LA; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4 *>(&As[buf][lds_off(c >> 2, c & 3)]) = ra[slot][i];
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4 *>(&Bs[buf][lds_off(c >> 2, c & 3)]) = rb[slot][i];
     }
   };
 
-  v16i acc[2][2];
+  v16i acc[WMB][WNB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WNB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int g = lane >> 5, l32 = lane & 31;
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nk) gload(kb + 1);
-    uint32_t aw[2][8], bw[2][8];
+  uint4 fa[2][WMB][2], fb[2][WNB][2];  // packed fragments of two k-steps
+  auto lread = [&](int f, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint8_t *src = &As[buf][(wm * 64 + i * 32 + l32) * kLdsRow + g * 32];
-      const uint4 x0 = *reinterpret_cast<const uint4 *>(src);
-      const uint4 x1 = *reinterpret_cast<const uint4 *>(src + 16);
-      aw[i][0] = x0.x; aw[i][1] = x0.y; aw[i][2] = x0.z; aw[i][3] = x0.w;
-      aw[i][4] = x1.x; aw[i][5] = x1.y; aw[i][6] = x1.z; aw[i][7] = x1.w;
+    for (int i = 0; i < WMB; ++i) {
+      const int row = wm * 32 * WMB + i * 32 + l32;
+      fa[f][i][0] = *reinterpret_cast<const uint4 *>(&As[buf][lds_off(row, 2 * g)]);
+      fa[f][i][1] = *reinterpret_cast<const uint4 *>(&As[buf][lds_off(row, 2 * g + 1)]);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t *src = &Bs[buf][(wn * 64 + j * 32 + l32) * kLdsRow + g * 32];
-      const uint4 x0 = *reinterpret_cast<const uint4 *>(src);
-      const uint4 x1 = *reinterpret_cast<const uint4 *>(src + 16);
-      bw[j][0] = x0.x; bw[j][1] = x0.y; bw[j][2] = x0.z; bw[j][3] = x0.w;
-      bw[j][4] = x1.x; bw[j][5] = x1.y; bw[j][6] = x1.z; bw[j][7] = x1.w;
+    for (int j = 0; j < WNB; ++j) {
+      const int row = wn * 32 * WNB + j * 32 + l32;
+      fb[f][j][0] = *reinterpret_cast<const uint4 *>(&Bs[buf][lds_off(row, 2 * g)]);
+      fb[f][j][1] = *reinterpret_cast<const uint4 *>(&Bs[buf][lds_off(row, 2 * g + 1)]);
     }
+  };
+  auto compute = [&](int f) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v4i ao[2], bo[2];
+      v4i ao[WMB], bo[WNB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        ao[i] = XU ? widen_unsigned(aw[i][2 * c], aw[i][2 * c + 1])
-                   : widen_signed(aw[i][2 * c], aw[i][2 * c + 1]);
+      for (int i = 0; i < WMB; ++i) {
+        const uint4 &x = fa[f][i][c >> 1];
+        const uint32_t w0 = (c & 1) ? x.z : x.x, w1 = (c & 1) ? x.w : x.y;
+        ao[i] = XU ? widen_unsigned(w0, w1) : widen_signed(w0, w1);
+      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bo[j] = widen_signed(bw[j][2 * c], bw[j][2 * c + 1]);
+      for (int j = 0; j < WNB; ++j) {
+        const uint4 &x = fb[f][j][c >> 1];
+        bo[j] = widen_signed((c & 1) ? x.z : x.x, (c & 1) ? x.w : x.y);
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WMB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < WNB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[i], bo[j], acc[i][j], 0, 0, 0);
     }
-    if (kb + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // prologue: steps 0 and 1 into LDS, step 0's fragments into registers
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s)
+    if (s < nsteps) gload(s, s);
+  sstore(0, 0);
+  if (nsteps > 1) sstore(1, 1);
+  __syncthreads();
+  if (kDepth < nsteps) gload(0, kDepth);
+  if (kDepth + 1 < nsteps) gload(1, kDepth + 1);
+  lread(0, 0);
+  // main loop, unrolled by 6 = lcm(2 fragment sets, 3 LDS buffers, kDepth = 3)
+  for (int kb0 = 0; kb0 < nsteps; kb0 += 6) {
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+      const int kb = kb0 + s;
+      if (kb < nsteps) {
+        if (kb + 1 < nsteps) lread((s + 1) & 1, (s + 1) % 3);
+        compute(s & 1);
+        if (kb + 2 < nsteps) {
+          sstore((s + 2) % 3, (s + 2) % kDepth);
+          if (kb + 2 + kDepth < nsteps) gload((s + 2) % kDepth, kb + 2 + kDepth);
+        }
+        __syncthreads();
+      }
+    }
   }
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   constexpr int kShift = XU ? 4 : 8;
+  const int64_t row0 = m0 + wm * 32 * WMB, col0 = n0 + wn * 32 * WNB;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < WMB; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t gn = n0 + wn * 64 + j * 32 + l32;
-      const int64_t rbase = m0 + wm * 64 + i * 32 + 4 * g;
+    for (int j = 0; j < WNB; ++j) {
+      const int64_t gn = col0 + 32 * j + l32;
+      const int64_t rbase = row0 + 32 * i + 4 * g;
       if (MODE == 0) {
         int32_t *out = reinterpret_cast<int32_t *>(p.out);
 #pragma unroll
@@ -159,16 +244,14 @@ __global__ __launch_bounds__(256) void gemm_w4a4(GemmArgs p) {
         if (MODE == 2 && p.n_out > 0) {
           // FP16 outlier product on FP16 matrix cores, fp32 accumulation on
           // top of the dequantized INT4 part.
-          const int64_t am = m0 + wm * 64 + i * 32 + l32;
-          const int64_t bn = n0 + wn * 64 + j * 32 + l32;
+          const int64_t am = min(row0 + 32 * i + l32, p.T - 1);
+          const int64_t bn = min(col0 + 32 * j + l32, p.N - 1);
           const __half *arow = p.xo + am * p.n_out;
           const __half *brow = p.wo + bn * p.n_out;
           for (int k0 = 0; k0 < p.n_out; k0 += 16) {
             v8h av, bv;
-            uint4 ua = am < p.T ? *reinterpret_cast<const uint4 *>(arow + k0 + g * 8)
-                                : make_uint4(0, 0, 0, 0);
-            uint4 ub = bn < p.N ? *reinterpret_cast<const uint4 *>(brow + k0 + g * 8)
-                                : make_uint4(0, 0, 0, 0);
+            const uint4 ua = *reinterpret_cast<const uint4 *>(arow + k0 + g * 8);
+            const uint4 ub = *reinterpret_cast<const uint4 *>(brow + k0 + g * 8);
             __builtin_memcpy(&av, &ua, 16);
             __builtin_memcpy(&bv, &ub, 16);
             f = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, f, 0, 0, 0);
@@ -185,19 +268,236 @@ __global__ __launch_bounds__(256) void gemm_w4a4(GemmArgs p) {
   }
 }
 
-hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
-  const dim3 grid((unsigned)((p.N + kBN - 1) / kBN), (unsigned)((p.T + kBM - 1) / kBM));
-  const dim3 block(256);
+// ---------------------------------------------------------------------------
+// gemm_wg: the large-T kernel.  Widening int4 to int8 costs VALU work that
+// does not overlap the matrix cores, so each packed chunk is widened once
+// per workgroup on its way into LDS (instead of once per wavefront that
+// reads it), and the wavefronts read ready int8 MFMA operands.
+// Workgroup = 8 wavefronts (4 x 2, each 64 x 64) on a 256 x 128 tile; a
+// k-step is 128 codes: 64 packed bytes per row in global memory, 128 int8
+// bytes per row in LDS.  LDS is double-buffered (96 KB) with one barrier
+// per k-step: step kb+1 is widened and stored while step kb is multiplied.
+// Unpacked rows are 8 slots of 16 bytes; slot s of row r sits at
+// s ^ ((r >> 1) & 7), so the 16 rows a group of 16 lanes touches (reads: one
+// row per lane; stores: four lanes per row) fall in distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kWgBM = 256, kWgBN = 128, kWgRow = 128;
+
+__device__ __forceinline__ int wg_off(int row, int slot) {
+  return row * kWgRow + ((slot ^ ((row >> 1) & 7)) << 4);
+}
+
+template <int MW, bool XU, int MODE>
+__global__ __launch_bounds__(128 * MW) void gemm_wg(GemmArgs p, int nt_m, int nt_n) {
+  // K is a multiple of 128 codes here (whole 64-byte k-steps, no tail).
+  // MW x 2 wavefronts of 64 x 64; tile (64*MW) x 128.
+  constexpr int NT = 128 * MW, BM = 64 * MW, BN = kWgBN, LA = BM * 4 / NT, LB = BN * 4 / NT;
+  constexpr int D = 4;  // global prefetch distance (k-steps); unroll = lcm(D, 2 LDS buffers)
+  __shared__ __align__(16) uint8_t As[2][BM * kWgRow];
+  __shared__ __align__(16) uint8_t Bs[2][BN * kWgRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % MW, wn = wave / MW;
+  int tm, tn;
+  map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t Kb = p.Kb;
+  const int nsteps = (int)(Kb / kBKB);
+
+  const uint8_t *abase = p.qx + m0 * Kb;
+  const uint8_t *bbase = p.qw + n0 * Kb;
+  uint32_t aoff[LA], boff[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int c = tid + i * NT;
+    aoff[i] = (uint32_t)((min(m0 + (c >> 2), p.T - 1) - m0) * Kb) + (c & 3) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int c = tid + i * NT;
+    boff[i] = (uint32_t)((min(n0 + (c >> 2), p.N - 1) - n0) * Kb) + (c & 3) * 16;
+  }
+  // The loop below issues the same loads and stores every step, with no
+  // data-dependent branches around them, so the compiler can wait for just
+  // the oldest prefetch group (a conditional load makes it wait for all).
+  uint4 ra[D][LA], rb[D][LB];
+  auto gload = [&](int slot, int kb) {  // kb is clamped by the caller
+    const uint8_t *a = abase + (int64_t)kb * kBKB, *b = bbase + (int64_t)kb * kBKB;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[slot][i] = *reinterpret_cast<const uint4 *>(a + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[slot][i] = *reinterpret_cast<const uint4 *>(b + boff[i]);
+  };
+  auto widen_store = [&](uint8_t *base, int c, uint4 w, bool xu) {
+    const int row = c >> 2, q = c & 3;
+    const v4i s0 = xu ? widen_unsigned(w.x, w.y) : widen_signed(w.x, w.y);
+    const v4i s1 = xu ? widen_unsigned(w.z, w.w) : widen_signed(w.z, w.w);
+    *reinterpret_cast<v4i *>(base + wg_off(row, 2 * q)) = s0;
+    *reinterpret_cast<v4i *>(base + wg_off(row, 2 * q + 1)) = s1;
+  };
+  auto sstore = [&](int buf, int slot) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) widen_store(As[buf], tid + i * NT, ra[slot][i], XU);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) widen_store(Bs[buf], tid + i * NT, rb[slot][i], false);
+  };
+
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+  const int g = lane >> 5, l32 = lane & 31;
+  auto compute = [&](int buf) {
+    // all 16 fragment reads first, so the MFMAs only wait for the oldest ones
+    v4i ao[4][2], bo[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ao[c][i] = *reinterpret_cast<const v4i *>(&As[buf][wg_off(wm * 64 + i * 32 + l32, 2 * c + g)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bo[c][j] = *reinterpret_cast<const v4i *>(&Bs[buf][wg_off(wn * 64 + j * 32 + l32, 2 * c + g)]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[c][i], bo[c][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int last = nsteps - 1;
+#pragma unroll
+  for (int s = 0; s < D; ++s) gload(s, min(s, last));
+  sstore(0, 0);
+  __syncthreads();
+  gload(0, min(D, last));
+  // steps padded to a multiple of D; padded steps load/store but skip compute
+  for (int kb0 = 0; kb0 < nsteps; kb0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int kb = kb0 + s;
+      sstore((s + 1) & 1, (s + 1) % D);           // step kb+1 (garbage past the end: never used)
+      gload((s + 1) % D, min(kb + 1 + D, last));  // refill the slot just consumed
+      if (kb < nsteps) compute(s & 1);
+      __syncthreads();
+    }
+  }
+
+  // epilogue (same accumulator layout as gemm_w4a4)
+  constexpr int kShift = XU ? 4 : 8;
+  const int64_t row0 = m0 + wm * 64, col0 = n0 + wn * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t gn = col0 + 32 * j + l32;
+      const int64_t rbase = row0 + 32 * i + 4 * g;
+      if (MODE == 0) {
+        int32_t *out = reinterpret_cast<int32_t *>(p.out);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
+          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = acc[i][j][r] >> kShift;
+        }
+      } else {
+        v16f f;
+        const float swn = gn < p.N ? p.sw[gn] : 0.0f;
+        const int32_t rsn = (MODE == 2 && p.zx && gn < p.N) ? p.rowsum[gn] : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
+          int32_t v = acc[i][j][r] >> kShift;
+          float sxm = 0.0f;
+          if (gm < p.T) {
+            sxm = p.sx[gm];
+            if (MODE == 2 && p.zx) v -= p.zx[gm] * rsn;
+          }
+          f[r] = (float)v * sxm * swn;
+        }
+        if (MODE == 2 && p.n_out > 0) {
+          const int64_t am = min(row0 + 32 * i + l32, p.T - 1);
+          const int64_t bn = min(col0 + 32 * j + l32, p.N - 1);
+          const __half *arow = p.xo + am * p.n_out;
+          const __half *brow = p.wo + bn * p.n_out;
+          for (int k0 = 0; k0 < p.n_out; k0 += 16) {
+            v8h av, bv;
+            const uint4 ua = *reinterpret_cast<const uint4 *>(arow + k0 + g * 8);
+            const uint4 ub = *reinterpret_cast<const uint4 *>(brow + k0 + g * 8);
+            __builtin_memcpy(&av, &ua, 16);
+            __builtin_memcpy(&bv, &ub, 16);
+            f = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, f, 0, 0, 0);
+          }
+        }
+        __half *out = reinterpret_cast<__half *>(p.out);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
+          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(f[r]);
+        }
+      }
+    }
+  }
+}
+
+template <int MW>
+static hipError_t launch_wg(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  constexpr int BM = 64 * MW;
+  const int nt_m = (int)((p.T + BM - 1) / BM), nt_n = (int)((p.N + kWgBN - 1) / kWgBN);
+  const dim3 grid((unsigned)(nt_m * nt_n)), block(128 * MW);
   if (mode == 0) {
-    if (x_unsigned) gemm_w4a4<true, 0><<<grid, block, 0, st>>>(p);
-    else gemm_w4a4<false, 0><<<grid, block, 0, st>>>(p);
+    if (x_unsigned) gemm_wg<MW, true, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_wg<MW, false, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   } else if (mode == 1) {
-    gemm_w4a4<false, 1><<<grid, block, 0, st>>>(p);
+    gemm_wg<MW, false, 1><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   } else {
-    if (x_unsigned) gemm_w4a4<true, 2><<<grid, block, 0, st>>>(p);
-    else gemm_w4a4<false, 2><<<grid, block, 0, st>>>(p);
+    if (x_unsigned) gemm_wg<MW, true, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_wg<MW, false, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   }
   return hipGetLastError();
+}
+
+template <int WMB, int WNB>
+static hipError_t launch_tiles(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  constexpr int BM = 64 * WMB, BN = 64 * WNB;
+  const int nt_m = (int)((p.T + BM - 1) / BM), nt_n = (int)((p.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(nt_m * nt_n)), block(256);
+  if (mode == 0) {
+    if (x_unsigned) gemm_w4a4<WMB, WNB, true, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_w4a4<WMB, WNB, false, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else if (mode == 1) {
+    gemm_w4a4<WMB, WNB, false, 1><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else {
+    if (x_unsigned) gemm_w4a4<WMB, WNB, true, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_w4a4<WMB, WNB, false, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  }
+  return hipGetLastError();
+}
+
+static int gemm_variant() {
+  static int v = [] {
+    const char *e = getenv("RQ_GEMM_VARIANT");
+    return e ? atoi(e) : 1;
+  }();
+  return v;
+}
+
+hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  switch (gemm_variant()) {
+    case 2: return launch_tiles<4, 2>(p, x_unsigned, mode, st);
+    case 3: return launch_tiles<2, 4>(p, x_unsigned, mode, st);
+    case 4: return launch_tiles<2, 2>(p, x_unsigned, mode, st);
+    case 5:
+      return (p.T >= 128 && p.Kb % kBKB == 0) ? launch_wg<2>(p, x_unsigned, mode, st)
+                                              : launch_tiles<2, 2>(p, x_unsigned, mode, st);
+    default:
+      return (p.T >= 256 && p.Kb % kBKB == 0) ? launch_wg<4>(p, x_unsigned, mode, st)
+                                              : launch_tiles<2, 2>(p, x_unsigned, mode, st);
+  }
 }
 
 }  // namespace rq

@@ -163,6 +163,305 @@ __global__ __launch_bounds__(256) void fwht4096_quant(const __half *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// fwht4096_mfma: the same transforms on FP16 matrix cores.
+//
+// A 4096-wide row viewed as M[a][b] = x[64a + b] (64 x 64).  Since
+// H_4096 = H_64 kron H_64, x . H_4096 / 64 = H_64 . M . H_64 / 64, two 64^3
+// products; a GSR row with blocks of B <= 64 is the single product M . G,
+// G = blockdiag(Wal_B).  Both run on v_mfma_f32_32x32x16_f16:
+//   - the fp16 input is exact as an MFMA operand and +-2^k are exact fp16
+//     values, so the first product only rounds in its fp32 accumulation;
+//   - the second Hadamard product takes its fp32 input as hi + lo fp16
+//     (hi rounded to nearest, lo the remainder), 2^-22 relative.  So that lo
+//     never falls into fp16 subnormals, the first product is scaled by a
+//     per-row power of two chosen from the exponent of max|x| (exact), which
+//     puts the largest intermediate just below 2^15; the quantizer divides
+//     it out again (exact).
+// Constant operands come from compile-time sign tables (16 bytes per lane).
+// Output layout (both cases): accumulator [mb][nb] register r of lane
+// (r32, g) holds element 64*(r32 + 32*nb) + 32*mb + 8*(r/4) + 4*g + r%4,
+// so four consecutive elements share a lane and a lane pair (l, l+32)
+// swaps halves (v_permlane32_swap) into 16 contiguous packed bytes.
+// ---------------------------------------------------------------------------
+constexpr int cpopc(uint32_t v) {
+  int c = 0;
+  while (v) {
+    c += (int)(v & 1u);
+    v >>= 1;
+  }
+  return c;
+}
+constexpr uint32_t cbitrev(uint32_t v, int bits) {
+  uint32_t r = 0;
+  for (int i = 0; i < bits; ++i) r |= ((v >> i) & 1u) << (bits - 1 - i);
+  return r;
+}
+
+struct OpTab {
+  uint32_t w[8][64][4];  // [operand][lane][dword]: 8 fp16 values per lane
+};
+
+// Step 1 of the Hadamard product, B = H_64: operand (cb, kc) of lane
+// (r32, g) is column b' = r32 + 32*cb, slot s is row b = 16*kc + 8*g + s.
+// Only the sign bits are stored; the kernel ORs in a per-row magnitude.
+constexpr OpTab make_had1() {
+  OpTab t{};
+  for (int cb = 0; cb < 2; ++cb)
+    for (int kc = 0; kc < 4; ++kc)
+      for (int l = 0; l < 64; ++l)
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t col = (l & 31) + 32 * cb, b = 16 * kc + 8 * (l >> 5) + s;
+          const uint32_t sign = (uint32_t)(cpopc(b & col) & 1);
+          t.w[cb * 4 + kc][l][s / 2] |= (sign << 15) << (16 * (s & 1));
+        }
+  return t;
+}
+// Step 2, B = H_64 (+-1): operand (nb, rb, c) of lane (r32, g) is column
+// a' = r32 + 32*nb; slot s is row a = 32*rb + 16*c + 8*(s/4) + 4*g + s%4,
+// the row the step-1 accumulator register 8*c + s of that lane holds.
+constexpr OpTab make_had2() {
+  OpTab t{};
+  for (int nb = 0; nb < 2; ++nb)
+    for (int rb = 0; rb < 2; ++rb)
+      for (int c = 0; c < 2; ++c)
+        for (int l = 0; l < 64; ++l)
+          for (int s = 0; s < 8; ++s) {
+            const uint32_t col = (l & 31) + 32 * nb;
+            const uint32_t a = 32 * rb + 16 * c + 8 * (s >> 2) + 4 * (l >> 5) + (s & 3);
+            const uint32_t v = 0x3C00u | ((uint32_t)(cpopc(a & col) & 1) << 15);
+            t.w[(nb * 2 + rb) * 2 + c][l][s / 2] |= v << (16 * (s & 1));
+          }
+  return t;
+}
+// GSR, A = G^T with G = blockdiag(Wal_B): operand (mb, kc) of lane (r32, g)
+// is output j = r32 + 32*mb, slot s is input b = 16*kc + 8*g + s;
+// G[b][j] = H_B[sigma(b%B)][j%B] inside a block (sigma = bitrev o gray:
+// row sigma(s) of H_B is the one with s sign changes), 0 across blocks.
+constexpr OpTab make_gsr(int blog2) {
+  OpTab t{};
+  const uint32_t B = 1u << blog2, bm = B - 1;
+  for (int mb = 0; mb < 2; ++mb)
+    for (int kc = 0; kc < 4; ++kc)
+      for (int l = 0; l < 64; ++l)
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t j = (l & 31) + 32 * mb, b = 16 * kc + 8 * (l >> 5) + s;
+          uint32_t v = 0;
+          if ((b >> blog2) == (j >> blog2)) {
+            const uint32_t bl = b & bm, sig = cbitrev(bl ^ (bl >> 1), blog2);
+            v = 0x3C00u | ((uint32_t)(cpopc(sig & (j & bm)) & 1) << 15);
+          }
+          t.w[mb * 4 + kc][l][s / 2] |= v << (16 * (s & 1));
+        }
+  return t;
+}
+
+__device__ const OpTab kHad1 = make_had1();
+__device__ const OpTab kHad2 = make_had2();
+__device__ const OpTab kGsr8 = make_gsr(3);
+__device__ const OpTab kGsr16 = make_gsr(4);
+__device__ const OpTab kGsr32 = make_gsr(5);
+__device__ const OpTab kGsr64 = make_gsr(6);
+
+__device__ __forceinline__ uint4 tab_load(const OpTab &t, int op, int lane) {
+  return *reinterpret_cast<const uint4 *>(&t.w[op][lane][0]);
+}
+
+__device__ __forceinline__ v8h as_h8(uint4 u) {
+  v8h h;
+  __builtin_memcpy(&h, &u, 16);
+  return h;
+}
+
+__device__ __forceinline__ v16f mfma16(uint4 a, uint4 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+}
+
+// Split eight fp32 values into fp16 hi (nearest) and lo (remainder) operands.
+__device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 a = (_Float16)f[2 * j], b = (_Float16)f[2 * j + 1];
+    const float ra = f[2 * j] - (float)a, rb = f[2 * j + 1] - (float)b;
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    h[j] = (uint32_t)ua | ((uint32_t)ub << 16);
+    auto pr = __builtin_amdgcn_cvt_pkrtz(ra, rb);
+    __builtin_memcpy(&l[j], &pr, 4);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  return v;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// 1.5 * 2^23 + 8: fma(v, inv, kMagic8) = kMagic8 + rne(v*inv) for |v*inv| < 2^22,
+// so the low nibble of the result's bit pattern is the code + 8.
+constexpr float kMagic8 = 12582920.0f;
+
+template <bool GSR, bool CSUM>
+__global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ x, int64_t T,
+                                                     int64_t ldx, uint8_t *__restrict__ q,
+                                                     float *__restrict__ scale,
+                                                     int32_t *__restrict__ code_sum, float clip,
+                                                     int blog2, float norm) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int r32 = lane & 31, g = lane >> 5;
+  const __half *row = x + t * ldx;
+
+  uint4 mop[2][4];  // M[a = r32 + 32*rb][b = 16*kc + 8*g + s], s = 0..7
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      mop[rb][kc] = *reinterpret_cast<const uint4 *>(row + 64 * (r32 + 32 * rb) + 16 * kc + 8 * g);
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  float nrm = norm;
+
+  if (GSR) {
+    // C[j][a] = sum_b G[b][j] M[a][b]: A = G^T (table), B = M (column a = lane).
+    const OpTab &tab = blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint4 a = tab_load(tab, mb * 4 + kc, lane);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, mop[nb][kc], acc[mb][nb]);
+      }
+  } else {
+    // per-row scale 2^sx: step-1 operand magnitude 2^(te-15), te = min(38 - e, 30)
+    // with e the fp16 exponent field of max|x|, so |P * 2^sx| < 2^15.
+    uint32_t mx = 0;
+    {
+      u16x2 m2 = {0, 0};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint32_t d[4] = {mop[rb][kc].x, mop[rb][kc].y, mop[rb][kc].z, mop[rb][kc].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u16x2 v;
+            const uint32_t dm = d[i] & 0x7FFF7FFFu;
+            __builtin_memcpy(&v, &dm, 4);
+            m2 = __builtin_elementwise_max(m2, v);
+          }
+        }
+      mx = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+    }
+    const int e = (int)((mx >> 10) & 0x1Fu);
+    const int te = min(38 - e, 30);
+    const uint32_t mag = (uint32_t)te << 10, magd = mag | (mag << 16);
+    nrm = __builtin_ldexpf(1.0f, 9 - te);  // undoes 2^(te - 9)
+    // step 1: P = M . H_64 * 2^(te-15), lanes <-> column b', registers <-> row a
+    v16f p[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[rb][cb][r] = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        uint4 hb = tab_load(kHad1, cb * 4 + kc, lane);
+        hb.x |= magd;
+        hb.y |= magd;
+        hb.z |= magd;
+        hb.w |= magd;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) p[rb][cb] = mfma16(mop[rb][kc], hb, p[rb][cb]);
+      }
+    }
+    // step 2: Y^T[b'][a'] = sum_a P[a][b'] H_64[a][a'] with A = P^T taken
+    // straight from the step-1 accumulators.
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float f[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) f[s] = p[rb][mb][8 * c + s];
+          uint4 hi, lo;
+          split8(f, hi, lo);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const uint4 hb = tab_load(kHad2, (nb * 2 + rb) * 2 + c, lane);
+            acc[mb][nb] = mfma16(hi, hb, acc[mb][nb]);
+            acc[mb][nb] = mfma16(lo, hb, acc[mb][nb]);
+          }
+        }
+      }
+    }
+  }
+
+  // per-row symmetric scale from the normalized absmax
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][j][r]));
+  amax = wave_max(amax) * nrm;
+  float s, inv;
+  sym_scale(amax, clip, s, inv);
+  const float invn = inv * nrm;
+  const float lo_c = kMagic8 - 7.0f, hi_c = kMagic8 + 7.0f;
+  float csum = 0.0f;
+  uint8_t *qrow = q + t * 2048;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    uint32_t d[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      uint32_t h[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        uint32_t bits[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float f = __builtin_fmaf(acc[mb][nb][4 * j4 + i], invn, kMagic8);
+          f = __builtin_amdgcn_fmed3f(f, lo_c, hi_c);
+          if (CSUM) csum += f - kMagic8;
+          __builtin_memcpy(&bits[i], &f, 4);
+        }
+        // low byte of bits[i] is code+8 in [1, 15]; pack pairs, then bytes
+        const uint32_t p01 = (bits[1] << 4) | bits[0];
+        const uint32_t p23 = (bits[3] << 4) | bits[2];
+        h[mb] = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);
+      }
+      auto sw = __builtin_amdgcn_permlane32_swap(h[0], h[1], false, false);
+      d[j4] = ((uint32_t)sw[0] | ((uint32_t)sw[1] << 16)) ^ 0x88888888u;  // offset -> two's complement
+    }
+    *reinterpret_cast<uint4 *>(qrow + 32 * (r32 + 32 * nb) + 16 * g) = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+  if (CSUM) {
+    const int cs = wave_sum((int)csum);
+    if (lane == 0) code_sum[t] = cs;
+  }
+  if (lane == 0) scale[t] = s;
+}
+
+// ---------------------------------------------------------------------------
 // rowlds_quant: one workgroup (256 threads) per row, grid-stride over rows.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
@@ -477,6 +776,20 @@ hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int 
                            float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                            hipStream_t st) {
   const int64_t blocks = (T + kF4096Waves - 1) / kF4096Waves;
+  const bool had = !gsr && span_log2 == 12, gsr_mfma = gsr && span_log2 >= 3 && span_log2 <= 6;
+  if (had || gsr_mfma) {
+    const dim3 grid((unsigned)blocks), block(256);
+    const __half *xh = (const __half *)x;
+    if (had && code_sum)
+      fwht4096_mfma<false, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f);
+    else if (had)
+      fwht4096_mfma<false, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f);
+    else if (code_sum)
+      fwht4096_mfma<true, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+    else
+      fwht4096_mfma<true, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+    return hipGetLastError();
+  }
   if (gsr)
     fwht4096_quant<true><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
         (const __half *)x, T, ldx, q, scale, code_sum, clip, span_log2, norm);

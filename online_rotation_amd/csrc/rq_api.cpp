@@ -170,7 +170,8 @@ static rq_status check_gemm(const uint8_t *qx, int64_t T, int64_t K, const uint8
   if (T < 0 || K <= 0 || N < 1) return fail(RQ_EINVAL, "need T >= 0, K > 0, N >= 1");
   if (K % 64) return fail(RQ_ESHAPE, "K=%lld must be a multiple of 64", (long long)K);
   if (K > kMaxK) return fail(RQ_ESHAPE, "K=%lld exceeds %lld", (long long)K, (long long)kMaxK);
-  if ((T + 127) / 128 > 65535) return fail(RQ_ESHAPE, "T=%lld exceeds the grid limit", (long long)T);
+  if ((T + 127) / 128 > 65535 || ((T + 63) / 64) * ((N + 63) / 64) > 2147483647LL)
+    return fail(RQ_ESHAPE, "T=%lld, N=%lld exceed the grid limit", (long long)T, (long long)N);
   if (T > 0) {
     if (!qx || !qw || !out) return fail(RQ_EINVAL, "qx, qw and the output are required");
     if (!aligned(qx, 16) || !aligned(qw, 16)) return fail(RQ_EALIGN, "qx and qw must be 16-byte aligned");

@@ -48,6 +48,9 @@ QUANT_CASES = [
     ("gsr64-4096-clip", "gsr", 301, 4096, "gsr", 64, 0.9, 0),
     ("gsr16-4096", "gsr", 37, 4096, "gsr", 16, 1.0, 0),
     ("gsr256-4096", "gsr", 37, 4096, "gsr", 256, 1.0, 0),
+    ("gsr8-4096", "gsr", 37, 4096, "gsr", 8, 1.0, 0),
+    ("gsr32-4096-clip", "gsr", 37, 4096, "gsr", 32, 0.9, 0),
+    ("gsr128-4096", "gsr", 37, 4096, "gsr", 128, 1.0, 0),
     ("gsr64-1024-rowlds", "gsr", 41, 1024, "gsr", 64, 0.9, 0),
     ("had64-rowlds", "llama7b", 33, 64, "hadamard", 0, 1.0, 0),
     ("had1024-rowlds", "llama7b", 33, 1024, "hadamard", 0, 1.0, 0),
@@ -146,7 +149,7 @@ def test_prepare_weights_matches_oracle(case):
 # ----------------------------------------------------------------------------- GEMM
 
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
-               (8, 300, 8192)]
+               (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -161,7 +164,7 @@ def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
     assert np.array_equal(host(acc), o.int_gemm(qx, qw))
 
 
-@pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968)])
+@pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032)])
 def test_linear_epilogue_on_oracle_codes(T, N, K):
     note(f"[w4a4_linear] T={T} N={N} K={K}")
     rng = np.random.default_rng(K + T)
@@ -172,7 +175,8 @@ def test_linear_epilogue_on_oracle_codes(T, N, K):
     check_y(host(y), o.dequant_sym(o.int_gemm(qx, qw), sx, sw))
 
 
-@pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False)])
+@pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False),
+                                            (300, 150, 256, True), (260, 70, 32, False)])
 def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     note(f"[mixed_linear] T={T} N={N} n_out={n_out} asym={asym}")
     K = 7936
