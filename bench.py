@@ -36,8 +36,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama7b", choices=["llama7b", "gsr", "flat"])
-    ap.add_argument("--sets", type=int, default=24, help="buffer sets cycled per step")
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode"])
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled per step (0: >640 MB)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -56,13 +57,14 @@ def cpu_baseline(inp, wl, seconds):
     kw = {"block": wl.block} if kind == "gsr" else {}
     if kind == "kron":
         kw = {"p1": inp["p1"], "p2": inp["p2"], "chan_scale": inp["s"]}
-    wq = o.prepare_weights(inp["w"], kind, **kw)          # offline side, untimed
-    ts = min(256, wl.T)
+    idx = inp["outlier_ch"] if wl.asym else None
+    wq = o.prepare_weights(inp["w"], kind, outlier_idx=idx, **kw)   # offline side, untimed
+    ts = min(256, inp["x"].shape[0])
     xs = inp["x"][:ts]
     runs = 0
     t0 = time.perf_counter()
     while True:
-        xq = o.rotate_quant(xs, kind, clip=wl.clip_x, **kw)
+        xq = o.rotate_quant(xs, kind, clip=wl.clip_x, asym=wl.asym, outlier_idx=idx, **kw)
         o.linear(xq, wq)
         runs += 1
         el = time.perf_counter() - t0
@@ -70,7 +72,7 @@ def cpu_baseline(inp, wl, seconds):
             break
     ops = 2.0 * ts * wl.N * wl.K * runs
     return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"{ts} of {wl.T} tokens of the {wl.name} workload (full K={wl.K}, N={wl.N}), "
+            "sample": f"{ts} of {inp['x'].shape[0]} tokens of the {wl.name} workload (full K={wl.K}, N={wl.N}), "
                       f"rotate+quantize+INT GEMM+dequant, {runs} runs in {el:.1f} s; weight prep untimed"}
 
 
@@ -99,23 +101,40 @@ def main():
 
     x0 = torch.from_numpy(inp["x"]).to(dev)
     w0 = torch.from_numpy(inp["w"]).to(dev)
-    wq0 = rq.rq_prepare_weights(w0, rot)                   # offline weight side
+    T = x0.shape[0]
+    mixed = wl.asym
+    idx = torch.from_numpy(inp["outlier_ch"]).to(dev) if mixed else None
+    n_out = wl.n_out if mixed else 0
+    Kq = K - n_out                                       # codes per row through the INT4 path
+    wq0 = rq.rq_prepare_weights(w0, rot, outlier_idx=idx)  # offline weight side
+    del w0
     torch.cuda.synchronize()
 
-    S = args.sets
+    # enough buffer sets that inputs come from HBM, not the 256 MB Infinity Cache
+    w_bytes = N * Kq // 2 + N * 4 + (N * 4 + N * n_out * 2 if mixed else 0)
+    x_bytes = T * K * 2 + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
+    S = args.sets if args.sets > 0 else max(2, -(-(640 << 20) // (w_bytes + x_bytes)))
     xs = [x0.clone() for _ in range(S)]
-    qws = [wq0["q"].clone() for _ in range(S)]
-    sws = [wq0["scale"].clone() for _ in range(S)]
-    xq = [{"q": torch.empty((T, K // 2), dtype=torch.uint8, device=dev),
-           "scale": torch.empty((T,), dtype=torch.float32, device=dev)} for _ in range(S)]
+    wqs = [{k: (v.clone() if v is not None and k != "_workspace" else v) for k, v in wq0.items()}
+           for _ in range(S)]
+    xq = [{"q": torch.empty((T, Kq // 2), dtype=torch.uint8, device=dev),
+           "scale": torch.empty((T,), dtype=torch.float32, device=dev),
+           "zero": torch.empty((T,), dtype=torch.int32, device=dev) if mixed else None,
+           "x_out": torch.empty((T, n_out), dtype=torch.float16, device=dev) if mixed else None}
+          for _ in range(S)]
     ys = [torch.empty((T, N), dtype=torch.float16, device=dev) for _ in range(S)]
-    footprint = S * (T * K * 2 + T * K // 2 + T * 4 + N * K // 2 + N * 4 + T * N * 2)
+    footprint = S * (w_bytes + x_bytes)
 
     def rotate(i):
-        rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, out=xq[i])
+        rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, asym=mixed, outlier_idx=idx, out=xq[i])
 
     def gemm(i):
-        rq.rq_w4a4_linear(xq[i]["q"], xq[i]["scale"], qws[i], sws[i], out=ys[i])
+        if mixed:
+            rq.rq_mixed_outlier_linear(xq[i]["q"], xq[i]["scale"], xq[i]["zero"], wqs[i]["q"],
+                                       wqs[i]["scale"], wqs[i]["rowsum"], xq[i]["x_out"],
+                                       wqs[i]["w_out"], out=ys[i])
+        else:
+            rq.rq_w4a4_linear(xq[i]["q"], xq[i]["scale"], wqs[i]["q"], wqs[i]["scale"], out=ys[i])
 
     def step(i):
         rotate(i)
@@ -140,8 +159,9 @@ def main():
         return g
 
     g_step = capture(step, args.steps)
-    g_rot = capture(rotate, S * 4)
-    g_gemm = capture(gemm, S * 4)
+    reps_per_graph = max(S, 32)
+    g_rot = capture(rotate, reps_per_graph)
+    g_gemm = capture(gemm, reps_per_graph)
 
     # graph replays reproduce the eager result (checked on every replay)
     for _ in range(2):
@@ -177,13 +197,15 @@ def main():
     torch.cuda.synchronize()
     step_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
-    rot_s = timed(g_rot, S * 4, args.reps)
-    gemm_s = timed(g_gemm, S * 4, args.reps)
+    rot_s = timed(g_rot, reps_per_graph, args.reps)
+    gemm_s = timed(g_gemm, reps_per_graph, args.reps)
 
-    ops = 2.0 * T * N * K
-    rq_bytes = T * K * 2 + T * (K // 2) + T * 4
+    ops = 2.0 * T * N * Kq + 2.0 * T * N * n_out      # INT4 part + fp16 outlier part
+    rq_bytes = T * K * 2 + T * (Kq // 2) + T * 4 + (T * 4 + T * n_out * 2 if mixed else 0)
     gemm_tops = ops / gemm_s / 1e12
     rq_gbs = rq_bytes / rot_s / 1e9
+    gemm_bytes = w_bytes + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
+    decode = T <= 64                                  # weight-streaming regime
     rec = {
         "metric": METRIC,
         "value": round(ops / step_s / 1e12, 2),
@@ -197,15 +219,22 @@ def main():
         "vs_baseline": None,
         "dtype": "int4",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: rotate({wl.rot}) + per-token INT4 + W4A4 linear, "
-                               f"X fp16 [{T},{K}], W int4 [{N},{K}]",
-                   "T": T, "K": K, "N": N, "rotation": wl.rot, "block": wl.block,
+        "config": {"workload": f"{wl.name}: rotate({wl.rot}) + per-token INT4"
+                               f"{' asymmetric + fp16 outliers' if mixed else ''} + W4A4 linear, "
+                               f"X fp16 [{T},{K}], W int4 [{N},{Kq}]" + (f" + fp16 [{N},{n_out}]" if mixed else ""),
+                   "T": T, "K": K, "N": N, "rotation": wl.rot, "block": wl.block, "n_out": n_out,
                    "clip_x": wl.clip_x, "buffer_sets": S, "footprint_MB": round(footprint / 2**20)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_w4a4", "achieved": round(gemm_tops, 1),
-                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
-                     "avg_launch_us": round(gemm_s * 1e6, 3)},
-        "rotate_quant": {"bound": "hbm", "kernel": "fwht4096_quant" if wl.rot != "kron" else "kron_quant",
+        "roofline": ({"bound": "hbm", "kernel": "gemm_w4a4", "achieved": round(gemm_bytes / gemm_s / 1e9, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gemm_bytes / gemm_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                      "bytes_per_launch": gemm_bytes, "avg_launch_us": round(gemm_s * 1e6, 3)}
+                     if decode else
+                     {"bound": "mfma", "kernel": "gemm_w4a4", "achieved": round(gemm_tops, 1),
+                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                      "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                      "avg_launch_us": round(gemm_s * 1e6, 3)}),
+        "rotate_quant": {"bound": "hbm", "kernel": {"hadamard": "fwht4096_mfma", "gsr": "fwht4096_mfma",
+                                                   "kron": "kron_quant", "none": "rowlds_quant"}[wl.rot],
                          "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(rq_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": rq_bytes,
                          "avg_launch_us": round(rot_s * 1e6, 3)},

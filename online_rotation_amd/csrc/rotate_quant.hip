@@ -462,6 +462,229 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// split_quant: no rotation (QUIK), K <= 8192 and K % 32 == 0.  Thread t of a
+// 256-thread workgroup owns columns [32t, 32t+32) of every row it quantizes.
+// Once per workgroup: a bit mask of the outlier columns, its per-word
+// exclusive prefix counts (a block scan) and, per thread, an AND mask that
+// zeroes the thread's outlier halves.  Zeroed outliers leave
+// min(min x, 0) and max(max x, 0) -- and the absolute maximum -- unchanged,
+// so the per-row reductions need no per-value test.  Per row the thread
+// quantizes its 32 values (one fma against a zero-point-shifted magic
+// number, one clamp), deletes its outlier nibbles from the 128-bit code run
+// and ORs the run into a packed row in LDS at its compacted nibble offset;
+// the packed row is then copied out with coalesced stores.
+// ---------------------------------------------------------------------------
+constexpr int kSplitThreads = 256;
+constexpr float kMagic0 = 12582912.0f;  // 1.5 * 2^23
+
+// delete nibble `b` (0..31) of the 128-bit value w (w[0] lowest), shifting the
+// higher nibbles down by one
+__device__ __forceinline__ void del_nibble(uint32_t *w, int b) {
+  const int wi = b >> 3, sh = (b & 7) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hi_in = i < 3 ? (w[i + 1] << 28) : 0u;
+    const uint32_t shifted = (w[i] >> 4) | hi_in;
+    if (i > wi) {
+      w[i] = shifted;
+    } else if (i == wi) {
+      const uint32_t keep = sh ? ((1u << sh) - 1u) : 0u;
+      w[i] = (w[i] & keep) | (shifted & ~keep);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSplitThreads) void split_quant(
+    const __half *__restrict__ x, int64_t T, int K, int64_t ldx, int asym, float clip,
+    const int32_t *__restrict__ outlier_idx, int n_out, uint8_t *__restrict__ q,
+    float *__restrict__ scale, int32_t *__restrict__ zero, int32_t *__restrict__ code_sum,
+    __half *__restrict__ x_out) {
+  __shared__ uint32_t mask[kSplitThreads];
+  __shared__ int wsum[4];
+  __shared__ uint32_t packed[kSplitThreads * 4 + 1];  // packed codes of one row (+1 spill word)
+  __shared__ float redf[8];
+  __shared__ int redi[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = K / 32;  // mask words == active threads
+  const int Kn = K - n_out;
+  const bool active = tid < nw;
+
+  // ---- per-workgroup setup
+  mask[tid] = 0u;
+  __syncthreads();
+  for (int j = tid; j < n_out; j += kSplitThreads) {
+    const int c = outlier_idx[j];
+    if (c >= 0 && c < K) atomicOr(&mask[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  const uint32_t m = mask[tid];
+  const int cnt = active ? __popc(m) : 0;
+  // exclusive prefix of cnt over threads (wave scan + 4 wave totals)
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = incl - cnt;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int pos0 = 32 * tid - before;  // compacted nibble position of this thread's first normal column
+  uint32_t keep[16];                   // AND masks zeroing the thread's outlier halves
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    keep[i] = (((m >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) | (((m >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
+  const int nwords = (Kn + 7) / 8;  // packed row words
+  for (int i = tid; i < kSplitThreads * 4 + 1; i += kSplitThreads) packed[i] = 0u;
+  __syncthreads();
+
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const __half *row = x + t * ldx;
+    uint32_t d[16];
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(row + 32 * tid + 8 * i);
+        d[4 * i] = u.x; d[4 * i + 1] = u.y; d[4 * i + 2] = u.z; d[4 * i + 3] = u.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d[i] &= keep[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d[i] = 0u;
+    }
+    // per-thread min / max (or absmax) on packed fp16, then the block reduction
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 mn2 = {0, 0}, mx2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f16x2 h;
+      __builtin_memcpy(&h, &d[i], 4);
+      if (!asym) h = __builtin_elementwise_abs(h);
+      mn2 = __builtin_elementwise_min(mn2, h);
+      mx2 = __builtin_elementwise_max(mx2, h);
+    }
+    float mn = fminf((float)mn2.x, (float)mn2.y);
+    float mx = fmaxf((float)mx2.x, (float)mx2.y);
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      redf[wave] = mn;
+      redf[4 + wave] = mx;
+    }
+    __syncthreads();
+    mn = fminf(fminf(redf[0], redf[1]), fminf(redf[2], redf[3]));
+    mx = fmaxf(fmaxf(redf[4], redf[5]), fmaxf(redf[6], redf[7]));
+    float s, inv, base, lo_c, hi_c;
+    int zp = 0;
+    if (asym) {
+      asym_params(mn, mx, s, inv, zp);
+      base = kMagic0 + (float)zp;      // code = clamp(rne(x/s) + zero, 0, 15)
+      lo_c = kMagic0;
+      hi_c = kMagic0 + 15.0f;
+    } else {
+      sym_scale(mx, clip, s, inv);
+      base = kMagic8;                  // low nibble = code + 8
+      lo_c = kMagic8 - 7.0f;
+      hi_c = kMagic8 + 7.0f;
+    }
+    int csum = 0;
+    if (active) {
+      uint32_t w[4];
+      float fsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const __half2 h = *reinterpret_cast<const __half2 *>(&d[4 * i + j]);
+          const float2 f = __half22float2(h);
+          const float q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(f.x, inv, base), lo_c, hi_c);
+          const float q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(f.y, inv, base), lo_c, hi_c);
+          fsum += (q0 - base) + (q1 - base);
+          uint32_t b0, b1;
+          __builtin_memcpy(&b0, &q0, 4);
+          __builtin_memcpy(&b1, &q1, 4);
+          wd |= ((b0 & 0xFu) | ((b1 & 0xFu) << 4)) << (8 * j);
+        }
+        w[i] = asym ? wd : (wd ^ 0x88888888u);  // symmetric: offset-8 nibble -> two's complement
+      }
+      // the run of this thread's normal-column codes, outliers deleted
+      uint32_t mm = m;
+      while (mm) {
+        const int b = 31 - __clz(mm);  // highest first, so lower positions stay put
+        del_nibble(w, b);
+        mm &= ~(1u << b);
+      }
+      // fsum is the sum of (code - zero) over all 32 values; the zeroed
+      // outliers contribute exactly 0 to it
+      csum = (int)fsum + (asym ? zp * (32 - cnt) : 0);
+      // place the run (32 - cnt nibbles) at nibble position pos0
+      const int sh = (pos0 & 7) * 4, w0i = pos0 >> 3;
+      const int nrun = 32 - cnt;
+      uint32_t out[5];
+      // clear nibbles beyond the run
+      if (nrun < 32) {
+        const int wi = nrun >> 3, bi = (nrun & 7) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i > wi) w[i] = 0u;
+          else if (i == wi) w[i] &= bi ? ((1u << bi) - 1u) : 0u;
+        }
+      }
+      out[0] = w[0] << sh;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) out[i] = (w[i] << sh) | (sh ? (w[i - 1] >> (32 - sh)) : 0u);
+      out[4] = sh ? (w[3] >> (32 - sh)) : 0u;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        if (out[i]) atomicOr(&packed[w0i + i], out[i]);
+      // outlier columns keep their fp16 bits
+      if (n_out) {
+        uint32_t mo = m;
+        int r = before;
+        while (mo) {
+          const int b = __ffs(mo) - 1;
+          const unsigned short* rh = reinterpret_cast<const unsigned short *>(row);
+          if (r < n_out) reinterpret_cast<unsigned short *>(x_out)[t * (int64_t)n_out + r] = rh[32 * tid + b];
+          ++r;
+          mo &= mo - 1;
+        }
+      }
+    }
+    if (code_sum) {
+      // zeroed outliers quantize to the zero point (asym) or 0 (sym): exact correction above
+      csum = wave_sum(csum);
+      if (lane == 0) redi[wave] = csum;
+    }
+    __syncthreads();
+    uint8_t *qrow = q + t * (int64_t)(Kn / 2);
+    for (int i = tid; i < nwords; i += kSplitThreads) {
+      reinterpret_cast<uint32_t *>(qrow)[i] = packed[i];
+      packed[i] = 0u;
+    }
+    if (tid == 0) {
+      scale[t] = s;
+      if (asym) zero[t] = zp;
+      if (code_sum) code_sum[t] = redi[0] + redi[1] + redi[2] + redi[3];
+    }
+    packed[kSplitThreads * 4] = 0u;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
+                        const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
+                        int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
+  const int64_t grid = T < 1024 ? T : 1024;
+  split_quant<<<dim3((unsigned)grid), dim3(kSplitThreads), 0, st>>>(
+      (const __half *)x, T, (int)K, ldx, asym ? 1 : 0, clip, outlier_idx, n_out, q, scale, zero,
+      code_sum, (__half *)x_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // rowlds_quant: one workgroup (256 threads) per row, grid-stride over rows.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;

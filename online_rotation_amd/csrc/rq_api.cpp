@@ -101,6 +101,11 @@ rq_status run_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_r
     e = rq::launch_fwht4096(x, T, ldx, gsr, span_log2, norm, qd->clip_ratio, q, scale, code_sum, st);
     return hip_status(e, "fwht4096_quant launch");
   }
+  if (rot->kind == RQ_ROT_NONE && K <= 8192 && K % 32 == 0) {
+    e = rq::launch_split(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
+                         qd->n_out, q, scale, zero, code_sum, x_out, st);
+    return hip_status(e, "split_quant launch");
+  }
   e = rq::launch_rowlds(x, T, K, ldx, span_log2, gsr, norm, qd->asymmetric != 0, qd->clip_ratio,
                         qd->outlier_idx, qd->n_out, q, scale, zero, code_sum, x_out, st);
   return hip_status(e, "rowlds_quant launch");

@@ -96,16 +96,36 @@ def test_rotate_quant_strided_rows():
     check_sym_quant(host(out2["q"]), host(out2["scale"]), o.rotate_quant(inp2["x"], "hadamard"))
 
 
-@pytest.mark.parametrize("T,K,n_out", [(37, 8192, 256), (5, 8192, 0), (3, 1024, 64)])
-def test_asymmetric_outlier_split_matches_oracle(T, K, n_out):
-    note(f"[rotate_quant] asym T={T} K={K} n_out={n_out}")
+def _outlier_pattern(inp, K, n_out, pattern):
+    if pattern == "workload":
+        return np.ascontiguousarray(inp["outlier_ch"][:n_out]).astype(np.int32)
+    # clustered: a dense run across word boundaries, both ends, and strays
+    rng = np.random.default_rng(K + n_out)
+    run = np.arange(K // 2 - 40, K // 2 - 40 + (n_out - 2) // 2)
+    rest = np.setdiff1d(np.arange(1, K - 1), run)
+    stray = rng.choice(rest, n_out - 2 - run.size, replace=False)
+    idx = np.concatenate([[K - 1], run, stray, [0]]).astype(np.int32)
+    assert np.unique(idx).size == n_out
+    return idx
+
+
+# The split kernel covers K <= 8192 (K % 32 == 0), the LDS row kernel the
+# rest; 1100 rows exceed the split kernel's grid so its row loop turns over.
+@pytest.mark.parametrize("T,K,n_out,pattern", [
+    (37, 8192, 256, "workload"), (5, 8192, 0, "workload"), (3, 1024, 64, "workload"),
+    (1100, 1024, 64, "clustered"), (29, 8192, 512, "clustered"), (7, 16384, 0, "workload"),
+    (11, 4096, 0, "workload")])
+def test_asymmetric_outlier_split_matches_oracle(T, K, n_out, pattern):
+    note(f"[rotate_quant] asym T={T} K={K} n_out={n_out} {pattern}")
     inp = workloads.make_inputs("quik_prefill", T=T, K=K, with_weights=False)
-    x, idx = inp["x"], inp["outlier_ch"][:n_out]
+    x, idx = inp["x"], _outlier_pattern(inp, K, n_out, pattern)
     ref = o.rotate_quant(x, "none", asym=True, outlier_idx=idx if n_out else None)
     out = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True,
-                             outlier_idx=dev(idx) if n_out else None)
+                             outlier_idx=dev(idx) if n_out else None, code_sum=True)
     torch.cuda.synchronize()
     check_asym_quant(host(out["q"]), host(out["scale"]), host(out["zero"]), ref)
+    q_gpu = o.unpack_int4(host(out["q"]), signed=False).astype(np.int64)
+    assert np.array_equal(host(out["code_sum"]), q_gpu.sum(axis=1))
     if n_out:
         assert np.array_equal(host(out["x_out"]).view(np.uint16), ref["x_out"].view(np.uint16))
         # the order of the index list does not matter
