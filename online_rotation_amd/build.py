@@ -12,16 +12,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.cpp", "rotate_quant.hip", "gemm_w4a4.hip"]
+SOURCES = ["rq_api.cpp", "rotate_quant.hip", "gemm_w4a4.hip", "gemm_ra.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA accumulators in VGPRs (no AGPR copies)
     "-Wall", "-Wno-unused-function",
 ]
+# MFMA accumulators in VGPRs (no AGPR copies) where a kernel fits in 256
+# VGPRs; gemm_ra keeps its 128 accumulators in AGPRs instead.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM}
 
 
 def _hipcc() -> str:
@@ -40,7 +43,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"]
-        cmd = [hipcc, *HIPCC_FLAGS, *lang, "-I", os.path.join(ROOT, "include"), "-c",
+        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", os.path.join(ROOT, "include"), "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -1,0 +1,298 @@
+// gemm_ra.hip -- the large-T INT4 x INT4 GEMM with INT32 accumulation and
+// the fused dequantization epilogue (QUIK blog, "QUIK quantization" part 4:
+// INT4 operands, INT32 accumulation; part 1: dequantize, then add the FP16
+// outlier product before the one fp16 rounding), for gfx950.
+//
+// Workgroup: 256 threads = 4 wavefronts, one per SIMD; tile 256 tokens x 128
+// output channels.  Wavefront w owns tile rows [64w, 64w + 64) against all
+// 128 columns: 2 x 4 MFMA 32x32x32 blocks, 128 accumulator registers.
+//
+// What sets the design, per 32-code k slice and CU: 32 MFMAs (8 per SIMD).
+// Measured on this chip, LDS serves about 136 bytes per clock per CU to
+// 16-byte reads, and about four independent VALU instructions issue for free
+// beside each MFMA.
+//   - A rows belong to one wavefront only, so A goes global -> registers and
+//     is widened there (1.5 VALU per MFMA); it never touches LDS.
+//   - B columns are shared by all four wavefronts.  Each 16-byte int4 chunk
+//     is loaded by one thread, widened once (0.75 VALU per MFMA) and stored
+//     as int8, and the wavefronts read MFMA-ready fragments: 16 KB of reads
+//     and 4 KB of writes per k slice and CU, about half the LDS rate.
+// A k-step is 128 codes (64 bytes per row), four groups of 8 MFMAs.  Global
+// loads run kRaD steps ahead in a register ring; the B tile in LDS is
+// triple-buffered with one barrier per step, placed so that no fragment
+// read waits on it: every MFMA group's fragments are read one group ahead,
+// across step boundaries too.  Every step issues the same loads and stores
+// with no branch around them (row indices are clamped into the matrices,
+// and steps past the end re-load the last one), so the compiler waits only
+// for the load group it needs next.
+#include "gemm_common.h"
+#include "rq_kernels.h"
+
+#include <type_traits>
+
+namespace rq {
+
+namespace {
+
+constexpr int kRaBM = 256, kRaBN = 128;
+constexpr int kRaD = 3;                   // global load ring depth (k-steps)
+constexpr int kRaNB = 3;                  // B buffers in LDS
+constexpr int kRaU = kRaD % kRaNB == 0 ? kRaD : kRaD * kRaNB;  // unroll: slot and buffer indices static
+constexpr int kRaRow = 128;               // LDS bytes per B row and k-step (int8)
+constexpr int kRaBuf = kRaBN * kRaRow;    // one buffer: 16 KB
+
+// Widened slot s (16 bytes) of LDS row r sits at s ^ ((r >> 1) & 7): the 16
+// rows that a group of 16 lanes reads (one row per lane) or writes (four
+// lanes per row) then fall in distinct banks.
+__device__ __forceinline__ int ra_off(int row, int slot) {
+  return row * kRaRow + ((slot ^ ((row >> 1) & 7)) << 4);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+
+}  // namespace
+
+template <bool XU, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
+  __shared__ __align__(16) uint8_t Bs[kRaNB * kRaBuf];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kRaBM, n0 = (int64_t)tn * kRaBN, Kb = p.Kb;
+  const int nsteps = (int)(Kb >> 6), last = nsteps - 1;
+
+  // Slot s of a k-step = int4 dwords 2s, 2s+1 (codes 16s .. 16s+15), widened
+  // to one 16-byte MFMA operand.  MFMA c of a step takes slot 4g + c in lane
+  // group g, on both operands.
+  // A: lane (l32, g) loads dwords [8g, 8g+8) of rows 64w + l32 and 64w + 32 + l32.
+  const int64_t ar = m0 + wave * 64 + l32;
+  const uint8_t *ap0 = p.qx + min(ar, p.T - 1) * Kb + 32 * g;
+  const uint8_t *ap1 = p.qx + min(ar + 32, p.T - 1) * Kb + 32 * g;
+  // B staging: thread t loads 16-byte chunk q = t & 3 (slots 2q, 2q+1) of tile
+  // rows t >> 2 and 64 + (t >> 2).
+  const int br = tid >> 2, bq = tid & 3;
+  const uint8_t *bp0 = p.qw + min(n0 + br, p.N - 1) * Kb + 16 * bq;
+  const uint8_t *bp1 = p.qw + min(n0 + 64 + br, p.N - 1) * Kb + 16 * bq;
+  const int ws0 = ra_off(br, 2 * bq), ws1 = ra_off(br, 2 * bq + 1);
+  const int ws2 = ra_off(br + 64, 2 * bq), ws3 = ra_off(br + 64, 2 * bq + 1);
+  // fragment of block j, MFMA c: row 32j + l32, slot 4g + c.  ((32j + l32) >> 1) & 7
+  // does not depend on j, so the offset is j * 32 * kRaRow + rs[c].
+  int rs[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) rs[c] = l32 * kRaRow + (((4 * g + c) ^ ((l32 >> 1) & 7)) << 4);
+
+  uint4 ra[kRaD][4], rb[kRaD][2];
+  auto gload = [&](int s, int kb) {
+    const int64_t o = (int64_t)kb * 64;
+    ra[s][0] = ldg16(ap0 + o);
+    ra[s][1] = ldg16(ap0 + o + 16);
+    ra[s][2] = ldg16(ap1 + o);
+    ra[s][3] = ldg16(ap1 + o + 16);
+    rb[s][0] = ldg16(bp0 + o);
+    rb[s][1] = ldg16(bp1 + o);
+  };
+  // half h of the B staging of slot s, widened, into LDS buffer buf
+  auto bstore = [&](int buf, int s, int h) {
+    uint8_t *B = Bs + buf * kRaBuf;
+    const uint4 &w = rb[s][h];
+    *reinterpret_cast<v4i *>(B + (h ? ws2 : ws0)) = widen_signed(w.x, w.y);
+    *reinterpret_cast<v4i *>(B + (h ? ws3 : ws1)) = widen_signed(w.z, w.w);
+  };
+  v4i bf[2][4];  // B fragments, double-buffered across MFMA groups
+  auto bread = [&](int f, int buf, int c) {
+    const uint8_t *B = Bs + buf * kRaBuf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[f][j] = *reinterpret_cast<const v4i *>(B + j * 32 * kRaRow + rs[c]);
+  };
+  auto awiden = [&](int s, int c, v4i *aw) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 &w = ra[s][2 * i + (c >> 1)];
+      const uint32_t w0 = (c & 1) ? w.z : w.x, w1 = (c & 1) ? w.w : w.y;
+      aw[i] = XU ? widen_unsigned(w0, w1) : widen_signed(w0, w1);
+    }
+  };
+
+  v16i acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+  auto mfma8 = [&](const v4i *aw, int f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aw[i], bf[f][j], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: steps 0 .. kRaD-1 in flight, B(0) into buffer 0, its first fragments
+#pragma unroll
+  for (int s = 0; s < kRaD; ++s) gload(s, min(s, last));
+  bstore(0, 0, 0);
+  bstore(0, 0, 1);
+  __syncthreads();
+  bread(0, 0, 0);
+
+  // Step kb: A(kb) in load slot kb % kRaD, B(kb) in LDS buffer kb % kRaNB
+  // with MFMA group 0's fragments already in registers, B(kb+1) in load slot
+  // (kb+1) % kRaD.  Each of the four MFMA groups reads the next group's
+  // fragments first.  B(kb+1) is stored into buffer (kb+1) % kRaNB during
+  // groups 0 and 1, the barrier sits before group 2, and group 3 reads step
+  // kb+1's first fragments.  With three buffers, buffer (kb+1) % 3 was last
+  // read in step kb-2, before every wave passed step kb-1's barrier.
+  auto steps = [&](int kb0, auto tail) {
+#pragma unroll
+    for (int v = 0; v < kRaU; ++v) {
+      const int kb = kb0 + v;
+      const int u = v % kRaD, us = (v + 1) % kRaD;     // load slots of steps kb, kb+1
+      const int ub = v % kRaNB, nb = (v + 1) % kRaNB;  // LDS buffers of steps kb, kb+1
+      const bool live = !decltype(tail)::value || kb < nsteps;
+      v4i aw[2];
+      // (sched_barrier: keep each group's fragment reads ahead of its MFMAs;
+      // the scheduler otherwise sinks them next to their first use)
+      // group 0
+      bread(1, ub, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      awiden(u, 0, aw);
+      if (live) mfma8(aw, 0);
+      bstore(nb, us, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // group 1
+      bread(0, ub, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      awiden(u, 1, aw);
+      if (live) mfma8(aw, 1);
+      bstore(nb, us, 1);
+      __syncthreads();
+      // group 2
+      bread(1, ub, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      awiden(u, 2, aw);
+      if (live) mfma8(aw, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // group 3: A(kb) is fully widened after this, so its slot is refilled
+      awiden(u, 3, aw);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(u, min(kb + kRaD, last));
+      bread(0, nb, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) mfma8(aw, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Whole groups of kRaU steps in the loop; a final partial group (steps
+  // past the end only load and store) outside it, so that no branch sits
+  // inside the loop (a branch there makes the compiler copy the load ring
+  // at the back edge, waiting for every load in flight).
+  int kb0 = 0;
+  for (; kb0 + kRaU <= nsteps; kb0 += kRaU) steps(kb0, std::false_type());
+  if (kb0 < nsteps) steps(kb0, std::true_type());
+
+  // Epilogue.  32x32 accumulator layout: lane l, register r holds row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
+  constexpr int kShift = XU ? 4 : 8;
+  const int64_t row0 = m0 + wave * 64, col0 = n0;
+  if (MODE == 0) {
+    int32_t *out = reinterpret_cast<int32_t *>(p.out);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t gn = col0 + 32 * j + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = acc[i][j][r] >> kShift;
+        }
+      }
+    return;
+  }
+  float swn[4];
+  int32_t rsn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t gn = min(col0 + 32 * j + l32, p.N - 1);
+    swn[j] = p.sw[gn];
+    rsn[j] = (MODE == 2 && p.zx) ? p.rowsum[gn] : 0;
+  }
+  v16f f[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t gm = min(row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3), p.T - 1);
+      const float sxm = p.sx[gm];
+      const int32_t zxm = (MODE == 2 && p.zx) ? p.zx[gm] : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int32_t v = acc[i][j][r] >> kShift;
+        if (MODE == 2) v -= zxm * rsn[j];
+        f[i][j][r] = (float)v * sxm * swn[j];
+      }
+    }
+  if (MODE == 2 && p.n_out > 0) {
+    // FP16 outlier product on FP16 matrix cores, fp32 accumulation on top of
+    // the dequantized INT4 part.  Lane (l32, g) supplies halves
+    // [k0 + 8g, k0 + 8g + 8) of its row (A) or column (B).
+    const __half *xa0 = p.xo + min(row0 + l32, p.T - 1) * p.n_out + 8 * g;
+    const __half *xa1 = p.xo + min(row0 + 32 + l32, p.T - 1) * p.n_out + 8 * g;
+    const __half *wb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wb[j] = p.wo + min(col0 + 32 * j + l32, p.N - 1) * p.n_out + 8 * g;
+    for (int k0 = 0; k0 < p.n_out; k0 += 16) {
+      v8h av[2], bv[4];
+      uint4 t = *reinterpret_cast<const uint4 *>(xa0 + k0);
+      __builtin_memcpy(&av[0], &t, 16);
+      t = *reinterpret_cast<const uint4 *>(xa1 + k0);
+      __builtin_memcpy(&av[1], &t, 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        t = *reinterpret_cast<const uint4 *>(wb[j] + k0);
+        __builtin_memcpy(&bv[j], &t, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          f[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], f[i][j], 0, 0, 0);
+    }
+  }
+  __half *out = reinterpret_cast<__half *>(p.out);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t gn = col0 + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(f[i][j][r]);
+      }
+    }
+}
+
+bool gemm_ra_fits(const GemmArgs &p) { return p.T >= 256 && p.Kb % 64 == 0 && p.Kb >= 64; }
+
+hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  const int nt_m = (int)((p.T + kRaBM - 1) / kRaBM), nt_n = (int)((p.N + kRaBN - 1) / kRaBN);
+  const dim3 grid((unsigned)(nt_m * nt_n)), block(256);
+  if (mode == 0) {
+    if (x_unsigned) gemm_ra<true, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else if (mode == 1) {
+    gemm_ra<false, 1><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else {
+    if (x_unsigned) gemm_ra<true, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rq

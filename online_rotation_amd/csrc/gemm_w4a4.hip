@@ -24,6 +24,7 @@
 //     was stored and overwritten two steps after it was read.
 #include "rq_device.h"
 #include "rq_kernels.h"
+#include "gemm_common.h"
 
 #include <stdlib.h>
 
@@ -39,41 +40,6 @@ constexpr int kDepth = 3;             // global prefetch distance in k-steps
 // touch distinct banks within every group of 8 or 16 lanes.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kBKB + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
-}
-
-__device__ __forceinline__ v4i widen_signed(uint32_t w0, uint32_t w1) {
-  v4i r;
-  r[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-  r[1] = (int)(w0 & 0xF0F0F0F0u);
-  r[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-  r[3] = (int)(w1 & 0xF0F0F0F0u);
-  return r;
-}
-
-__device__ __forceinline__ v4i widen_unsigned(uint32_t w0, uint32_t w1) {
-  v4i r;
-  r[0] = (int)(w0 & 0x0F0F0F0Fu);
-  r[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
-  r[2] = (int)(w1 & 0x0F0F0F0Fu);
-  r[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
-  return r;
-}
-
-// Workgroup id -> output tile.  Consecutive ids go round-robin to the 8
-// XCDs; remapping gives each XCD a contiguous range of positions, and the
-// grouped order walks 8 row-tiles against consecutive column tiles, so the
-// workgroups resident on one XCD share rows and columns in its L2.
-__device__ __forceinline__ void map_tile(int bid, int nt_m, int nt_n, int &tm, int &tn) {
-  const int nt = nt_m * nt_n;
-  int pos = bid;
-  if ((nt & 7) == 0) pos = (bid & 7) * (nt >> 3) + (bid >> 3);
-  constexpr int G = 8;
-  const int group = pos / (G * nt_n);
-  const int first = group * G;
-  const int gsz = min(G, nt_m - first);
-  const int in = pos - group * G * nt_n;
-  tm = first + in % gsz;
-  tn = in / gsz;
 }
 
 template <int WMB, int WNB, bool XU, int MODE>
@@ -494,9 +460,12 @@ hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t
     case 5:
       return (p.T >= 128 && p.Kb % kBKB == 0) ? launch_wg<2>(p, x_unsigned, mode, st)
                                               : launch_tiles<2, 2>(p, x_unsigned, mode, st);
-    default:
+    case 6:
       return (p.T >= 256 && p.Kb % kBKB == 0) ? launch_wg<4>(p, x_unsigned, mode, st)
                                               : launch_tiles<2, 2>(p, x_unsigned, mode, st);
+    default:
+      return gemm_ra_fits(p) ? launch_gemm_ra(p, x_unsigned, mode, st)
+                             : launch_tiles<2, 2>(p, x_unsigned, mode, st);
   }
 }
 

@@ -462,20 +462,54 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// split_quant: no rotation (QUIK), K <= 8192 and K % 32 == 0.  Thread t of a
-// 256-thread workgroup owns columns [32t, 32t+32) of every row it quantizes.
-// Once per workgroup: a bit mask of the outlier columns, its per-word
-// exclusive prefix counts (a block scan) and, per thread, an AND mask that
-// zeroes the thread's outlier halves.  Zeroed outliers leave
-// min(min x, 0) and max(max x, 0) -- and the absolute maximum -- unchanged,
-// so the per-row reductions need no per-value test.  Per row the thread
-// quantizes its 32 values (one fma against a zero-point-shifted magic
-// number, one clamp), deletes its outlier nibbles from the 128-bit code run
-// and ORs the run into a packed row in LDS at its compacted nibble offset;
-// the packed row is then copied out with coalesced stores.
+// split_quant: no rotation (QUIK), K % 32 == 0, K <= 32768.  Thread t of a
+// 256-thread workgroup owns the WPT words of 32 columns that start at column
+// 32 WPT t, in every row the workgroup quantizes.
+// Once per workgroup: a bit mask of the outlier columns, each word's
+// exclusive prefix count (a block scan) and, per word, AND masks that zero
+// its outlier halves.  Zeroed outliers leave min(min x, 0), max(max x, 0) and
+// the absolute maximum unchanged, so the row reductions test no value.  Per
+// row each thread quantizes its values (one fma against a magic number
+// shifted by the zero point, one clamp), deletes the outlier nibbles from
+// each word's 128-bit code run and ORs the run into a packed row in LDS at
+// its compacted nibble offset; the packed row then goes out with coalesced
+// stores.
+//
+// Rounding matches rne(x / s) with s = fp32(S), S the exact real scale
+// (clip*amax/7 or (hi - lo)/15).  The inputs are fp16, so x / S lies either
+// exactly on a rounding boundary k + 1/2 or at least ~2^-15 (relative) away
+// from every boundary; the reciprocal of s (2^-24 off) only matters for the
+// exact ties, and there x / s falls on the side that the rounding of S to s
+// decides.  directed_inv moves the reciprocal by at most one ulp so that
+// x * inv lands on that same side.  When S == s the ties are real and go to
+// even; such rows take rne_quotient, which tests the boundary exactly.
 // ---------------------------------------------------------------------------
 constexpr int kSplitThreads = 256;
 constexpr float kMagic0 = 12582912.0f;  // 1.5 * 2^23
+
+// Reciprocal of s nudged to the side of 1/s on which exact ties must land.
+// num / den = S; `exact` is set when s == S.
+__device__ __forceinline__ float directed_inv(float s, float inv, float num, float den, bool &exact) {
+  const float r = __builtin_fmaf(-den, s, num);   // S - s, sign exact
+  const float e = __builtin_fmaf(-s, inv, 1.0f);  // 1/s - inv, sign exact
+  exact = r == 0.0f;
+  uint32_t bits = __float_as_uint(inv);
+  if (r > 0.0f && e > 0.0f) ++bits;       // s < S: ties round away from zero, need inv >= 1/s
+  else if (r < 0.0f && e < 0.0f) --bits;  // s > S: ties round toward zero, need inv <= 1/s
+  return __uint_as_float(bits);
+}
+
+// rne(x / s) exactly, for s > 0: the candidate from x * inv, then the sign of
+// x - b s (exact in one fma) at the boundary b on that side.
+__device__ __forceinline__ float rne_quotient(float x, float s, float inv) {
+  const float t = x * inv;
+  const float c = __builtin_rintf(t);
+  const bool up = t > c;
+  const float b = up ? c + 0.5f : c - 0.5f;
+  const float d = __builtin_fmaf(-b, s, x);
+  if (d == 0.0f) return __builtin_rintf(b);
+  return up ? (d > 0.0f ? c + 1.0f : c) : (d < 0.0f ? c - 1.0f : c);
+}
 
 // delete nibble `b` (0..31) of the 128-bit value w (w[0] lowest), shifting the
 // higher nibbles down by one
@@ -494,31 +528,39 @@ __device__ __forceinline__ void del_nibble(uint32_t *w, int b) {
   }
 }
 
+template <int WPT>
 __global__ __launch_bounds__(kSplitThreads) void split_quant(
     const __half *__restrict__ x, int64_t T, int K, int64_t ldx, int asym, float clip,
     const int32_t *__restrict__ outlier_idx, int n_out, uint8_t *__restrict__ q,
     float *__restrict__ scale, int32_t *__restrict__ zero, int32_t *__restrict__ code_sum,
     __half *__restrict__ x_out) {
-  __shared__ uint32_t mask[kSplitThreads];
+  constexpr int NW = kSplitThreads * WPT;
+  __shared__ uint32_t mask[NW];
   __shared__ int wsum[4];
-  __shared__ uint32_t packed[kSplitThreads * 4 + 1];  // packed codes of one row (+1 spill word)
+  __shared__ uint32_t packed[NW * 4 + 1];  // packed codes of one row (+1 spill word)
   __shared__ float redf[8];
   __shared__ int redi[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nw = K / 32;  // mask words == active threads
+  const int nw = K / 32;
   const int Kn = K - n_out;
-  const bool active = tid < nw;
 
   // ---- per-workgroup setup
-  mask[tid] = 0u;
+  for (int i = tid; i < NW; i += kSplitThreads) mask[i] = 0u;
   __syncthreads();
   for (int j = tid; j < n_out; j += kSplitThreads) {
     const int c = outlier_idx[j];
     if (c >= 0 && c < K) atomicOr(&mask[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
-  const uint32_t m = mask[tid];
-  const int cnt = active ? __popc(m) : 0;
+  uint32_t m[WPT];
+  bool active[WPT];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    active[j] = tid * WPT + j < nw;
+    m[j] = mask[tid * WPT + j];
+    cnt += __popc(m[j]);
+  }
   // exclusive prefix of cnt over threads (wave scan + 4 wave totals)
   int incl = cnt;
 #pragma unroll
@@ -528,43 +570,55 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
   }
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int before = incl - cnt;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  const int pos0 = 32 * tid - before;  // compacted nibble position of this thread's first normal column
-  uint32_t keep[16];                   // AND masks zeroing the thread's outlier halves
+  int before[WPT];  // outlier columns left of each word
+  before[0] = incl - cnt;
+  for (int w = 0; w < wave; ++w) before[0] += wsum[w];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    keep[i] = (((m >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) | (((m >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
+  for (int j = 1; j < WPT; ++j) before[j] = before[j - 1] + __popc(m[j - 1]);
+  uint32_t keep[WPT][16];  // AND masks zeroing each word's outlier halves
+#pragma unroll
+  for (int j = 0; j < WPT; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      keep[j][i] = (((m[j] >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) |
+                   (((m[j] >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
   const int nwords = (Kn + 7) / 8;  // packed row words
-  for (int i = tid; i < kSplitThreads * 4 + 1; i += kSplitThreads) packed[i] = 0u;
+  for (int i = tid; i < NW * 4 + 1; i += kSplitThreads) packed[i] = 0u;
   __syncthreads();
 
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     const __half *row = x + t * ldx;
-    uint32_t d[16];
-    if (active) {
+    uint32_t d[WPT][16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(row + 32 * tid + 8 * i);
-        d[4 * i] = u.x; d[4 * i + 1] = u.y; d[4 * i + 2] = u.z; d[4 * i + 3] = u.w;
+    for (int j = 0; j < WPT; ++j) {
+      if (active[j]) {
+        const __half *src = row + 32 * (tid * WPT + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * i);
+          d[j][4 * i] = u.x & keep[j][4 * i];
+          d[j][4 * i + 1] = u.y & keep[j][4 * i + 1];
+          d[j][4 * i + 2] = u.z & keep[j][4 * i + 2];
+          d[j][4 * i + 3] = u.w & keep[j][4 * i + 3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[j][i] = 0u;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) d[i] &= keep[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) d[i] = 0u;
     }
     // per-thread min / max (or absmax) on packed fp16, then the block reduction
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 mn2 = {0, 0}, mx2 = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      f16x2 h;
-      __builtin_memcpy(&h, &d[i], 4);
-      if (!asym) h = __builtin_elementwise_abs(h);
-      mn2 = __builtin_elementwise_min(mn2, h);
-      mx2 = __builtin_elementwise_max(mx2, h);
-    }
+    for (int j = 0; j < WPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f16x2 h;
+        __builtin_memcpy(&h, &d[j][i], 4);
+        if (!asym) h = __builtin_elementwise_abs(h);
+        mn2 = __builtin_elementwise_min(mn2, h);
+        mx2 = __builtin_elementwise_max(mx2, h);
+      }
     float mn = fminf((float)mn2.x, (float)mn2.y);
     float mx = fmaxf((float)mx2.x, (float)mx2.y);
     mn = wave_min(mn);
@@ -578,54 +632,68 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     mx = fmaxf(fmaxf(redf[4], redf[5]), fmaxf(redf[6], redf[7]));
     float s, inv, base, lo_c, hi_c;
     int zp = 0;
+    bool exact = false;
     if (asym) {
-      asym_params(mn, mx, s, inv, zp);
+      const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
+      s = (hi - lo) / 15.0f;
+      inv = s > 0.0f ? 1.0f / s : 0.0f;
+      if (s > 0.0f) {
+        inv = directed_inv(s, inv, hi - lo, 15.0f, exact);
+        const float zf = exact ? rne_quotient(-lo, s, inv) : __builtin_fmaf(-lo, inv, kMagic0) - kMagic0;
+        zp = (int)__builtin_amdgcn_fmed3f(zf, 0.0f, 15.0f);
+      }
       base = kMagic0 + (float)zp;      // code = clamp(rne(x/s) + zero, 0, 15)
       lo_c = kMagic0;
       hi_c = kMagic0 + 15.0f;
     } else {
       sym_scale(mx, clip, s, inv);
+      if (s > 0.0f) inv = directed_inv(s, inv, clip * mx, 7.0f, exact);
       base = kMagic8;                  // low nibble = code + 8
       lo_c = kMagic8 - 7.0f;
       hi_c = kMagic8 + 7.0f;
     }
     int csum = 0;
-    if (active) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      if (!active[j]) continue;
       uint32_t w[4];
       float fsum = 0.0f;
+      auto code = [&](float f) {
+        const float v = exact ? rne_quotient(f, s, inv) + base : __builtin_fmaf(f, inv, base);
+        return __builtin_amdgcn_fmed3f(v, lo_c, hi_c);
+      };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t wd = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const __half2 h = *reinterpret_cast<const __half2 *>(&d[4 * i + j]);
+        for (int k = 0; k < 4; ++k) {
+          const __half2 h = *reinterpret_cast<const __half2 *>(&d[j][4 * i + k]);
           const float2 f = __half22float2(h);
-          const float q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(f.x, inv, base), lo_c, hi_c);
-          const float q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(f.y, inv, base), lo_c, hi_c);
+          const float q0 = code(f.x), q1 = code(f.y);
           fsum += (q0 - base) + (q1 - base);
           uint32_t b0, b1;
           __builtin_memcpy(&b0, &q0, 4);
           __builtin_memcpy(&b1, &q1, 4);
-          wd |= ((b0 & 0xFu) | ((b1 & 0xFu) << 4)) << (8 * j);
+          wd |= ((b0 & 0xFu) | ((b1 & 0xFu) << 4)) << (8 * k);
         }
         w[i] = asym ? wd : (wd ^ 0x88888888u);  // symmetric: offset-8 nibble -> two's complement
       }
-      // the run of this thread's normal-column codes, outliers deleted
-      uint32_t mm = m;
+      // the run of this word's normal-column codes, outliers deleted
+      uint32_t mm = m[j];
       while (mm) {
         const int b = 31 - __clz(mm);  // highest first, so lower positions stay put
         del_nibble(w, b);
         mm &= ~(1u << b);
       }
-      // fsum is the sum of (code - zero) over all 32 values; the zeroed
-      // outliers contribute exactly 0 to it
-      csum = (int)fsum + (asym ? zp * (32 - cnt) : 0);
-      // place the run (32 - cnt nibbles) at nibble position pos0
-      const int sh = (pos0 & 7) * 4, w0i = pos0 >> 3;
-      const int nrun = 32 - cnt;
-      uint32_t out[5];
-      // clear nibbles beyond the run
-      if (nrun < 32) {
+      const int cj = __popc(m[j]);
+      // fsum is the sum of (code - zero) over the word's 32 values; the
+      // zeroed outliers contribute exactly 0 to it
+      csum += (int)fsum + (asym ? zp * (32 - cj) : 0);
+      // place the run (32 - cj nibbles) at nibble position pos
+      const int pos = 32 * (tid * WPT + j) - before[j];
+      const int sh = (pos & 7) * 4, w0i = pos >> 3;
+      const int nrun = 32 - cj;
+      if (nrun < 32) {  // clear the nibbles past the run
         const int wi = nrun >> 3, bi = (nrun & 7) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -633,6 +701,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
           else if (i == wi) w[i] &= bi ? ((1u << bi) - 1u) : 0u;
         }
       }
+      uint32_t out[5];
       out[0] = w[0] << sh;
 #pragma unroll
       for (int i = 1; i < 4; ++i) out[i] = (w[i] << sh) | (sh ? (w[i - 1] >> (32 - sh)) : 0u);
@@ -642,19 +711,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
         if (out[i]) atomicOr(&packed[w0i + i], out[i]);
       // outlier columns keep their fp16 bits
       if (n_out) {
-        uint32_t mo = m;
-        int r = before;
+        uint32_t mo = m[j];
+        int r = before[j];
+        const unsigned short *rh = reinterpret_cast<const unsigned short *>(row) + 32 * (tid * WPT + j);
         while (mo) {
           const int b = __ffs(mo) - 1;
-          const unsigned short* rh = reinterpret_cast<const unsigned short *>(row);
-          if (r < n_out) reinterpret_cast<unsigned short *>(x_out)[t * (int64_t)n_out + r] = rh[32 * tid + b];
+          if (r < n_out) reinterpret_cast<unsigned short *>(x_out)[t * (int64_t)n_out + r] = rh[b];
           ++r;
           mo &= mo - 1;
         }
       }
     }
     if (code_sum) {
-      // zeroed outliers quantize to the zero point (asym) or 0 (sym): exact correction above
       csum = wave_sum(csum);
       if (lane == 0) redi[wave] = csum;
     }
@@ -669,7 +737,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
       if (asym) zero[t] = zp;
       if (code_sum) code_sum[t] = redi[0] + redi[1] + redi[2] + redi[3];
     }
-    packed[kSplitThreads * 4] = 0u;
+    packed[NW * 4] = 0u;
     __syncthreads();
   }
 }
@@ -678,9 +746,17 @@ hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool a
                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
   const int64_t grid = T < 1024 ? T : 1024;
-  split_quant<<<dim3((unsigned)grid), dim3(kSplitThreads), 0, st>>>(
-      (const __half *)x, T, (int)K, ldx, asym ? 1 : 0, clip, outlier_idx, n_out, q, scale, zero,
-      code_sum, (__half *)x_out);
+  const int words = (int)(K / 32);
+  const dim3 g((unsigned)grid), b(kSplitThreads);
+  const __half *xh = (const __half *)x;
+  __half *xo = (__half *)x_out;
+  const int a = asym ? 1 : 0;
+  if (words <= kSplitThreads)
+    split_quant<1><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
+  else if (words <= 2 * kSplitThreads)
+    split_quant<2><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
+  else
+    split_quant<4><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
   return hipGetLastError();
 }
 
@@ -695,15 +771,10 @@ struct RowArgs {
   int span_log2;      // 0: no transform
   int gsr;            // output permutation within each 2^span_log2 block
   float norm;
-  int asym;
   float clip;
-  const int32_t *outlier_idx;
-  int n_out;
   uint8_t *q;
   float *scale;
-  int32_t *zero;
   int32_t *code_sum;
-  __half *x_out;
 };
 
 __device__ __forceinline__ float block_reduce_max(float v, float *red) {
@@ -714,14 +785,6 @@ __device__ __forceinline__ float block_reduce_max(float v, float *red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__device__ __forceinline__ float block_reduce_min(float v, float *red) {
-  v = wave_min(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
-}
-
 __device__ __forceinline__ int block_reduce_sum(int v, int *red) {
   v = wave_sum(v);
   __syncthreads();
@@ -730,53 +793,14 @@ __device__ __forceinline__ int block_reduce_sum(int v, int *red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Dynamic LDS: vals fp32 [K] | ncol int32 [K] | ocol int32 [K] | mask u32 [W] | wpre int32 [W],
-// W = ceil(K/32) (the last four only when n_out > 0).
+// Dynamic LDS: vals fp32 [K].
 __global__ __launch_bounds__(kRowThreads) void rowlds_quant(RowArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float redf[4];
   __shared__ int redi[4];
   const int K = (int)p.K;
-  const int Kn = K - p.n_out;
   float *vals = reinterpret_cast<float *>(smem);
-  int32_t *ncol = reinterpret_cast<int32_t *>(vals + K);
-  int32_t *ocol = ncol + K;
-  const int W = (K + 31) / 32;
-  uint32_t *mask = reinterpret_cast<uint32_t *>(ocol + K);
-  int32_t *wpre = reinterpret_cast<int32_t *>(mask + W);
   const int tid = threadIdx.x;
-
-  if (p.n_out > 0) {
-    // Column classes, built once per workgroup: bit mask of outlier columns,
-    // per-word exclusive prefix counts, then the compacted column maps.
-    for (int w = tid; w < W; w += kRowThreads) mask[w] = 0u;
-    for (int j = tid; j < p.n_out; j += kRowThreads) ocol[j] = 0;  // defined even for bad index lists
-    __syncthreads();
-    for (int j = tid; j < p.n_out; j += kRowThreads) {
-      const int c = p.outlier_idx[j];
-      if (c >= 0 && c < K) atomicOr(&mask[c >> 5], 1u << (c & 31));
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int w = 0; w < W; ++w) {
-        wpre[w] = run;
-        run += __popc(mask[w]);
-      }
-    }
-    __syncthreads();
-    for (int c = tid; c < K; c += kRowThreads) {
-      const uint32_t m = mask[c >> 5];
-      const int before = wpre[c >> 5] + __popc(m & ((1u << (c & 31)) - 1u));
-      if ((m >> (c & 31)) & 1u) {
-        if (before < p.n_out) ocol[before] = c;
-      } else {
-        const int pos = c - before;
-        if (pos < Kn) ncol[pos] = c;
-      }
-    }
-    __syncthreads();
-  }
 
   for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
     const __half *row = p.x + t * p.ldx;
@@ -798,9 +822,9 @@ __global__ __launch_bounds__(kRowThreads) void rowlds_quant(RowArgs p) {
       }
       __syncthreads();
     }
-    // value at compacted (normal) position pos
-    auto value_at = [&](int pos) -> float {
-      int c = p.n_out > 0 ? ncol[pos] : pos;
+    // rotated value of column c; GSR reads its block's transform output in
+    // sequency order, sigma(s) = bitrev(gray(s))
+    auto value_at = [&](int c) -> float {
       if (p.gsr) {
         const int bm = (1 << p.span_log2) - 1;
         const int s_ = c & bm;
@@ -808,49 +832,22 @@ __global__ __launch_bounds__(kRowThreads) void rowlds_quant(RowArgs p) {
       }
       return vals[c] * p.norm;
     };
+    float amax = 0.0f;
+    for (int c = tid; c < K; c += kRowThreads) amax = fmaxf(amax, fabsf(value_at(c)));
+    amax = block_reduce_max(amax, redf);
     float s, inv;
-    int zero = 0;
-    if (p.asym) {
-      float mn = INFINITY, mx = -INFINITY;
-      for (int pos = tid; pos < Kn; pos += kRowThreads) {
-        const float v = value_at(pos);
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-      }
-      mn = block_reduce_min(mn, redf);
-      mx = block_reduce_max(mx, redf);
-      asym_params(mn, mx, s, inv, zero);
-    } else {
-      float amax = 0.0f;
-      for (int pos = tid; pos < Kn; pos += kRowThreads) amax = fmaxf(amax, fabsf(value_at(pos)));
-      amax = block_reduce_max(amax, redf);
-      sym_scale(amax, p.clip, s, inv);
-    }
-    const float zf = (float)zero;
+    sym_scale(amax, p.clip, s, inv);
     int csum = 0;
-    uint8_t *qrow = p.q + t * (int64_t)(Kn / 2);
-    for (int pb = tid; pb < Kn / 2; pb += kRowThreads) {
-      const float v0 = value_at(2 * pb), v1 = value_at(2 * pb + 1);
-      int c0, c1;
-      if (p.asym) {
-        c0 = quant_asym(v0, inv, zf);
-        c1 = quant_asym(v1, inv, zf);
-      } else {
-        c0 = quant_sym(v0, inv, 7.0f);
-        c1 = quant_sym(v1, inv, 7.0f);
-      }
+    uint8_t *qrow = p.q + t * (int64_t)(K / 2);
+    for (int pb = tid; pb < K / 2; pb += kRowThreads) {
+      const int c0 = quant_sym(value_at(2 * pb), inv, 7.0f);
+      const int c1 = quant_sym(value_at(2 * pb + 1), inv, 7.0f);
       csum += c0 + c1;
       qrow[pb] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
-    }
-    if (p.n_out > 0) {
-      const unsigned short *rh = reinterpret_cast<const unsigned short *>(row);
-      unsigned short *xo = reinterpret_cast<unsigned short *>(p.x_out) + t * (int64_t)p.n_out;
-      for (int j = tid; j < p.n_out; j += kRowThreads) xo[j] = rh[ocol[j]];
     }
     if (p.code_sum) csum = block_reduce_sum(csum, redi);
     if (tid == 0) {
       p.scale[t] = s;
-      if (p.asym) p.zero[t] = zero;
       if (p.code_sum) p.code_sum[t] = csum;
     }
     __syncthreads();  // vals is reused by the next row
@@ -1022,15 +1019,10 @@ hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int 
   return hipGetLastError();
 }
 
-size_t rowlds_smem_bytes(int64_t K, int n_out) {
-  size_t b = (size_t)K * 4;
-  if (n_out > 0) b += (size_t)K * 8 + (size_t)((K + 31) / 32) * 8;
-  return b;
-}
+size_t rowlds_smem_bytes(int64_t K) { return (size_t)K * 4; }
 
 hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int span_log2, bool gsr,
-                         float norm, bool asym, float clip, const int32_t *outlier_idx, int n_out,
-                         uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum, void *x_out,
+                         float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                          hipStream_t st) {
   RowArgs p;
   p.x = (const __half *)x;
@@ -1040,16 +1032,11 @@ hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int s
   p.span_log2 = span_log2;
   p.gsr = gsr ? 1 : 0;
   p.norm = norm;
-  p.asym = asym ? 1 : 0;
   p.clip = clip;
-  p.outlier_idx = outlier_idx;
-  p.n_out = n_out;
   p.q = q;
   p.scale = scale;
-  p.zero = zero;
   p.code_sum = code_sum;
-  p.x_out = (__half *)x_out;
-  const size_t smem = rowlds_smem_bytes(K, n_out);
+  const size_t smem = rowlds_smem_bytes(K);
   hipError_t e = hipFuncSetAttribute((const void *)rowlds_quant,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;

@@ -40,7 +40,8 @@ int ilog2(int64_t v) {
 }
 
 constexpr int64_t kMaxK = 65536;
-constexpr size_t kMaxLds = 160 * 1024 - 64;  // gfx950 LDS per workgroup, minus static reductions
+constexpr size_t kMaxLds = 160 * 1024 - 64;
+constexpr int kSplitMaxK = 32768;  // the split quantizer: 256 threads x 4 words of 32 columns  // gfx950 LDS per workgroup, minus static reductions
 
 // Checks shared by the activation and weight quantizers.
 rq_status check_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_rot_desc *rot,
@@ -73,9 +74,10 @@ rq_status check_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq
     if (qd->n_out > 0 && (!x_out || !aligned(x_out, 2))) return fail(RQ_EINVAL, "x_out is required when n_out > 0");
     if (qd->n_out > 0 && !aligned(qd->outlier_idx, 4)) return fail(RQ_EALIGN, "outlier_idx must be 4-byte aligned");
   }
-  if (rot->kind != RQ_ROT_KRON && !(rot->kind == RQ_ROT_HADAMARD && K == 4096) &&
-      !(rot->kind == RQ_ROT_GSR && K == 4096) && rq::rowlds_smem_bytes(K, qd->n_out) > kMaxLds)
-    return fail(RQ_ESHAPE, "row of K=%lld with n_out=%d does not fit in LDS", (long long)K, qd->n_out);
+  if (rot->kind == RQ_ROT_NONE && (K % 32 || K > kSplitMaxK))
+    return fail(RQ_ESHAPE, "without a rotation K must be a multiple of 32 and at most %d (K=%lld)", kSplitMaxK, (long long)K);
+  if ((rot->kind == RQ_ROT_HADAMARD || rot->kind == RQ_ROT_GSR) && K != 4096 && rq::rowlds_smem_bytes(K) > kMaxLds)
+    return fail(RQ_ESHAPE, "row of K=%lld does not fit in LDS", (long long)K);
   return ok();
 }
 
@@ -101,13 +103,12 @@ rq_status run_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_r
     e = rq::launch_fwht4096(x, T, ldx, gsr, span_log2, norm, qd->clip_ratio, q, scale, code_sum, st);
     return hip_status(e, "fwht4096_quant launch");
   }
-  if (rot->kind == RQ_ROT_NONE && K <= 8192 && K % 32 == 0) {
+  if (rot->kind == RQ_ROT_NONE) {
     e = rq::launch_split(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
                          qd->n_out, q, scale, zero, code_sum, x_out, st);
     return hip_status(e, "split_quant launch");
   }
-  e = rq::launch_rowlds(x, T, K, ldx, span_log2, gsr, norm, qd->asymmetric != 0, qd->clip_ratio,
-                        qd->outlier_idx, qd->n_out, q, scale, zero, code_sum, x_out, st);
+  e = rq::launch_rowlds(x, T, K, ldx, span_log2, gsr, norm, qd->clip_ratio, q, scale, code_sum, st);
   return hip_status(e, "rowlds_quant launch");
 }
 

@@ -27,10 +27,9 @@ struct GemmArgs {
 hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int span_log2,
                            float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                            hipStream_t st);
-size_t rowlds_smem_bytes(int64_t K, int n_out);
+size_t rowlds_smem_bytes(int64_t K);
 hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int span_log2, bool gsr,
-                         float norm, bool asym, float clip, const int32_t *outlier_idx, int n_out,
-                         uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum, void *x_out,
+                         float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                          hipStream_t st);
 hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
@@ -41,6 +40,8 @@ hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, co
 hipError_t launch_kron_inverse_t(const float *p1, int n1, float *o1, const float *p2, int n2,
                                  float *o2, hipStream_t st);
 // mode 0: raw int32 accumulator; 1: symmetric fp16 output; 2: mixed fp16 output
+bool gemm_ra_fits(const GemmArgs &p);
+hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 
 }  // namespace rq

@@ -72,7 +72,8 @@ def _rotate_quant(T, K, ldx, rot, qd, x=FAKE, q=FAKE, scale=FAKE, zero=None, x_o
     (4, 4096, 4100, _rot("hadamard"), _qd(), rq.RQ_EALIGN),                   # ldx % 8
     (4, 4096, 4096, _rot("none"), _qd(asym=1, clip=0.9), rq.RQ_EINVAL),       # asym takes clip 1
     (4, 4104, 4104, _rot("none"), _qd(), rq.RQ_ESHAPE),                       # K % 64 with no split
-    (4, 32768, 32768, _rot("none"), _qd(idx=FAKE, n_out=64 * 3 + 128), rq.RQ_ESHAPE),  # LDS
+    (4, 32832, 32832, _rot("none"), _qd(idx=FAKE, n_out=64), rq.RQ_ESHAPE),   # K > 32768 unrotated
+    (4, 8232, 8232, _rot("none"), _qd(idx=FAKE, n_out=40), rq.RQ_ESHAPE),     # K % 32 unrotated
 ])
 def test_rotate_quant_validation(T, K, ldx, rot, qd, want):
     assert _rotate_quant(T, K, ldx, rot, qd, x_out=FAKE) == want

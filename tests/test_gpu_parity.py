@@ -109,11 +109,12 @@ def _outlier_pattern(inp, K, n_out, pattern):
     return idx
 
 
-# The split kernel covers K <= 8192 (K % 32 == 0), the LDS row kernel the
-# rest; 1100 rows exceed the split kernel's grid so its row loop turns over.
+# The split kernel covers every K % 32 == 0 up to 32768 (1, 2 or 4 words of
+# 32 columns per thread); 1100 rows exceed its grid, so its row loop turns over.
 @pytest.mark.parametrize("T,K,n_out,pattern", [
     (37, 8192, 256, "workload"), (5, 8192, 0, "workload"), (3, 1024, 64, "workload"),
-    (1100, 1024, 64, "clustered"), (29, 8192, 512, "clustered"), (7, 16384, 0, "workload"),
+    (1100, 1024, 64, "clustered"), (29, 8192, 512, "clustered"), (7, 16384, 256, "workload"),
+    (9, 16384, 128, "clustered"), (5, 32768, 256, "workload"), (3, 24576, 64, "clustered"),
     (11, 4096, 0, "workload")])
 def test_asymmetric_outlier_split_matches_oracle(T, K, n_out, pattern):
     note(f"[rotate_quant] asym T={T} K={K} n_out={n_out} {pattern}")
@@ -388,6 +389,64 @@ def test_edge_asymmetric_rows():
     torch.cuda.synchronize()
     check_asym_quant(host(out["q"]), host(out["scale"]), host(out["zero"]), ref)
     assert host(out["zero"])[0] == 0 and host(out["zero"])[1] == 15 and host(out["scale"])[2] == 0
+
+
+def _exact_tie_rows(seed=11, K=1024):
+    """fp16 rows whose quotients x / S hit rounding boundaries exactly in the
+    reals: symmetric rows with elements +-amax/2 (x/S = +-3.5, S = amax/7 not
+    representable, so the rounding of S to fp32 decides), symmetric rows with
+    S = 2^e representable (true ties, to even), asymmetric rows with hi = -lo
+    (zero point -lo/S = 7.5) and asymmetric rows with S = 2^e."""
+    rng = np.random.default_rng(seed)
+    sym = (rng.standard_normal((24, K)) * 0.3).astype(np.float16)
+    for r in range(16):
+        amax = np.float16(rng.uniform(0.5, 4.0))
+        sym[r] = np.clip(sym[r], -amax * 0.9, amax * 0.9)
+        sym[r, 0] = amax if r % 2 else -amax
+        sym[r, 1:9] = np.float16(amax / 2) * np.where(np.arange(8) % 2, 1, -1)
+    for r in range(16, 24):
+        e = 2.0 ** rng.integers(-4, 2)
+        sym[r] = np.clip(sym[r], -6.9 * e, 6.9 * e)
+        sym[r, 0] = 7 * e
+        sym[r, 1:15] = (np.arange(14) % 7 + 0.5) * e * np.where(np.arange(14) < 7, 1, -1)
+    asy = (rng.standard_normal((16, K)) * 0.3).astype(np.float16)
+    for r in range(8):
+        a = np.float16(rng.uniform(0.5, 4.0))
+        asy[r] = np.clip(asy[r], -a, a)
+        asy[r, 0], asy[r, 1] = a, -a
+    for r in range(8, 16):
+        e = 2.0 ** rng.integers(-4, 2)
+        lo, hi = (-7.5 * e, 7.5 * e) if r % 2 else (-5 * e, 10 * e)
+        asy[r] = np.clip(asy[r], lo, hi)
+        asy[r, 0], asy[r, 1] = lo, hi
+        asy[r, 2:12] = (np.arange(10) - 4.5) * e
+    return sym.astype(np.float16), asy.astype(np.float16)
+
+
+def test_edge_exact_fp16_ties():
+    """Unrotated fp16 inputs meet exact rounding boundaries often; the GPU
+    must round them as rne(x / fp32 scale) does, code for code."""
+    note("[edge] exact ties on fp16 inputs")
+    sym, asy = _exact_tie_rows()
+    ref = o.rotate_quant(sym, "none")
+    assert (np.abs(ref["pre"] - np.round(ref["pre"] - 0.5) - 0.5) < 1e-6).sum() >= 100
+    out = rq.rq_rotate_quant(dev(sym), rq.Rotation("none"))
+    torch.cuda.synchronize()
+    check_scales(host(out["scale"]), ref["scale"])
+    np.testing.assert_array_equal(o.unpack_int4(host(out["q"]), signed=True), ref["q"])
+    refa = o.rotate_quant(asy, "none", asym=True)
+    outa = rq.rq_rotate_quant(dev(asy), rq.Rotation("none"), asym=True)
+    torch.cuda.synchronize()
+    check_scales(host(outa["scale"]), refa["scale"])
+    np.testing.assert_array_equal(host(outa["zero"]), refa["zero"])
+    np.testing.assert_array_equal(o.unpack_int4(host(outa["q"]), signed=False), refa["q"])
+    # the weight side with an outlier split (outliers away from the crafted columns)
+    idx = np.sort(np.random.default_rng(12).choice(np.arange(64, 1024), 64, replace=False)).astype(np.int32)
+    wr = o.prepare_weights(sym, "none", outlier_idx=idx)
+    wq = rq.rq_prepare_weights(dev(sym), rq.Rotation("none"), outlier_idx=dev(idx))
+    torch.cuda.synchronize()
+    check_scales(host(wq["scale"]), wr["scale"])
+    np.testing.assert_array_equal(o.unpack_int4(host(wq["q"]), signed=True), wr["q"])
 
 
 def test_empty_and_single_row():
