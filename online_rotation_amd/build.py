@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.cpp", "rotate_quant.hip", "gemm_w4a4.hip", "gemm_ra.hip"]
+SOURCES = ["rq_api.cpp", "rotate_quant.hip", "kron.hip", "gemm_w4a4.hip", "gemm_ra.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code.
@@ -22,7 +22,7 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 # MFMA accumulators in VGPRs (no AGPR copies) where a kernel fits in 256
-# VGPRs; gemm_ra keeps its 128 accumulators in AGPRs instead.
+# VGPRs; gemm_ra and kron64_mfma keep their accumulators in AGPRs instead.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM}
 

@@ -1048,6 +1048,8 @@ hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int s
 hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, const float *fa,
                        const float *fb, const float *chan_scale, bool divide, float clip,
                        uint8_t *q, float *scale, int32_t *code_sum, hipStream_t st) {
+  if (n1 == 64 && n2 == 64)
+    return launch_kron64(x, T, ldx, fa, fb, chan_scale, divide, clip, q, scale, code_sum, st);
   const int64_t grid = T < 8192 ? T : 8192;
   kron_quant<<<dim3((unsigned)grid), dim3(256), 0, st>>>((const __half *)x, T, ldx, n1, n2, fa, fb,
                                                          chan_scale, divide ? 1 : 0, clip, q, scale,

@@ -34,6 +34,9 @@ hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int s
 hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
+hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,
+                         const float *chan_scale, bool divide, float clip, uint8_t *q, float *scale,
+                         int32_t *code_sum, hipStream_t st);
 hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, const float *fa,
                        const float *fb, const float *chan_scale, bool divide, float clip,
                        uint8_t *q, float *scale, int32_t *code_sum, hipStream_t st);
