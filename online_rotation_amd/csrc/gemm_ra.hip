@@ -40,6 +40,7 @@ constexpr int kRaNB = 3;                  // B buffers in LDS
 constexpr int kRaU = kRaD % kRaNB == 0 ? kRaD : kRaD * kRaNB;  // unroll: slot and buffer indices static
 constexpr int kRaRow = 128;               // LDS bytes per B row and k-step (int8)
 constexpr int kRaBuf = kRaBN * kRaRow;    // one buffer: 16 KB
+static_assert(kRaNB * kRaBuf >= (kRaBM + kRaBN) * 128, "outlier tiles must fit the B buffers");
 
 // Widened slot s (16 bytes) of LDS row r sits at s ^ ((r >> 1) & 7): the 16
 // rows that a group of 16 lanes reads (one row per lane) or writes (four
@@ -239,29 +240,67 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     }
   if (MODE == 2 && p.n_out > 0) {
     // FP16 outlier product on FP16 matrix cores, fp32 accumulation on top of
-    // the dequantized INT4 part.  Lane (l32, g) supplies halves
-    // [k0 + 8g, k0 + 8g + 8) of its row (A) or column (B).
-    const __half *xa0 = p.xo + min(row0 + l32, p.T - 1) * p.n_out + 8 * g;
-    const __half *xa1 = p.xo + min(row0 + 32 + l32, p.T - 1) * p.n_out + 8 * g;
-    const __half *wb[4];
+    // the dequantized INT4 part.  x_out (tile rows) and w_out (tile columns)
+    // go through the idle B buffers in chunks of 64 columns: 256 x 128 B and
+    // 128 x 128 B, loaded with coalesced 16-byte segments (the next chunk
+    // into registers while this one is multiplied).  Segment s of LDS row r
+    // sits at s ^ (r & 7).  MFMA step kk of a chunk takes halves
+    // [16kk + 8g, 16kk + 8g + 8) of a row in lane group g: segment 2kk + g.
+    uint8_t *Xs = Bs, *Ws = Bs + kRaBM * 128;
+    const int nch = (p.n_out + 63) / 64;
+    uint4 px[8], pw[4];
+    auto cload = [&](int c) {  // columns past n_out are clamped and never multiplied
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wb[j] = p.wo + min(col0 + 32 * j + l32, p.N - 1) * p.n_out + 8 * g;
-    for (int k0 = 0; k0 < p.n_out; k0 += 16) {
-      v8h av[2], bv[4];
-      uint4 t = *reinterpret_cast<const uint4 *>(xa0 + k0);
-      __builtin_memcpy(&av[0], &t, 16);
-      t = *reinterpret_cast<const uint4 *>(xa1 + k0);
-      __builtin_memcpy(&av[1], &t, 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        t = *reinterpret_cast<const uint4 *>(wb[j] + k0);
-        __builtin_memcpy(&bv[j], &t, 16);
+      for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, row = idx >> 3, col = min(64 * c + 8 * (idx & 7), p.n_out - 8);
+        px[i] = *reinterpret_cast<const uint4 *>(p.xo + min(m0 + row, p.T - 1) * p.n_out + col);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, row = idx >> 3, col = min(64 * c + 8 * (idx & 7), p.n_out - 8);
+        pw[i] = *reinterpret_cast<const uint4 *>(p.wo + min(n0 + row, p.N - 1) * p.n_out + col);
+      }
+    };
+    auto cstore = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          f[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], f[i][j], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, row = idx >> 3, sg = idx & 7;
+        *reinterpret_cast<uint4 *>(Xs + row * 128 + ((sg ^ (row & 7)) << 4)) = px[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, row = idx >> 3, sg = idx & 7;
+        *reinterpret_cast<uint4 *>(Ws + row * 128 + ((sg ^ (row & 7)) << 4)) = pw[i];
+      }
+    };
+    cload(0);
+    __syncthreads();  // every wave is done with the B buffers
+    for (int c = 0; c < nch; ++c) {
+      cstore();
+      __syncthreads();
+      if (c + 1 < nch) cload(c + 1);
+      const int ksteps = min(4, (p.n_out - 64 * c) / 16);
+      for (int kk = 0; kk < ksteps; ++kk) {
+        v8h av[2], bv[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = wave * 64 + 32 * i + l32;
+          const uint4 t = *reinterpret_cast<const uint4 *>(Xs + r * 128 + (((2 * kk + g) ^ (r & 7)) << 4));
+          __builtin_memcpy(&av[i], &t, 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 32 * j + l32;
+          const uint4 t = *reinterpret_cast<const uint4 *>(Ws + r * 128 + (((2 * kk + g) ^ (r & 7)) << 4));
+          __builtin_memcpy(&bv[j], &t, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            f[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], f[i][j], 0, 0, 0);
+      }
+      __syncthreads();  // before the next chunk overwrites the tiles
     }
   }
   __half *out = reinterpret_cast<__half *>(p.out);
