@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.cpp", "rotate_quant.hip", "kron.hip", "gemm_w4a4.hip", "gemm_ra.hip"]
+SOURCES = ["rq_api.cpp", "rotate_quant.hip", "kron.hip", "gemm_w4a4.hip", "gemm_ra.hip",
+           "gemm_decode.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code.
@@ -24,7 +25,7 @@ HIPCC_FLAGS = [
 # MFMA accumulators in VGPRs (no AGPR copies) where a kernel fits in 256
 # VGPRs; gemm_ra and kron64_mfma keep their accumulators in AGPRs instead.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM}
+EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM, "gemm_decode.hip": VGPR_FORM}
 
 
 def _hipcc() -> str:

@@ -463,7 +463,11 @@ hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t
     case 6:
       return (p.T >= 256 && p.Kb % kBKB == 0) ? launch_wg<4>(p, x_unsigned, mode, st)
                                               : launch_tiles<2, 2>(p, x_unsigned, mode, st);
+    case 7:
+      return gemm_ra_fits(p) ? launch_gemm_ra(p, x_unsigned, mode, st)
+                             : launch_tiles<2, 2>(p, x_unsigned, mode, st);
     default:
+      if (gemm_decode_fits(p)) return launch_gemm_decode(p, x_unsigned, mode, st);
       return gemm_ra_fits(p) ? launch_gemm_ra(p, x_unsigned, mode, st)
                              : launch_tiles<2, 2>(p, x_unsigned, mode, st);
   }

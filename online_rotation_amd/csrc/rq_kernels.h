@@ -43,6 +43,8 @@ hipError_t launch_kron(const void *x, int64_t T, int64_t ldx, int n1, int n2, co
 hipError_t launch_kron_inverse_t(const float *p1, int n1, float *o1, const float *p2, int n2,
                                  float *o2, hipStream_t st);
 // mode 0: raw int32 accumulator; 1: symmetric fp16 output; 2: mixed fp16 output
+bool gemm_decode_fits(const GemmArgs &p);
+hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);

@@ -169,8 +169,12 @@ def test_prepare_weights_matches_oracle(case):
 
 # ----------------------------------------------------------------------------- GEMM
 
+# T <= 32 runs the decode kernel (K split over four wavefronts, a ragged
+# split when K/128 is not a multiple of 4), T >= 256 the register-A kernel,
+# the rest and K % 128 != 0 the LDS-tile kernel.
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
-               (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64)]
+               (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
+               (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -197,7 +201,8 @@ def test_linear_epilogue_on_oracle_codes(T, N, K):
 
 
 @pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False),
-                                            (300, 150, 256, True), (260, 70, 32, False)])
+                                            (300, 150, 256, True), (260, 70, 32, False),
+                                            (8, 300, 256, True), (32, 64, 96, True), (1, 40, 32, False)])
 def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     note(f"[mixed_linear] T={T} N={N} n_out={n_out} asym={asym}")
     K = 7936
