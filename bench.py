@@ -1,17 +1,23 @@
 """Benchmark of the rotated W4A4 linear layer on one MI355X.
 
-One step = the whole online path on one batch: rq_rotate_quant (4096-point
-Walsh-Hadamard + per-token INT4) followed by rq_w4a4_linear (INT4 GEMM,
-INT32 accumulation, fp16 dequant), LLaMA-2-7B-shaped T=2048, K=N=4096.
-Weights are rotated and quantized once beforehand (offline, untimed).
+One step = the whole online path on one batch of one workload:
+rq_rotate_quant (the workload's online transform + per-token INT4) followed
+by the INT4 GEMM with its dequantization epilogue (rq_w4a4_linear, or
+rq_mixed_outlier_linear with FP16 outlier columns).  Weights are rotated and
+quantized once beforehand (offline, untimed).  The default workload is the
+LLaMA-2-7B-shaped projection: T=2048, K=N=4096, 4096-point Walsh-Hadamard.
 
-Inputs cycle through enough buffer sets (>512 MB) that HBM, not the 256 MB
-Infinity Cache, serves them.  Steps are captured in a HIP graph and replayed
-so host launch cost does not enter the timing; per-kernel durations come from
-HIP events on the launch stream around graphs of back-to-back launches of one
-kernel.
+Inputs cycle through enough buffer sets (>640 MB) that HBM, not the 256 MB
+Infinity Cache, serves them.  The K timed steps are one HIP graph replay,
+bracketed by events on the stream the kernels run on; per-kernel durations
+come from events around graphs of back-to-back launches of one call.
 
-Prints one JSON line (see the fields below).
+Prints one JSON line.  `roofline` is the dominant kernel (the GEMM) against
+its bound: INT8 MFMA dense peak, or HBM at decode sizes (T <= 32);
+`roofline.traffic` comes from the rocprofv3 counter record under profiles/
+when one exists for this kernel, workload and kernel source, else null.
+`--counters` instead launches calibration kernels of known traffic and the
+two calls a few times, for `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` runs.
 """
 from __future__ import annotations
 
@@ -29,6 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 rotated-linear TOPS (T=2048,K=N=4096) + rotate-quant GB/s, % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+FP64_PEAK_TFLOPS = 78.6        # MI355X dense FP64 MFMA
+CALIB_BYTES = 512 << 20        # calibration fill / sum for the counter runs
 
 
 def parse():
@@ -42,7 +50,27 @@ def parse():
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="launch the calibration kernels and each call a few times, print one line")
     return ap.parse_args()
+
+
+def gemm_kernel(T, Kb):
+    """The GEMM kernel the library dispatches to (launch_gemm's rules)."""
+    if Kb % 64 == 0 and T <= 32:
+        return "gemm_decode"
+    if Kb % 64 == 0 and T >= 256:
+        return "gemm_ra"
+    return "gemm_w4a4"
+
+
+def quant_kernel(wl):
+    """The quantizer kernel the library dispatches to (run_quant's rules)."""
+    if wl.rot in ("hadamard", "gsr") and wl.K == 4096:
+        return "fwht4096_mfma"
+    if wl.rot == "kron":
+        return "kron64_mfma" if wl.K == 4096 else "kron_quant"
+    return "split_quant" if wl.rot == "none" else "rowlds_quant"
 
 
 def cpu_baseline(inp, wl, seconds):
@@ -79,12 +107,13 @@ def cpu_baseline(inp, wl, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
     import online_rotation_amd as rq
+    from online_rotation_amd import prof
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -139,6 +168,23 @@ def main():
     def step(i):
         rotate(i)
         gemm(i)
+
+    if args.counters:
+        # calibration: a float64 fill writes CALIB_BYTES, a float64 sum reads
+        # them (the only float64 kernels in the run); then four passes over
+        # the buffer sets, so that the median launch is a steady-state one
+        calib = torch.empty(CALIB_BYTES // 8, dtype=torch.float64, device=dev)
+        for _ in range(3):
+            calib.fill_(1.0)
+        for _ in range(3):
+            calib.sum()
+        for i in range(4 * S):
+            step(i % S)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters": "done", "workload": wl.name, "calib_bytes": CALIB_BYTES,
+                          "gemm_kernel": gemm_kernel(T, Kq // 2), "quant_kernel": quant_kernel(wl)}),
+              flush=True)
+        return
 
     # eager warmup (also the reference for the graph-replay check)
     for i in range(max(args.warmup, S)):
@@ -205,7 +251,25 @@ def main():
     gemm_tops = ops / gemm_s / 1e12
     rq_gbs = rq_bytes / rot_s / 1e9
     gemm_bytes = w_bytes + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
-    decode = T <= 64                                  # weight-streaming regime
+    gk, qk = gemm_kernel(T, Kq // 2), quant_kernel(wl)
+    decode = gk == "gemm_decode"
+    traffic = prof.read_traffic(os.path.join(ROOT, "profiles", f"{gk}_{wl.name}_traffic.txt"), gk)
+    if decode:
+        roof = {"bound": "hbm", "achieved": round(gemm_bytes / gemm_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gemm_bytes / gemm_s / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": gk, "algorithmic_bytes_per_launch": gemm_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                "kernel": gk, "ops_per_launch": ops, "note": "integer ops against the INT8 MFMA peak"}
+    roof["avg_launch_us"] = round(gemm_s * 1e6, 3)
+    quant = {"kernel": qk, "bound": "hbm", "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": rq_bytes,
+             "avg_launch_us": round(rot_s * 1e6, 3)}
+    if qk == "kron64_mfma":   # the FP64 transform: 2 x 64^3 multiply-adds per token
+        fl = 2.0 * 2 * 64 ** 3 * T
+        quant["fp64_tflops"] = round(fl / rot_s / 1e12, 2)
+        quant["fp64_frac"] = round(fl / rot_s / 1e12 / FP64_PEAK_TFLOPS, 4)
     rec = {
         "metric": METRIC,
         "value": round(ops / step_s / 1e12, 2),
@@ -224,20 +288,8 @@ def main():
                                f"X fp16 [{T},{K}], W int4 [{N},{Kq}]" + (f" + fp16 [{N},{n_out}]" if mixed else ""),
                    "T": T, "K": K, "N": N, "rotation": wl.rot, "block": wl.block, "n_out": n_out,
                    "clip_x": wl.clip_x, "buffer_sets": S, "footprint_MB": round(footprint / 2**20)},
-        "roofline": ({"bound": "hbm", "kernel": "gemm_w4a4", "achieved": round(gemm_bytes / gemm_s / 1e9, 1),
-                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(gemm_bytes / gemm_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                      "bytes_per_launch": gemm_bytes, "avg_launch_us": round(gemm_s * 1e6, 3)}
-                     if decode else
-                     {"bound": "mfma", "kernel": "gemm_w4a4", "achieved": round(gemm_tops, 1),
-                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                      "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
-                      "avg_launch_us": round(gemm_s * 1e6, 3)}),
-        "rotate_quant": {"bound": "hbm", "kernel": {"hadamard": "fwht4096_mfma", "gsr": "fwht4096_mfma",
-                                                   "kron": "kron_quant", "none": "rowlds_quant"}[wl.rot],
-                         "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(rq_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": rq_bytes,
-                         "avg_launch_us": round(rot_s * 1e6, 3)},
+        "roofline": roof,
+        "rotate_quant": quant,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -113,6 +113,22 @@ def _gpu(*ts):
             raise ValueError("rq: tensors must live on the GPU (no CPU path exists)")
 
 
+def _want(t, name, dtype, shape=None, dense=True):
+    """Check what the C ABI will read through t: dtype, shape, and either
+    dense rows (the ABI takes no stride) or unit inner stride (it takes a
+    leading dimension)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"rq: {name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"rq: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"rq: {name} must be contiguous")
+    if not dense and t.dim() == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"rq: {name} needs unit stride along its rows")
+
+
 @dataclass
 class Rotation:
     """Online transform descriptor (tensors are kept alive by this object)."""
@@ -121,6 +137,18 @@ class Rotation:
     p1: object = None          # fp32 [n1, n1] device tensor (kron)
     p2: object = None          # fp32 [n2, n2] device tensor (kron)
     chan_scale: object = None  # fp32 [K] device tensor or None (kron)
+
+    def check(self, K: int):
+        import torch
+        if self.kind not in ROT_KINDS:
+            raise ValueError(f"rq: unknown rotation kind {self.kind!r}")
+        if self.kind == "kron":
+            if self.p1 is None or self.p2 is None:
+                raise ValueError("rq: kron needs p1 and p2")
+            n1, n2 = int(self.p1.shape[0]), int(self.p2.shape[0])
+            _want(self.p1, "p1", torch.float32, (n1, n1))
+            _want(self.p2, "p2", torch.float32, (n2, n2))
+            _want(self.chan_scale, "chan_scale", torch.float32, (K,))
 
     def desc(self) -> _RotDesc:
         n1 = int(self.p1.shape[0]) if self.p1 is not None else 0
@@ -140,6 +168,9 @@ def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
     import torch
     _gpu(x, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
     T, K = x.shape
+    _want(x, "x", torch.float16, dense=False)
+    _want(outlier_idx, "outlier_idx", torch.int32)
+    rot.check(K)
     qd, n_out = _qdesc(asym, clip, outlier_idx)
     dev = x.device
     o = dict(out or {})
@@ -148,6 +179,12 @@ def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
     o.setdefault("zero", torch.empty((T,), dtype=torch.int32, device=dev) if asym else None)
     o.setdefault("code_sum", torch.empty((T,), dtype=torch.int32, device=dev) if code_sum else None)
     o.setdefault("x_out", torch.empty((T, n_out), dtype=torch.float16, device=dev) if n_out else None)
+    _want(o["q"], "q", torch.uint8, (T, (K - n_out) // 2))
+    _want(o["scale"], "scale", torch.float32, (T,))
+    _want(o["zero"], "zero", torch.int32, (T,))
+    _want(o["code_sum"], "code_sum", torch.int32, (T,))
+    _want(o["x_out"], "x_out", torch.float16, (T, n_out))
+    _gpu(*o.values())
     rd = rot.desc()
     st = lib().rq_rotate_quant(_ptr(x), T, K, x.stride(0), ctypes.byref(rd), ctypes.byref(qd),
                                _ptr(o["q"]), _ptr(o["scale"]), _ptr(o["zero"]),
@@ -161,6 +198,9 @@ def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None) ->
     import torch
     _gpu(w, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
     N, K = w.shape
+    _want(w, "w", torch.float16, dense=False)
+    _want(outlier_idx, "outlier_idx", torch.int32)
+    rot.check(K)
     qd, n_out = _qdesc(False, clip, outlier_idx)
     dev = w.device
     rd = rot.desc()
@@ -181,10 +221,15 @@ def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None) ->
 def rq_w4a4_linear(qx, sx, qw, sw, out=None):
     """fp16 y [T, N] = acc * sx[t] * sw[n] from packed symmetric codes."""
     import torch
-    _gpu(qx, sx, qw, sw)
+    _gpu(qx, sx, qw, sw, out)
     T, Kb = qx.shape
     N = qw.shape[0]
+    _want(qx, "qx", torch.uint8)
+    _want(qw, "qw", torch.uint8, (N, Kb))
+    _want(sx, "sx", torch.float32, (T,))
+    _want(sw, "sw", torch.float32, (N,))
     y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=qx.device)
+    _want(y, "out", torch.float16, (T, N), dense=False)
     st = lib().rq_w4a4_linear(_ptr(qx), _ptr(sx), T, 2 * Kb, _ptr(qw), _ptr(sw), N, _ptr(y),
                               y.stride(0), _stream(qx.device))
     _check(st, "rq_w4a4_linear")
@@ -194,11 +239,22 @@ def rq_w4a4_linear(qx, sx, qw, sw, out=None):
 def rq_mixed_outlier_linear(qx, sx, zx, qw, sw, w_rowsum, x_out=None, w_out=None, out=None):
     """QUIK mixed linear: dequantized INT4 part + fp16 outlier product."""
     import torch
-    _gpu(qx, sx, zx, qw, sw, w_rowsum, x_out, w_out)
+    _gpu(qx, sx, zx, qw, sw, w_rowsum, x_out, w_out, out)
     T, Kb = qx.shape
     N = qw.shape[0]
     n_out = 0 if x_out is None else int(x_out.shape[1])
+    _want(qx, "qx", torch.uint8)
+    _want(qw, "qw", torch.uint8, (N, Kb))
+    _want(sx, "sx", torch.float32, (T,))
+    _want(zx, "zx", torch.int32, (T,))
+    _want(sw, "sw", torch.float32, (N,))
+    _want(w_rowsum, "w_rowsum", torch.int32, (N,))
+    _want(x_out, "x_out", torch.float16, (T, n_out))
+    if (x_out is None) != (w_out is None):
+        raise ValueError("rq: x_out and w_out come together")
+    _want(w_out, "w_out", torch.float16, (N, n_out))
     y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=qx.device)
+    _want(y, "out", torch.float16, (T, N), dense=False)
     st = lib().rq_mixed_outlier_linear(_ptr(qx), _ptr(sx), _ptr(zx), T, 2 * Kb, _ptr(qw),
                                        _ptr(sw), _ptr(w_rowsum), N, _ptr(x_out), _ptr(w_out),
                                        n_out, _ptr(y), y.stride(0), _stream(qx.device))
@@ -209,10 +265,13 @@ def rq_mixed_outlier_linear(qx, sx, zx, qw, sw, w_rowsum, x_out=None, w_out=None
 def rq_w4a4_gemm_i32(qx, qw, x_unsigned: bool = False, out=None):
     """Raw INT32 accumulator [T, N] (for bit-exact tests)."""
     import torch
-    _gpu(qx, qw)
+    _gpu(qx, qw, out)
     T, Kb = qx.shape
     N = qw.shape[0]
+    _want(qx, "qx", torch.uint8)
+    _want(qw, "qw", torch.uint8, (N, Kb))
     acc = out if out is not None else torch.empty((T, N), dtype=torch.int32, device=qx.device)
+    _want(acc, "out", torch.int32, (T, N), dense=False)
     st = lib().rq_w4a4_gemm_i32(_ptr(qx), 1 if x_unsigned else 0, T, 2 * Kb, _ptr(qw), N,
                                 _ptr(acc), acc.stride(0), _stream(qx.device))
     _check(st, "rq_w4a4_gemm_i32")
