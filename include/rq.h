@@ -71,6 +71,7 @@ typedef enum {
  *             M = (x * chan_scale) reshaped row-major.  K == n1 * n2,
  *             1 <= n1, n2 <= 64.  p1: fp32 [n1, n1], p2: fp32 [n2, n2],
  *             chan_scale: fp32 [K] or NULL (all ones).
+ *   NONE      K % 32 == 0, K <= 32768.
  * Rotations (kind != NONE) require n_out == 0 in the quantizer descriptor. */
 typedef struct {
   int32_t kind;
