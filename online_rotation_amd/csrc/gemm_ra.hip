@@ -5,7 +5,10 @@
 //
 // Workgroup: 256 threads = 4 wavefronts, one per SIMD; tile 256 tokens x 128
 // output channels.  Wavefront w owns tile rows [64w, 64w + 64) against all
-// 128 columns: 2 x 4 MFMA 32x32x32 blocks, 128 accumulator registers.
+// 128 columns: 2 x 4 MFMA 32x32x32 blocks, 128 accumulator registers.  The
+// kernel fits two workgroups per CU (256 registers per lane, 48 KB of LDS),
+// so that one workgroup's waits are covered by the other's MFMAs whenever a
+// CU gets more than one tile.
 //
 // What sets the design, per 32-code k slice and CU: 32 MFMAs (8 per SIMD).
 // Measured on this chip, LDS serves about 136 bytes per clock per CU to
@@ -56,7 +59,7 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
 }  // namespace
 
 template <bool XU, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   __shared__ __align__(16) uint8_t Bs[kRaNB * kRaBuf];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
