@@ -26,7 +26,6 @@
 #include "rq_kernels.h"
 #include "gemm_common.h"
 
-#include <stdlib.h>
 
 namespace rq {
 
@@ -234,199 +233,6 @@ __global__ __launch_bounds__(256) void gemm_w4a4(GemmArgs p, int nt_m, int nt_n)
   }
 }
 
-// ---------------------------------------------------------------------------
-// gemm_wg: the large-T kernel.  Widening int4 to int8 costs VALU work that
-// does not overlap the matrix cores, so each packed chunk is widened once
-// per workgroup on its way into LDS (instead of once per wavefront that
-// reads it), and the wavefronts read ready int8 MFMA operands.
-// Workgroup = 8 wavefronts (4 x 2, each 64 x 64) on a 256 x 128 tile; a
-// k-step is 128 codes: 64 packed bytes per row in global memory, 128 int8
-// bytes per row in LDS.  LDS is double-buffered (96 KB) with one barrier
-// per k-step: step kb+1 is widened and stored while step kb is multiplied.
-// Unpacked rows are 8 slots of 16 bytes; slot s of row r sits at
-// s ^ ((r >> 1) & 7), so the 16 rows a group of 16 lanes touches (reads: one
-// row per lane; stores: four lanes per row) fall in distinct banks.
-// ---------------------------------------------------------------------------
-constexpr int kWgBM = 256, kWgBN = 128, kWgRow = 128;
-
-__device__ __forceinline__ int wg_off(int row, int slot) {
-  return row * kWgRow + ((slot ^ ((row >> 1) & 7)) << 4);
-}
-
-template <int MW, bool XU, int MODE>
-__global__ __launch_bounds__(128 * MW) void gemm_wg(GemmArgs p, int nt_m, int nt_n) {
-  // K is a multiple of 128 codes here (whole 64-byte k-steps, no tail).
-  // MW x 2 wavefronts of 64 x 64; tile (64*MW) x 128.
-  constexpr int NT = 128 * MW, BM = 64 * MW, BN = kWgBN, LA = BM * 4 / NT, LB = BN * 4 / NT;
-  constexpr int D = 4;  // global prefetch distance (k-steps); unroll = lcm(D, 2 LDS buffers)
-  __shared__ __align__(16) uint8_t As[2][BM * kWgRow];
-  __shared__ __align__(16) uint8_t Bs[2][BN * kWgRow];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % MW, wn = wave / MW;
-  int tm, tn;
-  map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t Kb = p.Kb;
-  const int nsteps = (int)(Kb / kBKB);
-
-  const uint8_t *abase = p.qx + m0 * Kb;
-  const uint8_t *bbase = p.qw + n0 * Kb;
-  uint32_t aoff[LA], boff[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int c = tid + i * NT;
-    aoff[i] = (uint32_t)((min(m0 + (c >> 2), p.T - 1) - m0) * Kb) + (c & 3) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int c = tid + i * NT;
-    boff[i] = (uint32_t)((min(n0 + (c >> 2), p.N - 1) - n0) * Kb) + (c & 3) * 16;
-  }
-  // The loop below issues the same loads and stores every step, with no
-  // data-dependent branches around them, so the compiler can wait for just
-  // the oldest prefetch group (a conditional load makes it wait for all).
-  uint4 ra[D][LA], rb[D][LB];
-  auto gload = [&](int slot, int kb) {  // kb is clamped by the caller
-    const uint8_t *a = abase + (int64_t)kb * kBKB, *b = bbase + (int64_t)kb * kBKB;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[slot][i] = *reinterpret_cast<const uint4 *>(a + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[slot][i] = *reinterpret_cast<const uint4 *>(b + boff[i]);
-  };
-  auto widen_store = [&](uint8_t *base, int c, uint4 w, bool xu) {
-    const int row = c >> 2, q = c & 3;
-    const v4i s0 = xu ? widen_unsigned(w.x, w.y) : widen_signed(w.x, w.y);
-    const v4i s1 = xu ? widen_unsigned(w.z, w.w) : widen_signed(w.z, w.w);
-    *reinterpret_cast<v4i *>(base + wg_off(row, 2 * q)) = s0;
-    *reinterpret_cast<v4i *>(base + wg_off(row, 2 * q + 1)) = s1;
-  };
-  auto sstore = [&](int buf, int slot) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) widen_store(As[buf], tid + i * NT, ra[slot][i], XU);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) widen_store(Bs[buf], tid + i * NT, rb[slot][i], false);
-  };
-
-  v16i acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-  const int g = lane >> 5, l32 = lane & 31;
-  auto compute = [&](int buf) {
-    // all 16 fragment reads first, so the MFMAs only wait for the oldest ones
-    v4i ao[4][2], bo[4][2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        ao[c][i] = *reinterpret_cast<const v4i *>(&As[buf][wg_off(wm * 64 + i * 32 + l32, 2 * c + g)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bo[c][j] = *reinterpret_cast<const v4i *>(&Bs[buf][wg_off(wn * 64 + j * 32 + l32, 2 * c + g)]);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[c][i], bo[c][j], acc[i][j], 0, 0, 0);
-  };
-
-  const int last = nsteps - 1;
-#pragma unroll
-  for (int s = 0; s < D; ++s) gload(s, min(s, last));
-  sstore(0, 0);
-  __syncthreads();
-  gload(0, min(D, last));
-  // steps padded to a multiple of D; padded steps load/store but skip compute
-  for (int kb0 = 0; kb0 < nsteps; kb0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int kb = kb0 + s;
-      sstore((s + 1) & 1, (s + 1) % D);           // step kb+1 (garbage past the end: never used)
-      gload((s + 1) % D, min(kb + 1 + D, last));  // refill the slot just consumed
-      if (kb < nsteps) compute(s & 1);
-      __syncthreads();
-    }
-  }
-
-  // epilogue (same accumulator layout as gemm_w4a4)
-  constexpr int kShift = XU ? 4 : 8;
-  const int64_t row0 = m0 + wm * 64, col0 = n0 + wn * 64;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t gn = col0 + 32 * j + l32;
-      const int64_t rbase = row0 + 32 * i + 4 * g;
-      if (MODE == 0) {
-        int32_t *out = reinterpret_cast<int32_t *>(p.out);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
-          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = acc[i][j][r] >> kShift;
-        }
-      } else {
-        v16f f;
-        const float swn = gn < p.N ? p.sw[gn] : 0.0f;
-        const int32_t rsn = (MODE == 2 && p.zx && gn < p.N) ? p.rowsum[gn] : 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
-          int32_t v = acc[i][j][r] >> kShift;
-          float sxm = 0.0f;
-          if (gm < p.T) {
-            sxm = p.sx[gm];
-            if (MODE == 2 && p.zx) v -= p.zx[gm] * rsn;
-          }
-          f[r] = (float)v * sxm * swn;
-        }
-        if (MODE == 2 && p.n_out > 0) {
-          const int64_t am = min(row0 + 32 * i + l32, p.T - 1);
-          const int64_t bn = min(col0 + 32 * j + l32, p.N - 1);
-          const __half *arow = p.xo + am * p.n_out;
-          const __half *brow = p.wo + bn * p.n_out;
-          for (int k0 = 0; k0 < p.n_out; k0 += 16) {
-            v8h av, bv;
-            const uint4 ua = *reinterpret_cast<const uint4 *>(arow + k0 + g * 8);
-            const uint4 ub = *reinterpret_cast<const uint4 *>(brow + k0 + g * 8);
-            __builtin_memcpy(&av, &ua, 16);
-            __builtin_memcpy(&bv, &ub, 16);
-            f = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, f, 0, 0, 0);
-          }
-        }
-        __half *out = reinterpret_cast<__half *>(p.out);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t gm = rbase + 8 * (r >> 2) + (r & 3);
-          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(f[r]);
-        }
-      }
-    }
-  }
-}
-
-template <int MW>
-static hipError_t launch_wg(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
-  constexpr int BM = 64 * MW;
-  const int nt_m = (int)((p.T + BM - 1) / BM), nt_n = (int)((p.N + kWgBN - 1) / kWgBN);
-  const dim3 grid((unsigned)(nt_m * nt_n)), block(128 * MW);
-  if (mode == 0) {
-    if (x_unsigned) gemm_wg<MW, true, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-    else gemm_wg<MW, false, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-  } else if (mode == 1) {
-    gemm_wg<MW, false, 1><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-  } else {
-    if (x_unsigned) gemm_wg<MW, true, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-    else gemm_wg<MW, false, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-  }
-  return hipGetLastError();
-}
-
 template <int WMB, int WNB>
 static hipError_t launch_tiles(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
   constexpr int BM = 64 * WMB, BN = 64 * WNB;
@@ -444,33 +250,13 @@ static hipError_t launch_tiles(const GemmArgs &p, bool x_unsigned, int mode, hip
   return hipGetLastError();
 }
 
-static int gemm_variant() {
-  static int v = [] {
-    const char *e = getenv("RQ_GEMM_VARIANT");
-    return e ? atoi(e) : 1;
-  }();
-  return v;
-}
-
+// Dispatch: the decode kernel for T <= 32, the register-A kernel for
+// T >= 256, this file's LDS-tile kernel otherwise (and whenever K is not a
+// multiple of 128 codes).
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
-  switch (gemm_variant()) {
-    case 2: return launch_tiles<4, 2>(p, x_unsigned, mode, st);
-    case 3: return launch_tiles<2, 4>(p, x_unsigned, mode, st);
-    case 4: return launch_tiles<2, 2>(p, x_unsigned, mode, st);
-    case 5:
-      return (p.T >= 128 && p.Kb % kBKB == 0) ? launch_wg<2>(p, x_unsigned, mode, st)
-                                              : launch_tiles<2, 2>(p, x_unsigned, mode, st);
-    case 6:
-      return (p.T >= 256 && p.Kb % kBKB == 0) ? launch_wg<4>(p, x_unsigned, mode, st)
-                                              : launch_tiles<2, 2>(p, x_unsigned, mode, st);
-    case 7:
-      return gemm_ra_fits(p) ? launch_gemm_ra(p, x_unsigned, mode, st)
-                             : launch_tiles<2, 2>(p, x_unsigned, mode, st);
-    default:
-      if (gemm_decode_fits(p)) return launch_gemm_decode(p, x_unsigned, mode, st);
-      return gemm_ra_fits(p) ? launch_gemm_ra(p, x_unsigned, mode, st)
-                             : launch_tiles<2, 2>(p, x_unsigned, mode, st);
-  }
+  if (gemm_decode_fits(p)) return launch_gemm_decode(p, x_unsigned, mode, st);
+  if (gemm_ra_fits(p)) return launch_gemm_ra(p, x_unsigned, mode, st);
+  return launch_tiles<2, 2>(p, x_unsigned, mode, st);
 }
 
 }  // namespace rq
