@@ -136,9 +136,188 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs p) {
   }
 }
 
+// gemm_decode16: T <= 16, activation codes staged in LDS.
+//
+// Reading the activation fragment of every k-step from L2 next to the weight
+// fragment measured ~25% off the weight stream's rate, so here each
+// workgroup copies the T activation rows (and, for the outlier product, the
+// T rows of x_out) into LDS once, and the register ring carries weight bytes
+// only.  One wavefront owns 16 output channels.
+// v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_f16 operands: lane l supplies
+// row (A) or column (B) l%16 and k group l/16; register r of lane l holds
+// row 4(l/16) + r, column l%16 (measured on gfx950).
+// The stream of a wavefront is nsteps INT4 steps followed by n_out/32 FP16
+// outlier steps; lane (c, kg) loads bytes [64j + 16kg, 64j + 16kg + 16) of
+// its weight row (INT4: codes 128j + 32kg ..; FP16: w_out halves 32j + 8kg ..)
+// and the same span of the staged activation row.  Widened dwords (x, y)
+// feed INT8 MFMA 0 and (z, w) MFMA 1.  Each step issues both MFMA kinds and
+// zeroes the operands of the kind it is not, so the loop has no branch;
+// the zero products leave both accumulators (and their summation order)
+// exactly as a loop over the live steps alone would.
+namespace {
+constexpr int kD16 = 8;          // load ring depth (k-steps)
+constexpr int kD16Chunks = 16;   // staged 16-byte chunks per thread (64 KB per workgroup)
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+// staged row pitches: 16 bytes of padding put the 16 rows a load
+// instruction reads on 16 distinct 16-byte LDS bank groups
+__host__ __device__ inline uint32_t d16_pitch(int64_t bytes) { return (uint32_t)bytes + 16; }
+__host__ __device__ inline size_t d16_lds(int64_t T, int64_t Kb, int64_t n_out) {
+  return (size_t)T * d16_pitch(Kb) + (n_out ? (size_t)T * d16_pitch(2 * n_out) : 0);
+}
+// the staged bytes fit the per-thread chunk budget
+inline bool d16_fits(int64_t T, int64_t Kb, int64_t n_out) {
+  return T <= 16 && T * (Kb / 16 + n_out / 8) <= 256 * kD16Chunks;
+}
+// floor(c / d) = umulhi(c, m) with m = ceil(2^32 / d) = floor((2^32 - 1) / d) + 1
+// (d >= 2): exact while c * d < 2^32
+__device__ inline uint32_t d16_magic(uint32_t d) { return 0xFFFFFFFFu / d + 1; }
+}  // namespace
+
+template <bool XU, int MODE>
+__global__ __launch_bounds__(256) void gemm_decode16(GemmArgs p) {
+  extern __shared__ __align__(16) uint8_t xs[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, l16 = lane & 15;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 16, Kb = p.Kb;
+  const int nsteps = (int)(Kb >> 6), last = nsteps - 1;
+  const int nk = MODE == 2 ? p.n_out / 32 : 0;  // outlier steps
+  const int S = nsteps + nk;
+  const uint32_t T = (uint32_t)p.T;
+  const uint32_t pa = d16_pitch(Kb), po = d16_pitch(2 * (int64_t)p.n_out);
+  const uint32_t xo_base = T * pa;
+
+  // weight stream of this lane: INT4 row, then its outlier row
+  const int64_t nrow = min(n0 + l16, p.N - 1);
+  const uint8_t *bp = p.qw + nrow * Kb + 16 * kg;
+  const uint8_t *wp = nk ? reinterpret_cast<const uint8_t *>(p.wo + nrow * p.n_out) + 16 * kg : bp;
+  auto src = [&](int j) {
+    return j < nsteps ? bp + 64 * (int64_t)j : wp + 64 * (int64_t)min(j - nsteps, nk - 1);
+  };
+
+  // Staging: 16-byte chunks c < na are activation codes (row c / ka), the
+  // next no are x_out halves (row (c - na) / ko); kD16Chunks per thread.
+  const uint32_t ka = (uint32_t)(Kb >> 4), ko = (uint32_t)p.n_out >> 3;
+  const uint32_t na = T * ka, no = nk ? T * ko : 0;
+  const uint8_t *xo = reinterpret_cast<const uint8_t *>(p.xo);
+  // Two groups of 8 loads in registers; a lane past the end reloads the
+  // last chunk (one shared line per instruction).
+  const uint32_t nt = na + no;
+  v4u s0[kD16Chunks / 2], s1[kD16Chunks / 2];
+  auto sload = [&](v4u (&v)[kD16Chunks / 2], int h) {
+#pragma unroll
+    for (int i = 0; i < kD16Chunks / 2; ++i) {
+      const uint32_t c = min(256 * (8 * h + i) + tid, nt - 1);
+      v[i] = *reinterpret_cast<const v4u *>(c < na ? p.qx + 16 * (int64_t)c : xo + 16 * (int64_t)(c - na));
+    }
+  };
+  sload(s0, 0);
+  sload(s1, 1);  // unconditional: a branch here makes the compiler wait for both groups at its join
+  // the weight ring's prologue goes out behind the staging loads, so waiting
+  // for the latter below leaves it in flight
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 rb[kD16];
+#pragma unroll
+  for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
+    auto sstore = [&](const v4u (&v)[kD16Chunks / 2], int h) {
+#pragma unroll
+      for (int i = 0; i < kD16Chunks / 2; ++i) {
+        const uint32_t c = 256 * (8 * h + i) + tid;
+        if (c < na) {
+          const uint32_t r = __umulhi(c, ma);
+          *reinterpret_cast<v4u *>(xs + r * pa + 16 * (c - r * ka)) = v[i];
+        } else if (c < nt) {
+          const uint32_t c2 = c - na, r = __umulhi(c2, mo);
+          *reinterpret_cast<v4u *>(xs + xo_base + r * po + 16 * (c2 - r * ko)) = v[i];
+        }
+      }
+    };
+    sstore(s0, 0);
+    if (nt > 256 * kD16Chunks / 2) sstore(s1, 1);
+  }
+  __syncthreads();
+  if (n0 >= p.N) return;  // whole wavefront past the last channel (after its share of the staging)
+
+  const uint32_t arow = min((uint32_t)l16, T - 1);
+  const uint8_t *xa = xs + arow * pa + 16 * kg;
+  const uint8_t *xoa = nk ? xs + xo_base + arow * po + 16 * kg : xa;  // never read unmasked when nk == 0
+  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  v4f fo = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb0 = 0; kb0 < S; kb0 += kD16) {
+#pragma unroll
+    for (int u = 0; u < kD16; ++u) {
+      const int j = kb0 + u;
+      const uint4 wq = rb[u];
+      const uint32_t l4 = j < nsteps ? 0xFFFFFFFFu : 0u;
+      const uint4 wa = *reinterpret_cast<const uint4 *>(xa + 64 * min(j, last));
+      const v4i a0 = XU ? widen_unsigned(wa.x & l4, wa.y & l4) : widen_signed(wa.x & l4, wa.y & l4);
+      const v4i a1 = XU ? widen_unsigned(wa.z & l4, wa.w & l4) : widen_signed(wa.z & l4, wa.w & l4);
+      const v4i b0 = widen_signed(wq.x, wq.y), b1 = widen_signed(wq.z, wq.w);
+      v8h ao, bo;
+      if (MODE == 2) {
+        const uint32_t lo = (j >= nsteps && j < S) ? 0xFFFFFFFFu : 0u;
+        const uint4 xv = *reinterpret_cast<const uint4 *>(xoa + 64 * max(min(j - nsteps, nk - 1), 0));
+        const uint4 am = {xv.x & lo, xv.y & lo, xv.z & lo, xv.w & lo};
+        const uint4 bm = {wq.x & lo, wq.y & lo, wq.z & lo, wq.w & lo};
+        __builtin_memcpy(&ao, &am, 16);
+        __builtin_memcpy(&bo, &bm, 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      rb[u] = *reinterpret_cast<const uint4 *>(src(min(j + kD16, S - 1)));
+      acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc1, 0, 0, 0);
+      if (MODE == 2) fo = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, fo, 0, 0, 0);
+    }
+  }
+
+  // Epilogue: register r of lane (l16, kg) is token 4kg + r, channel n0 + l16.
+  constexpr int kShift = XU ? 4 : 8;
+  const int64_t gn = n0 + l16;
+  if (MODE == 0) {
+    int32_t *out = reinterpret_cast<int32_t *>(p.out);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gm = 4 * kg + r;
+      if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = (acc0[r] + acc1[r]) >> kShift;
+    }
+    return;
+  }
+  const int64_t gnc = min(gn, p.N - 1);
+  const float swn = p.sw[gnc];
+  const int32_t rsn = (MODE == 2 && p.zx) ? p.rowsum[gnc] : 0;
+  __half *out = reinterpret_cast<__half *>(p.out);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t gm = 4 * kg + r;
+    const int64_t gmc = min(gm, p.T - 1);
+    int32_t v = (acc0[r] + acc1[r]) >> kShift;
+    if (MODE == 2 && p.zx) v -= p.zx[gmc] * rsn;
+    const float y = (float)v * p.sx[gmc] * swn + fo[r];
+    if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(y);
+  }
+}
+
 bool gemm_decode_fits(const GemmArgs &p) { return p.T <= 32 && p.Kb % 64 == 0 && p.Kb >= 64; }
 
 hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  const int64_t n_out = mode == 2 ? p.n_out : 0;
+  if (d16_fits(p.T, p.Kb, n_out)) {
+    const size_t lds = d16_lds(p.T, p.Kb, n_out);
+    const dim3 grid((unsigned)((p.N + 63) / 64)), block(256);
+    void (*k)(GemmArgs) = mode == 0 ? (x_unsigned ? gemm_decode16<true, 0> : gemm_decode16<false, 0>)
+                          : mode == 1 ? gemm_decode16<false, 1>
+                                      : (x_unsigned ? gemm_decode16<true, 2> : gemm_decode16<false, 2>);
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    k<<<grid, block, lds, st>>>(p);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((p.N + 127) / 128)), block(256);
   if (mode == 0) {
     if (x_unsigned) gemm_decode<true, 0><<<grid, block, 0, st>>>(p);

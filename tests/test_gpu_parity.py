@@ -169,12 +169,16 @@ def test_prepare_weights_matches_oracle(case):
 
 # ----------------------------------------------------------------------------- GEMM
 
-# T <= 32 runs the decode kernel (K split over four wavefronts, a ragged
-# split when K/128 is not a multiple of 4), T >= 256 the register-A kernel,
-# the rest and K % 128 != 0 the LDS-tile kernel.
+# With K % 128 == 0: T <= 16 runs the 16-channel decode kernel when the
+# activation rows fit its 64 KB LDS stage (T * K / 2 bytes; (16, 100, 8192)
+# fills it exactly, (16, 70, 8320) overflows it), otherwise and for T <= 32
+# the 32-channel decode kernel; T >= 256 the register-A kernel; the rest and
+# K % 128 != 0 the LDS-tile kernel.  N % 64 != 0 leaves idle wavefronts in
+# the last decode workgroup.
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
                (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
-               (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384)]
+               (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
+               (16, 100, 8192), (16, 70, 8320), (9, 65, 4608)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -189,7 +193,8 @@ def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
     assert np.array_equal(host(acc), o.int_gemm(qx, qw))
 
 
-@pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032)])
+@pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032),
+                                   (7, 190, 3968)])
 def test_linear_epilogue_on_oracle_codes(T, N, K):
     note(f"[w4a4_linear] T={T} N={N} K={K}")
     rng = np.random.default_rng(K + T)
@@ -202,7 +207,9 @@ def test_linear_epilogue_on_oracle_codes(T, N, K):
 
 @pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False),
                                             (300, 150, 256, True), (260, 70, 32, False),
-                                            (8, 300, 256, True), (32, 64, 96, True), (1, 40, 32, False)])
+                                            (8, 300, 256, True), (32, 64, 96, True), (1, 40, 32, False),
+                                            (15, 64, 96, True), (12, 130, 64, False), (5, 77, 0, True),
+                                            (16, 200, 256, True)])
 def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     note(f"[mixed_linear] T={T} N={N} n_out={n_out} asym={asym}")
     K = 7936
