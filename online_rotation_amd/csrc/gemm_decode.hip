@@ -4,16 +4,19 @@
 // product, round once), for T <= 32 on gfx950.
 //
 // At decode sizes the work is streaming the weight matrix once: 2TNK ops
-// against N*K/2 bytes, far below the MFMA ridge.  So the design serves HBM:
-//   - each wavefront owns 32 output channels (one 32x32 MFMA block column)
-//     and streams their weight rows from start to end, one sequential stream
-//     per row (splitting K across wavefronts gave every row several
-//     concurrent streams and measured 25% slower);
-//   - both operands go global -> registers -> widened int8 -> MFMA, with a
-//     kDcD-step register ring (the activation rows are a few KB, L2-resident;
-//     rows past T are clamped onto row T-1 and their outputs dropped);
-//   - the FP16 outlier fragments are all loaded before the ring's prologue,
-//     so their latency hides behind the first weight loads.
+// against N*K/2 bytes, far below the MFMA ridge.  So both kernels serve HBM:
+// each wavefront owns a block of output channels and streams their weight
+// rows from start to end, one sequential stream per row (splitting K across
+// wavefronts gave every row several concurrent streams and measured 25%
+// slower), through a register ring of k-steps.
+//   gemm_decode16 (T <= 16, activation stage <= 64 KB): 16 channels per
+//     wavefront, the activation rows staged in LDS, FP16 outlier columns as
+//     extra ring steps.
+//   gemm_decode (the rest): 32 channels per wavefront, activation fragments
+//     read from L2 next to the weights, outlier fragments loaded before the
+//     ring's prologue.
+#include <algorithm>
+
 #include "gemm_common.h"
 #include "rq_kernels.h"
 
@@ -155,8 +158,7 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs p) {
 // the zero products leave both accumulators (and their summation order)
 // exactly as a loop over the live steps alone would.
 namespace {
-constexpr int kD16 = 8;          // load ring depth (k-steps)
-constexpr int kD16Chunks = 16;   // staged 16-byte chunks per thread (64 KB per workgroup)
+constexpr int kD16 = 8;  // load ring depth (k-steps)
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // staged row pitches: 16 bytes of padding put the 16 rows a load
 // instruction reads on 16 distinct 16-byte LDS bank groups
@@ -164,22 +166,25 @@ __host__ __device__ inline uint32_t d16_pitch(int64_t bytes) { return (uint32_t)
 __host__ __device__ inline size_t d16_lds(int64_t T, int64_t Kb, int64_t n_out) {
   return (size_t)T * d16_pitch(Kb) + (n_out ? (size_t)T * d16_pitch(2 * n_out) : 0);
 }
-// the staged bytes fit the per-thread chunk budget
+// staged 16-byte chunks
+inline int64_t d16_chunks(int64_t T, int64_t Kb, int64_t n_out) { return T * (Kb / 16 + n_out / 8); }
+// the stage fits 64 KB of LDS, which four wavefronts load in two groups
 inline bool d16_fits(int64_t T, int64_t Kb, int64_t n_out) {
-  return T <= 16 && T * (Kb / 16 + n_out / 8) <= 256 * kD16Chunks;
+  return T <= 16 && d16_chunks(T, Kb, n_out) <= 4096;
 }
 // floor(c / d) = umulhi(c, m) with m = ceil(2^32 / d) = floor((2^32 - 1) / d) + 1
 // (d >= 2): exact while c * d < 2^32
 __device__ inline uint32_t d16_magic(uint32_t d) { return 0xFFFFFFFFu / d + 1; }
 }  // namespace
 
-template <bool XU, int MODE>
-__global__ __launch_bounds__(256) void gemm_decode16(GemmArgs p) {
+template <bool XU, int MODE, int G>
+__global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p) {
   extern __shared__ __align__(16) uint8_t xs[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, l16 = lane & 15;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 16, Kb = p.Kb;
+  const uint32_t nthr = blockDim.x;
+  const int64_t n0 = ((int64_t)blockIdx.x * (nthr >> 6) + wave) * 16, Kb = p.Kb;
   const int nsteps = (int)(Kb >> 6), last = nsteps - 1;
   const int nk = MODE == 2 ? p.n_out / 32 : 0;  // outlier steps
   const int S = nsteps + nk;
@@ -196,23 +201,24 @@ __global__ __launch_bounds__(256) void gemm_decode16(GemmArgs p) {
   };
 
   // Staging: 16-byte chunks c < na are activation codes (row c / ka), the
-  // next no are x_out halves (row (c - na) / ko); kD16Chunks per thread.
+  // next no are x_out halves (row (c - na) / ko); 8G per thread.
   const uint32_t ka = (uint32_t)(Kb >> 4), ko = (uint32_t)p.n_out >> 3;
   const uint32_t na = T * ka, no = nk ? T * ko : 0;
   const uint8_t *xo = reinterpret_cast<const uint8_t *>(p.xo);
-  // Two groups of 8 loads in registers; a lane past the end reloads the
-  // last chunk (one shared line per instruction).
+  // G groups of 8 loads in registers (G fixed at launch: a branch here makes
+  // the compiler wait for every load at its join); a lane past the end
+  // reloads the last chunk (one shared line per instruction).
   const uint32_t nt = na + no;
-  v4u s0[kD16Chunks / 2], s1[kD16Chunks / 2];
-  auto sload = [&](v4u (&v)[kD16Chunks / 2], int h) {
+  v4u s0[8], s1[8];
+  auto sload = [&](v4u (&v)[8], int h) {
 #pragma unroll
-    for (int i = 0; i < kD16Chunks / 2; ++i) {
-      const uint32_t c = min(256 * (8 * h + i) + tid, nt - 1);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = min(nthr * (8 * h + i) + tid, nt - 1);
       v[i] = *reinterpret_cast<const v4u *>(c < na ? p.qx + 16 * (int64_t)c : xo + 16 * (int64_t)(c - na));
     }
   };
   sload(s0, 0);
-  sload(s1, 1);  // unconditional: a branch here makes the compiler wait for both groups at its join
+  if (G == 2) sload(s1, 1);
   // the weight ring's prologue goes out behind the staging loads, so waiting
   // for the latter below leaves it in flight
   __builtin_amdgcn_sched_barrier(0);
@@ -222,10 +228,10 @@ __global__ __launch_bounds__(256) void gemm_decode16(GemmArgs p) {
   __builtin_amdgcn_sched_barrier(0);
   {
     const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
-    auto sstore = [&](const v4u (&v)[kD16Chunks / 2], int h) {
+    auto sstore = [&](const v4u (&v)[8], int h) {
 #pragma unroll
-      for (int i = 0; i < kD16Chunks / 2; ++i) {
-        const uint32_t c = 256 * (8 * h + i) + tid;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t c = nthr * (8 * h + i) + tid;
         if (c < na) {
           const uint32_t r = __umulhi(c, ma);
           *reinterpret_cast<v4u *>(xs + r * pa + 16 * (c - r * ka)) = v[i];
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(256) void gemm_decode16(GemmArgs p) {
       }
     };
     sstore(s0, 0);
-    if (nt > 256 * kD16Chunks / 2) sstore(s1, 1);
+    if (G == 2) sstore(s1, 1);
   }
   __syncthreads();
   if (n0 >= p.N) return;  // whole wavefront past the last channel (after its share of the staging)
@@ -305,11 +311,24 @@ bool gemm_decode_fits(const GemmArgs &p) { return p.T <= 32 && p.Kb % 64 == 0 &&
 hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
   const int64_t n_out = mode == 2 ? p.n_out : 0;
   if (d16_fits(p.T, p.Kb, n_out)) {
+    // w wavefronts (16 channels each) per workgroup, sized so that the
+    // channel blocks spread evenly over the 256 CUs: N = 28672 takes 256
+    // workgroups of 7 (448 of 4 left 64 CUs with half the work of the rest
+    // and measured 11% slower); at least 4, at most 8
+    const int64_t rb = (p.N + 15) / 16;
+    const int w = (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
+    const dim3 grid((unsigned)((rb + w - 1) / w)), block(64 * w);
+    const bool g2 = d16_chunks(p.T, p.Kb, n_out) > 8 * 64 * w;
     const size_t lds = d16_lds(p.T, p.Kb, n_out);
-    const dim3 grid((unsigned)((p.N + 63) / 64)), block(256);
-    void (*k)(GemmArgs) = mode == 0 ? (x_unsigned ? gemm_decode16<true, 0> : gemm_decode16<false, 0>)
-                          : mode == 1 ? gemm_decode16<false, 1>
-                                      : (x_unsigned ? gemm_decode16<true, 2> : gemm_decode16<false, 2>);
+    void (*k)(GemmArgs);
+    if (g2)
+      k = mode == 0   ? (x_unsigned ? gemm_decode16<true, 0, 2> : gemm_decode16<false, 0, 2>)
+          : mode == 1 ? gemm_decode16<false, 1, 2>
+                      : (x_unsigned ? gemm_decode16<true, 2, 2> : gemm_decode16<false, 2, 2>);
+    else
+      k = mode == 0   ? (x_unsigned ? gemm_decode16<true, 0, 1> : gemm_decode16<false, 0, 1>)
+          : mode == 1 ? gemm_decode16<false, 1, 1>
+                      : (x_unsigned ? gemm_decode16<true, 2, 1> : gemm_decode16<false, 2, 1>);
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -173,12 +173,13 @@ def test_prepare_weights_matches_oracle(case):
 # activation rows fit its 64 KB LDS stage (T * K / 2 bytes; (16, 100, 8192)
 # fills it exactly, (16, 70, 8320) overflows it), otherwise and for T <= 32
 # the 32-channel decode kernel; T >= 256 the register-A kernel; the rest and
-# K % 128 != 0 the LDS-tile kernel.  N % 64 != 0 leaves idle wavefronts in
-# the last decode workgroup.
+# K % 128 != 0 the LDS-tile kernel.  Ragged N leaves idle wavefronts in the
+# last decode workgroup; N > 16384 gives it more than 4 wavefronts (5 here,
+# with the stage loaded in one group of 8 chunks per thread, then in two).
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
                (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
                (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
-               (16, 100, 8192), (16, 70, 8320), (9, 65, 4608)]
+               (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
