@@ -177,7 +177,10 @@ __global__ __launch_bounds__(256) void fwht4096_quant(const __half *__restrict__
 //     per-row power of two chosen from the exponent of max|x| (exact), which
 //     puts the largest intermediate just below 2^15; the quantizer divides
 //     it out again (exact).
-// Constant operands come from compile-time sign tables (16 bytes per lane).
+// Constant operands come from compile-time sign tables (16 bytes per lane),
+// staged in LDS once per workgroup.  Up to 2048 tokens, one wavefront per
+// token; beyond, each wavefront takes an even number of tokens and loads the
+// next one while it computes the current one.
 // Output layout (both cases): accumulator [mb][nb] register r of lane
 // (r32, g) holds element 64*(r32 + 32*nb) + 32*mb + 8*(r/4) + 4*g + r%4,
 // so four consecutive elements share a lane and a lane pair (l, l+32)
@@ -277,16 +280,16 @@ __device__ __forceinline__ v16f mfma16(uint4 a, uint4 b, v16f c) {
 }
 
 // Split eight fp32 values into fp16 hi (nearest) and lo (remainder) operands.
+// (the pair conversion is one v_cvt_pk_f16_f32, round to nearest even)
 __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
   uint32_t h[4], l[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const _Float16 a = (_Float16)f[2 * j], b = (_Float16)f[2 * j + 1];
-    const float ra = f[2 * j] - (float)a, rb = f[2 * j + 1] - (float)b;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    h[j] = (uint32_t)ua | ((uint32_t)ub << 16);
+    const h2 ab = __builtin_convertvector((f2){f[2 * j], f[2 * j + 1]}, h2);
+    const float ra = f[2 * j] - (float)ab.x, rb = f[2 * j + 1] - (float)ab.y;
+    __builtin_memcpy(&h[j], &ab, 4);
     auto pr = __builtin_amdgcn_cvt_pkrtz(ra, rb);
     __builtin_memcpy(&l[j], &pr, 4);
   }
@@ -311,154 +314,202 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
                                                      int64_t ldx, uint8_t *__restrict__ q,
                                                      float *__restrict__ scale,
                                                      int32_t *__restrict__ code_sum, float clip,
-                                                     int blog2, float norm) {
+                                                     int blog2, float norm, int tpw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= T) return;
   const int r32 = lane & 31, g = lane >> 5;
-  const __half *row = x + t * ldx;
+  const int64_t nw = (int64_t)gridDim.x * 4;  // wavefronts in the grid
+  const int64_t t0 = (int64_t)blockIdx.x * 4 + wave;
 
-  uint4 mop[2][4];  // M[a = r32 + 32*rb][b = 16*kc + 8*g + s], s = 0..7
+  // Constant operands, staged in LDS once per workgroup: read through
+  // lgkmcnt, waiting for them never waits for a token prefetch in flight.
+  __shared__ uint4 ltab[GSR ? 8 : 16][64];
+  {
+    const OpTab &t1 = GSR ? (blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8) : kHad1;
+    constexpr int nop = GSR ? 8 : 16;
+    uint4 v[nop / 4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int j = 0; j < nop / 4; ++j) {
+      const int e = j * 256 + threadIdx.x, op = e >> 6, l = e & 63;
+      v[j] = op < 8 ? tab_load(t1, op, l) : tab_load(kHad2, op - 8, l);
+    }
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      mop[rb][kc] = *reinterpret_cast<const uint4 *>(row + 64 * (r32 + 32 * rb) + 16 * kc + 8 * g);
+    for (int j = 0; j < nop / 4; ++j) {
+      const int e = j * 256 + threadIdx.x;
+      ltab[e >> 6][e & 63] = v[j];
+    }
+  }
+  __syncthreads();
+  if (t0 >= T) return;
 
-  v16f acc[2][2];
+  // M[a = r32 + 32*rb][b = 16*kc + 8*g + s], s = 0..7
+  auto load = [&](uint4 (&mop)[2][4], int64_t t) {
+    const __half *row = x + t * ldx;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  float nrm = norm;
+      for (int kc = 0; kc < 4; ++kc)
+        mop[rb][kc] = *reinterpret_cast<const uint4 *>(row + 64 * (r32 + 32 * rb) + 16 * kc + 8 * g);
+  };
 
-  if (GSR) {
-    // C[j][a] = sum_b G[b][j] M[a][b]: A = G^T (table), B = M (column a = lane).
-    const OpTab &tab = blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8;
+  // transform, scale, quantize and store token t
+  auto body = [&](const uint4 (&mop)[2][4], int64_t t) {
+    v16f acc[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint4 a = tab_load(tab, mb * 4 + kc, lane);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, mop[nb][kc], acc[mb][nb]);
-      }
-  } else {
-    // per-row scale 2^sx: step-1 operand magnitude 2^(te-15), te = min(38 - e, 30)
-    // with e the fp16 exponent field of max|x|, so |P * 2^sx| < 2^15.
-    uint32_t mx = 0;
-    {
-      u16x2 m2 = {0, 0};
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    float nrm = norm;
+
+    if (GSR) {
+      // C[j][a] = sum_b G[b][j] M[a][b]: A = G^T (table), B = M (column a = lane).
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-          const uint32_t d[4] = {mop[rb][kc].x, mop[rb][kc].y, mop[rb][kc].z, mop[rb][kc].w};
+          const uint4 a = ltab[mb * 4 + kc][lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u16x2 v;
-            const uint32_t dm = d[i] & 0x7FFF7FFFu;
-            __builtin_memcpy(&v, &dm, 4);
-            m2 = __builtin_elementwise_max(m2, v);
-          }
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, mop[nb][kc], acc[mb][nb]);
         }
-      mx = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
-    }
-    const int e = (int)((mx >> 10) & 0x1Fu);
-    const int te = min(38 - e, 30);
-    const uint32_t mag = (uint32_t)te << 10, magd = mag | (mag << 16);
-    nrm = __builtin_ldexpf(1.0f, 9 - te);  // undoes 2^(te - 9)
-    // step 1: P = M . H_64 * 2^(te-15), lanes <-> column b', registers <-> row a
-    v16f p[2][2];
+    } else {
+      // per-row scale 2^sx: step-1 operand magnitude 2^(te-15), te = min(38 - e, 30)
+      // with e the fp16 exponent field of max|x|, so |P * 2^sx| < 2^15.
+      uint32_t mx = 0;
+      {
+        u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+          for (int kc = 0; kc < 4; ++kc) {
+            const uint32_t d[4] = {mop[rb][kc].x, mop[rb][kc].y, mop[rb][kc].z, mop[rb][kc].w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[rb][cb][r] = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        uint4 hb = tab_load(kHad1, cb * 4 + kc, lane);
-        hb.x |= magd;
-        hb.y |= magd;
-        hb.z |= magd;
-        hb.w |= magd;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) p[rb][cb] = mfma16(mop[rb][kc], hb, p[rb][cb]);
-      }
-    }
-    // step 2: Y^T[b'][a'] = sum_a P[a][b'] H_64[a][a'] with A = P^T taken
-    // straight from the step-1 accumulators.
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float f[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) f[s] = p[rb][mb][8 * c + s];
-          uint4 hi, lo;
-          split8(f, hi, lo);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const uint4 hb = tab_load(kHad2, (nb * 2 + rb) * 2 + c, lane);
-            acc[mb][nb] = mfma16(hi, hb, acc[mb][nb]);
-            acc[mb][nb] = mfma16(lo, hb, acc[mb][nb]);
+            for (int i = 0; i < 4; ++i) {
+              u16x2 v;
+              const uint32_t dm = d[i] & 0x7FFF7FFFu;
+              __builtin_memcpy(&v, &dm, 4);
+              m2 = __builtin_elementwise_max(m2, v);
+            }
           }
+        mx = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+      }
+      const int e = (int)((mx >> 10) & 0x1Fu);
+      const int te = min(38 - e, 30);
+      const uint32_t mag = (uint32_t)te << 10, magd = mag | (mag << 16);
+      nrm = __builtin_ldexpf(1.0f, 9 - te);  // undoes 2^(te - 9)
+      // step 1: P = M . H_64 * 2^(te-15), lanes <-> column b', registers <-> row a
+      v16f p[2][2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[rb][cb][r] = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          uint4 hb = ltab[cb * 4 + kc][lane];
+          hb.x |= magd;
+          hb.y |= magd;
+          hb.z |= magd;
+          hb.w |= magd;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) p[rb][cb] = mfma16(mop[rb][kc], hb, p[rb][cb]);
         }
       }
-    }
-  }
-
-  // per-row symmetric scale from the normalized absmax
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][j][r]));
-  amax = wave_max(amax) * nrm;
-  float s, inv;
-  sym_scale(amax, clip, s, inv);
-  const float invn = inv * nrm;
-  const float lo_c = kMagic8 - 7.0f, hi_c = kMagic8 + 7.0f;
-  float csum = 0.0f;
-  uint8_t *qrow = q + t * 2048;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    uint32_t d[4];
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      uint32_t h[2];
+      // step 2: Y^T[b'][a'] = sum_a P[a][b'] H_64[a][a'] with A = P^T taken
+      // straight from the step-1 accumulators.
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        uint32_t bits[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float f = __builtin_fmaf(acc[mb][nb][4 * j4 + i], invn, kMagic8);
-          f = __builtin_amdgcn_fmed3f(f, lo_c, hi_c);
-          if (CSUM) csum += f - kMagic8;
-          __builtin_memcpy(&bits[i], &f, 4);
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float f[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) f[s] = p[rb][mb][8 * c + s];
+            uint4 hi, lo;
+            split8(f, hi, lo);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const uint4 hb = ltab[8 + (nb * 2 + rb) * 2 + c][lane];
+              acc[mb][nb] = mfma16(hi, hb, acc[mb][nb]);
+              acc[mb][nb] = mfma16(lo, hb, acc[mb][nb]);
+            }
+          }
         }
-        // low byte of bits[i] is code+8 in [1, 15]; pack pairs, then bytes
-        const uint32_t p01 = (bits[1] << 4) | bits[0];
-        const uint32_t p23 = (bits[3] << 4) | bits[2];
-        h[mb] = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);
       }
-      auto sw = __builtin_amdgcn_permlane32_swap(h[0], h[1], false, false);
-      d[j4] = ((uint32_t)sw[0] | ((uint32_t)sw[1] << 16)) ^ 0x88888888u;  // offset -> two's complement
     }
-    *reinterpret_cast<uint4 *>(qrow + 32 * (r32 + 32 * nb) + 16 * g) = make_uint4(d[0], d[1], d[2], d[3]);
+
+    // per-row symmetric scale from the normalized absmax
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][j][r]));
+    amax = wave_max(amax) * nrm;
+    float s, inv;
+    sym_scale(amax, clip, s, inv);
+    const float invn = inv * nrm;
+    const float lo_c = kMagic8 - 7.0f, hi_c = kMagic8 + 7.0f;
+    float csum = 0.0f;
+    uint8_t *qrow = q + t * 2048;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uint32_t d[4];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        uint32_t h[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          uint32_t bits[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float f = __builtin_fmaf(acc[mb][nb][4 * j4 + i], invn, kMagic8);
+            f = __builtin_amdgcn_fmed3f(f, lo_c, hi_c);
+            if (CSUM) csum += f - kMagic8;
+            __builtin_memcpy(&bits[i], &f, 4);
+          }
+          // low byte of bits[i] is code+8 in [1, 15]; pack pairs, then bytes
+          const uint32_t p01 = (bits[1] << 4) | bits[0];
+          const uint32_t p23 = (bits[3] << 4) | bits[2];
+          h[mb] = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);
+        }
+        auto sw = __builtin_amdgcn_permlane32_swap(h[0], h[1], false, false);
+        d[j4] = ((uint32_t)sw[0] | ((uint32_t)sw[1] << 16)) ^ 0x88888888u;  // offset -> two's complement
+      }
+      *reinterpret_cast<uint4 *>(qrow + 32 * (r32 + 32 * nb) + 16 * g) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+    if (CSUM) {
+      const int cs = wave_sum((int)csum);
+      if (lane == 0) code_sum[t] = cs;
+    }
+    if (lane == 0) scale[t] = s;
+  };
+
+  // Tokens t0 + i*nw for i < tpw, tpw being 1 or even.  With P even the next
+  // token's loads are in flight while the current one is computed; indices
+  // past the end are clamped onto the last row (same inputs, same outputs),
+  // so the loop holds no branch.
+  uint4 b0[2][4], b1[2][4];
+  load(b0, t0);
+  if (tpw == 1) {
+    body(b0, t0);
+    return;
   }
-  if (CSUM) {
-    const int cs = wave_sum((int)csum);
-    if (lane == 0) code_sum[t] = cs;
+  for (int i = 0; i < tpw; i += 2) {
+    const int64_t ta = min(t0 + i * nw, T - 1), tb = min(t0 + (i + 1) * nw, T - 1),
+                  tc = min(t0 + (i + 2) * nw, T - 1);
+    load(b1, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    body(b0, ta);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, tc);
+    __builtin_amdgcn_sched_barrier(0);
+    body(b1, tb);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (lane == 0) scale[t] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -998,16 +1049,21 @@ hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int 
   const int64_t blocks = (T + kF4096Waves - 1) / kF4096Waves;
   const bool had = !gsr && span_log2 == 12, gsr_mfma = gsr && span_log2 >= 3 && span_log2 <= 6;
   if (had || gsr_mfma) {
-    const dim3 grid((unsigned)blocks), block(256);
+    // up to 2048 tokens (two wavefronts per SIMD) one token per wavefront;
+    // beyond, at most 2048 wavefronts that take an even number of tokens
+    // each, the next one's loads in flight while the current one is computed
+    constexpr int64_t kMaxWaves = 2048;
+    const int tpw = T <= kMaxWaves ? 1 : 2 * (int)((T + 2 * kMaxWaves - 1) / (2 * kMaxWaves));
+    const dim3 grid((unsigned)(((T + tpw - 1) / tpw + 3) / 4)), block(256);
     const __half *xh = (const __half *)x;
     if (had && code_sum)
-      fwht4096_mfma<false, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f);
+      fwht4096_mfma<false, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f, tpw);
     else if (had)
-      fwht4096_mfma<false, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f);
+      fwht4096_mfma<false, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, 12, 1.0f, tpw);
     else if (code_sum)
-      fwht4096_mfma<true, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+      fwht4096_mfma<true, true><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm, tpw);
     else
-      fwht4096_mfma<true, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm);
+      fwht4096_mfma<true, false><<<grid, block, 0, st>>>(xh, T, ldx, q, scale, code_sum, clip, span_log2, norm, tpw);
     return hipGetLastError();
   }
   if (gsr)

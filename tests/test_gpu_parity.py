@@ -316,6 +316,26 @@ def test_full_size_sampled(case):
     check_y(host(y)[np.ix_(ts, ns)], yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw, qmax_x=7))
 
 
+@pytest.mark.parametrize("T", [2049, 5000])
+@pytest.mark.parametrize("kind,block,clip", [("hadamard", 0, 1.0), ("gsr", 64, 0.9)])
+def test_rotate_quant_several_tokens_per_wavefront(T, kind, block, clip):
+    """K = 4096 above 2048 tokens: each wavefront takes an even number of tokens,
+    prefetching the next; indices past the end are clamped onto the last row
+    (T = 2049 gives most wavefronts such a clamped second token)."""
+    note(f"[rotate_quant tpw>1] kind={kind} T={T}")
+    x0 = workloads.make_inputs("llama7b", with_weights=False)["x"]
+    reps = -(-T // x0.shape[0])
+    x = np.concatenate([x0 * np.float16(1.0 + 0.25 * r) for r in range(reps)])[:T]
+    rng = np.random.default_rng(T)
+    ts = np.unique(np.concatenate([[0, 1, 1020, 1027, 1028, 2047, 2048, T - 2, T - 1],
+                                   rng.choice(T, 40, replace=False)]))
+    ts = ts[ts < T]
+    xr = o.rotate_quant(x[ts], kind, clip=clip, **_rot_args(kind, block))
+    xq = rq.rq_rotate_quant(dev(x), _gpu_rot(kind, block), clip=clip)
+    torch.cuda.synchronize()
+    check_sym_quant(host(xq["q"])[ts], host(xq["scale"])[ts], xr)
+
+
 @pytest.mark.parametrize("wl", ["quik_prefill", "quik_decode"])
 def test_full_size_quik_sampled(wl):
     note(f"[full] {wl}")
