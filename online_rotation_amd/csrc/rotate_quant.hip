@@ -591,6 +591,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
   __shared__ uint32_t packed[NW * 4 + 1];  // packed codes of one row (+1 spill word)
   __shared__ float redf[8];
   __shared__ int redi[4];
+  extern __shared__ uint16_t ocol[];  // [n_out] outlier columns, ascending
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = K / 32;
   const int Kn = K - n_out;
@@ -633,30 +634,67 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     for (int i = 0; i < 16; ++i)
       keep[j][i] = (((m[j] >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) |
                    (((m[j] >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j)
+    if (!active[j])
+#pragma unroll
+      for (int i = 0; i < 16; ++i) keep[j][i] = 0u;
+  // the outlier columns in ascending order (rank = before + position in word)
+  const int nset = min(wsum[0] + wsum[1] + wsum[2] + wsum[3], n_out);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    uint32_t mo = m[j];
+    for (int r = before[j]; mo; ++r, mo &= mo - 1)
+      if (r < n_out) ocol[r] = (uint16_t)(32 * (tid * WPT + j) + __ffs(mo) - 1);
+  }
   const int nwords = (Kn + 7) / 8;  // packed row words
   for (int i = tid; i < NW * 4 + 1; i += kSplitThreads) packed[i] = 0u;
   __syncthreads();
 
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  // A row's 16-byte chunks; inactive words reload the thread's last active
+  // word (their keep masks are zero), so the loads hold no branch.
+  auto load_row = [&](uint4 (&u)[WPT][4], int64_t t) {
     const __half *row = x + t * ldx;
-    uint32_t d[WPT][16];
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
-      if (active[j]) {
-        const __half *src = row + 32 * (tid * WPT + j);
+      const __half *src = row + 32 * min(tid * WPT + j, nw - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * i);
-          d[j][4 * i] = u.x & keep[j][4 * i];
-          d[j][4 * i + 1] = u.y & keep[j][4 * i + 1];
-          d[j][4 * i + 2] = u.z & keep[j][4 * i + 2];
-          d[j][4 * i + 3] = u.w & keep[j][4 * i + 3];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) d[j][i] = 0u;
-      }
+      for (int i = 0; i < 4; ++i) u[j][i] = *reinterpret_cast<const uint4 *>(src + 8 * i);
     }
+  };
+  // outlier values per thread gathered ahead of the codes: columns ogc
+  // (past the list, or with none: column 0, loaded but not stored)
+  constexpr int kOg = 4;
+  int ogc[kOg];
+#pragma unroll
+  for (int k = 0; k < kOg; ++k) ogc[k] = nset > 0 ? ocol[min(tid + kSplitThreads * k, nset - 1)] : 0;
+  uint4 cur[WPT][4], nxt[WPT][4];
+  load_row(cur, blockIdx.x);
+
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const __half *row = x + t * ldx;
+    // this row's first kOg * 256 outlier values (L2-resident by now), issued
+    // before the next row's loads so that waiting for them leaves those in flight
+    unsigned short og[kOg];
+#pragma unroll
+    for (int k = 0; k < kOg; ++k) og[k] = reinterpret_cast<const unsigned short *>(row)[ogc[k]];
+    __builtin_amdgcn_sched_barrier(0);
+    // the next row; the last one reloads this row (L2-resident) rather than
+    // branch, since a conditional load makes the compiler wait for it below
+    const int64_t tn = t + gridDim.x;
+    load_row(nxt, tn < T ? tn : t);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t d[WPT][16];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = cur[j][i];
+        d[j][4 * i] = u.x & keep[j][4 * i];
+        d[j][4 * i + 1] = u.y & keep[j][4 * i + 1];
+        d[j][4 * i + 2] = u.z & keep[j][4 * i + 2];
+        d[j][4 * i + 3] = u.w & keep[j][4 * i + 3];
+      }
     // per-thread min / max (or absmax) on packed fp16, then the block reduction
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 mn2 = {0, 0}, mx2 = {0, 0};
@@ -708,25 +746,29 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     for (int j = 0; j < WPT; ++j) {
       if (!active[j]) continue;
       uint32_t w[4];
-      float fsum = 0.0f;
+      uint32_t nsum = 0;  // sum of the 32 nibbles (outliers, zeroed, included)
       auto code = [&](float f) {
         const float v = exact ? rne_quotient(f, s, inv) + base : __builtin_fmaf(f, inv, base);
-        return __builtin_amdgcn_fmed3f(v, lo_c, hi_c);
+        const float c = __builtin_amdgcn_fmed3f(v, lo_c, hi_c);
+        uint32_t b;
+        __builtin_memcpy(&b, &c, 4);
+        return b;  // low byte: the nibble (asymmetric code, or symmetric code + 8), high bits 0
       };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t wd = 0;
+        uint32_t b[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const __half2 h = *reinterpret_cast<const __half2 *>(&d[j][4 * i + k]);
           const float2 f = __half22float2(h);
-          const float q0 = code(f.x), q1 = code(f.y);
-          fsum += (q0 - base) + (q1 - base);
-          uint32_t b0, b1;
-          __builtin_memcpy(&b0, &q0, 4);
-          __builtin_memcpy(&b1, &q1, 4);
-          wd |= ((b0 & 0xFu) | ((b1 & 0xFu) << 4)) << (8 * k);
+          b[2 * k] = code(f.x);
+          b[2 * k + 1] = code(f.y);
         }
+        // low bytes of the even values -> e = [n0, n2, n4, n6], odd -> o; nibble k = value k
+        const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000C0Cu);
+        const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);
+        const uint32_t wd = (o << 4) | e;
+        nsum = __builtin_amdgcn_udot8(wd, 0x11111111u, nsum, false);
         w[i] = asym ? wd : (wd ^ 0x88888888u);  // symmetric: offset-8 nibble -> two's complement
       }
       // the run of this word's normal-column codes, outliers deleted
@@ -737,9 +779,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
         mm &= ~(1u << b);
       }
       const int cj = __popc(m[j]);
-      // fsum is the sum of (code - zero) over the word's 32 values; the
-      // zeroed outliers contribute exactly 0 to it
-      csum += (int)fsum + (asym ? zp * (32 - cj) : 0);
+      // the word's normal-column codes: a zeroed outlier's nibble is the
+      // zero point (asymmetric) or 8 (symmetric, code 0)
+      csum += asym ? (int)nsum - zp * cj : (int)nsum - 8 * 32;
       // place the run (32 - cj nibbles) at nibble position pos
       const int pos = 32 * (tid * WPT + j) - before[j];
       const int sh = (pos & 7) * 4, w0i = pos >> 3;
@@ -760,18 +802,6 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
 #pragma unroll
       for (int i = 0; i < 5; ++i)
         if (out[i]) atomicOr(&packed[w0i + i], out[i]);
-      // outlier columns keep their fp16 bits
-      if (n_out) {
-        uint32_t mo = m[j];
-        int r = before[j];
-        const unsigned short *rh = reinterpret_cast<const unsigned short *>(row) + 32 * (tid * WPT + j);
-        while (mo) {
-          const int b = __ffs(mo) - 1;
-          if (r < n_out) reinterpret_cast<unsigned short *>(x_out)[t * (int64_t)n_out + r] = rh[b];
-          ++r;
-          mo &= mo - 1;
-        }
-      }
     }
     if (code_sum) {
       csum = wave_sum(csum);
@@ -788,7 +818,20 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
       if (asym) zero[t] = zp;
       if (code_sum) code_sum[t] = redi[0] + redi[1] + redi[2] + redi[3];
     }
+    // outlier columns keep their fp16 bits
+    unsigned short *xo = reinterpret_cast<unsigned short *>(x_out) + t * (int64_t)n_out;
+#pragma unroll
+    for (int k = 0; k < kOg; ++k) {
+      const int r = tid + kSplitThreads * k;
+      if (r < nset) xo[r] = og[k];
+    }
+    for (int r = tid + kSplitThreads * kOg; r < nset; r += kSplitThreads)
+      xo[r] = reinterpret_cast<const unsigned short *>(row)[ocol[r]];
     packed[NW * 4] = 0u;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[j][i] = nxt[j][i];
     __syncthreads();
   }
 }
@@ -802,12 +845,16 @@ hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool a
   const __half *xh = (const __half *)x;
   __half *xo = (__half *)x_out;
   const int a = asym ? 1 : 0;
-  if (words <= kSplitThreads)
-    split_quant<1><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
-  else if (words <= 2 * kSplitThreads)
-    split_quant<2><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
-  else
-    split_quant<4><<<g, b, 0, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
+  const size_t lds = (size_t)n_out * sizeof(uint16_t);  // the outlier column list
+  void (*k)(const __half *, int64_t, int, int64_t, int, float, const int32_t *, int, uint8_t *, float *,
+            int32_t *, int32_t *, __half *) =
+      words <= kSplitThreads ? split_quant<1> : words <= 2 * kSplitThreads ? split_quant<2> : split_quant<4>;
+  if (lds > 32 * 1024) {  // beyond what the static arrays leave of the default 64 KB
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k<<<g, b, lds, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
   return hipGetLastError();
 }
 
