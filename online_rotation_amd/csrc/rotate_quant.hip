@@ -16,6 +16,7 @@
 //                    factor, for the weight side of the affine transform.
 #include "rq_device.h"
 #include "rq_kernels.h"
+#include "split_common.h"
 
 namespace rq {
 
@@ -305,9 +306,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// 1.5 * 2^23 + 8: fma(v, inv, kMagic8) = kMagic8 + rne(v*inv) for |v*inv| < 2^22,
-// so the low nibble of the result's bit pattern is the code + 8.
-constexpr float kMagic8 = 12582920.0f;
+// kMagic8 (split_common.h) = 1.5 * 2^23 + 8: fma(v, inv, kMagic8) = kMagic8 +
+// rne(v*inv) for |v*inv| < 2^22, so the low nibble of the result's bit
+// pattern is the code + 8.
 
 template <bool GSR, bool CSUM>
 __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ x, int64_t T,
@@ -526,58 +527,9 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
 // its compacted nibble offset; the packed row then goes out with coalesced
 // stores.
 //
-// Rounding matches rne(x / s) with s = fp32(S), S the exact real scale
-// (clip*amax/7 or (hi - lo)/15).  The inputs are fp16, so x / S lies either
-// exactly on a rounding boundary k + 1/2 or at least ~2^-15 (relative) away
-// from every boundary; the reciprocal of s (2^-24 off) only matters for the
-// exact ties, and there x / s falls on the side that the rounding of S to s
-// decides.  directed_inv moves the reciprocal by at most one ulp so that
-// x * inv lands on that same side.  When S == s the ties are real and go to
-// even; such rows take rne_quotient, which tests the boundary exactly.
+// Codes, rounding and the word-level compaction: split_common.h.
 // ---------------------------------------------------------------------------
 constexpr int kSplitThreads = 256;
-constexpr float kMagic0 = 12582912.0f;  // 1.5 * 2^23
-
-// Reciprocal of s nudged to the side of 1/s on which exact ties must land.
-// num / den = S; `exact` is set when s == S.
-__device__ __forceinline__ float directed_inv(float s, float inv, float num, float den, bool &exact) {
-  const float r = __builtin_fmaf(-den, s, num);   // S - s, sign exact
-  const float e = __builtin_fmaf(-s, inv, 1.0f);  // 1/s - inv, sign exact
-  exact = r == 0.0f;
-  uint32_t bits = __float_as_uint(inv);
-  if (r > 0.0f && e > 0.0f) ++bits;       // s < S: ties round away from zero, need inv >= 1/s
-  else if (r < 0.0f && e < 0.0f) --bits;  // s > S: ties round toward zero, need inv <= 1/s
-  return __uint_as_float(bits);
-}
-
-// rne(x / s) exactly, for s > 0: the candidate from x * inv, then the sign of
-// x - b s (exact in one fma) at the boundary b on that side.
-__device__ __forceinline__ float rne_quotient(float x, float s, float inv) {
-  const float t = x * inv;
-  const float c = __builtin_rintf(t);
-  const bool up = t > c;
-  const float b = up ? c + 0.5f : c - 0.5f;
-  const float d = __builtin_fmaf(-b, s, x);
-  if (d == 0.0f) return __builtin_rintf(b);
-  return up ? (d > 0.0f ? c + 1.0f : c) : (d < 0.0f ? c - 1.0f : c);
-}
-
-// delete nibble `b` (0..31) of the 128-bit value w (w[0] lowest), shifting the
-// higher nibbles down by one
-__device__ __forceinline__ void del_nibble(uint32_t *w, int b) {
-  const int wi = b >> 3, sh = (b & 7) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t hi_in = i < 3 ? (w[i + 1] << 28) : 0u;
-    const uint32_t shifted = (w[i] >> 4) | hi_in;
-    if (i > wi) {
-      w[i] = shifted;
-    } else if (i == wi) {
-      const uint32_t keep = sh ? ((1u << sh) - 1u) : 0u;
-      w[i] = (w[i] & keep) | (shifted & ~keep);
-    }
-  }
-}
 
 template <int WPT>
 __global__ __launch_bounds__(kSplitThreads) void split_quant(
@@ -696,18 +648,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
         d[j][4 * i + 3] = u.w & keep[j][4 * i + 3];
       }
     // per-thread min / max (or absmax) on packed fp16, then the block reduction
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 mn2 = {0, 0}, mx2 = {0, 0};
 #pragma unroll
-    for (int j = 0; j < WPT; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        f16x2 h;
-        __builtin_memcpy(&h, &d[j][i], 4);
-        if (!asym) h = __builtin_elementwise_abs(h);
-        mn2 = __builtin_elementwise_min(mn2, h);
-        mx2 = __builtin_elementwise_max(mx2, h);
-      }
+    for (int j = 0; j < WPT; ++j) word_minmax(d[j], asym, mn2, mx2);
     float mn = fminf((float)mn2.x, (float)mn2.y);
     float mx = fmaxf((float)mx2.x, (float)mx2.y);
     mn = wave_min(mn);
@@ -719,90 +662,11 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     __syncthreads();
     mn = fminf(fminf(redf[0], redf[1]), fminf(redf[2], redf[3]));
     mx = fmaxf(fmaxf(redf[4], redf[5]), fmaxf(redf[6], redf[7]));
-    float s, inv, base, lo_c, hi_c;
-    int zp = 0;
-    bool exact = false;
-    if (asym) {
-      const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
-      s = (hi - lo) / 15.0f;
-      inv = s > 0.0f ? 1.0f / s : 0.0f;
-      if (s > 0.0f) {
-        inv = directed_inv(s, inv, hi - lo, 15.0f, exact);
-        const float zf = exact ? rne_quotient(-lo, s, inv) : __builtin_fmaf(-lo, inv, kMagic0) - kMagic0;
-        zp = (int)__builtin_amdgcn_fmed3f(zf, 0.0f, 15.0f);
-      }
-      base = kMagic0 + (float)zp;      // code = clamp(rne(x/s) + zero, 0, 15)
-      lo_c = kMagic0;
-      hi_c = kMagic0 + 15.0f;
-    } else {
-      sym_scale(mx, clip, s, inv);
-      if (s > 0.0f) inv = directed_inv(s, inv, clip * mx, 7.0f, exact);
-      base = kMagic8;                  // low nibble = code + 8
-      lo_c = kMagic8 - 7.0f;
-      hi_c = kMagic8 + 7.0f;
-    }
+    const RowQuant rqp = row_quant(asym, clip, wave_uniform(mn), wave_uniform(mx));
     int csum = 0;
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      if (!active[j]) continue;
-      uint32_t w[4];
-      uint32_t nsum = 0;  // sum of the 32 nibbles (outliers, zeroed, included)
-      auto code = [&](float f) {
-        const float v = exact ? rne_quotient(f, s, inv) + base : __builtin_fmaf(f, inv, base);
-        const float c = __builtin_amdgcn_fmed3f(v, lo_c, hi_c);
-        uint32_t b;
-        __builtin_memcpy(&b, &c, 4);
-        return b;  // low byte: the nibble (asymmetric code, or symmetric code + 8), high bits 0
-      };
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t b[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const __half2 h = *reinterpret_cast<const __half2 *>(&d[j][4 * i + k]);
-          const float2 f = __half22float2(h);
-          b[2 * k] = code(f.x);
-          b[2 * k + 1] = code(f.y);
-        }
-        // low bytes of the even values -> e = [n0, n2, n4, n6], odd -> o; nibble k = value k
-        const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000C0Cu);
-        const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);
-        const uint32_t wd = (o << 4) | e;
-        nsum = __builtin_amdgcn_udot8(wd, 0x11111111u, nsum, false);
-        w[i] = asym ? wd : (wd ^ 0x88888888u);  // symmetric: offset-8 nibble -> two's complement
-      }
-      // the run of this word's normal-column codes, outliers deleted
-      uint32_t mm = m[j];
-      while (mm) {
-        const int b = 31 - __clz(mm);  // highest first, so lower positions stay put
-        del_nibble(w, b);
-        mm &= ~(1u << b);
-      }
-      const int cj = __popc(m[j]);
-      // the word's normal-column codes: a zeroed outlier's nibble is the
-      // zero point (asymmetric) or 8 (symmetric, code 0)
-      csum += asym ? (int)nsum - zp * cj : (int)nsum - 8 * 32;
-      // place the run (32 - cj nibbles) at nibble position pos
-      const int pos = 32 * (tid * WPT + j) - before[j];
-      const int sh = (pos & 7) * 4, w0i = pos >> 3;
-      const int nrun = 32 - cj;
-      if (nrun < 32) {  // clear the nibbles past the run
-        const int wi = nrun >> 3, bi = (nrun & 7) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i > wi) w[i] = 0u;
-          else if (i == wi) w[i] &= bi ? ((1u << bi) - 1u) : 0u;
-        }
-      }
-      uint32_t out[5];
-      out[0] = w[0] << sh;
-#pragma unroll
-      for (int i = 1; i < 4; ++i) out[i] = (w[i] << sh) | (sh ? (w[i - 1] >> (32 - sh)) : 0u);
-      out[4] = sh ? (w[3] >> (32 - sh)) : 0u;
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-        if (out[i]) atomicOr(&packed[w0i + i], out[i]);
-    }
+    for (int j = 0; j < WPT; ++j)
+      if (active[j]) csum += quant_word(d[j], m[j], 32 * (tid * WPT + j) - before[j], asym, rqp, packed);
     if (code_sum) {
       csum = wave_sum(csum);
       if (lane == 0) redi[wave] = csum;
@@ -814,8 +678,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
       packed[i] = 0u;
     }
     if (tid == 0) {
-      scale[t] = s;
-      if (asym) zero[t] = zp;
+      scale[t] = rqp.s;
+      if (asym) zero[t] = rqp.zp;
       if (code_sum) code_sum[t] = redi[0] + redi[1] + redi[2] + redi[3];
     }
     // outlier columns keep their fp16 bits
