@@ -163,6 +163,32 @@ rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int3
                                   int64_t N, const void *x_out, const void *w_out, int32_t n_out,
                                   void *y, int64_t ldy, void *stream);
 
+/* rq_quant_decode_linear -- rq_rotate_quant with rot NONE followed by the
+ * linear layer, in one launch, for decode batches: each workgroup quantizes
+ * the T activation rows into on-chip memory and streams its weight rows
+ * against them, so the activation codes, scales and x_out never reach HBM
+ * (operator fusion of the online step to cut memory traffic: FlatQuant
+ * article, section 1; SpinQuant OpenReview, latency discussion: fused tensor
+ * core kernels).  The codes are those of rq_rotate_quant, and y is that of
+ *   qd->asymmetric or qd->n_out > 0:
+ *     rq_mixed_outlier_linear(codes, scale, zero or NULL, ..., w_rowsum, x_out, w_out, n_out)
+ *   otherwise: rq_w4a4_linear(codes, scale, qw, sw),
+ * bit for bit when T * ((K - n_out)/32 + n_out/8) <= 4096 (then the two calls
+ * run the same decode kernel); beyond, the fp32 outlier product may differ in
+ * its summation order.
+ *   x        fp16 [T, ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned
+ *   qd       the quantizer of rq_rotate_quant (asymmetric, clip_ratio,
+ *            outlier_idx [n_out]); n_out % 32 == 0
+ *   qw, sw, w_rowsum (asymmetric only), w_out [N, n_out] (n_out > 0 only):
+ *            as written by rq_prepare_weights with the same outlier_idx
+ *   y        out fp16 [T, ldy], ldy >= N
+ * Shapes: 1 <= T <= 16 (T == 0 is a no-op), K % 32 == 0, K <= 8192,
+ * (K - n_out) % 128 == 0; otherwise RQ_ESHAPE (use the two calls). */
+rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ldx,
+                                 const rq_quant_desc *qd, const uint8_t *qw, const float *sw,
+                                 const int32_t *w_rowsum, int64_t N, const void *w_out,
+                                 void *y, int64_t ldy, void *stream);
+
 /* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
  * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
  * otherwise signed.  acc int32 [T, ldacc], ldacc >= N. */

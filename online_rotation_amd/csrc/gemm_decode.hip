@@ -19,6 +19,7 @@
 
 #include "gemm_common.h"
 #include "rq_kernels.h"
+#include "split_common.h"
 
 namespace rq {
 
@@ -177,9 +178,211 @@ inline bool d16_fits(int64_t T, int64_t Kb, int64_t n_out) {
 __device__ inline uint32_t d16_magic(uint32_t d) { return 0xFFFFFFFFu / d + 1; }
 }  // namespace
 
+// G = 1, 2: the activation codes (and x_out) are loaded in G groups of 8
+// 16-byte chunks per thread.  G = 0: the fused form -- the workgroup
+// quantizes the T unrotated fp16 rows of f.x itself (QUIK part 1, with the
+// outlier split; the arithmetic of split_common.h, so the codes are those of
+// the standalone quantizer) straight into its LDS code rows, one wavefront
+// per row, and gathers x_out beside them; the codes never reach HBM.
+// The fused staging step (G = 0).  A row of K <= 8192 columns is 4 quarters
+// of 64 words (32 columns each); lane l holds word 64q + l of quarter q, so a
+// load instruction covers 4 KB of a row.  The T x 4 (row, quarter) chunks
+// are dealt round-robin to the wavefronts.  Per workgroup: the outlier bit
+// mask, each word's compacted position, AND masks zeroing the outlier halves
+// (an LDS table, read per chunk) and the outlier columns in ascending order.
+// Pass 1 folds every chunk's min / max into its row (LDS atomics on the bit
+// patterns of non-negative floats); pass 2 reloads the chunks (from L2) and
+// quantizes them with the row's parameters.  `prologue` issues the weight
+// ring's first loads once the setup is done.  LDS: the code rows (pitch pa),
+// the x_out rows (pitch po, from xo_base), then the outlier column list.
+template <bool ASYM, typename Prologue>
+__device__ __forceinline__ void stage_fused(const GemmArgs &p, const FuseArgs &f, uint8_t *xs, uint32_t pa,
+                                            uint32_t po, uint32_t xo_base, uint32_t T, int nk, float *sxl,
+                                            int *zxl, Prologue prologue) {
+  __shared__ uint32_t omask[256];
+  __shared__ v4u keepl[16][64];   // [4 quarter + 16-byte chunk][lane]
+  __shared__ uint32_t rlo[16], rhi[16];  // per row: bits of -min(min x, 0) and max(max x, 0) (or max |x|)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t nthr = blockDim.x, nwaves = nthr >> 6;
+  const int K = f.K, nw = K >> 5, n_out = p.n_out;
+  uint16_t *ocol = reinterpret_cast<uint16_t *>(xs + xo_base + (nk ? T * po : 0));
+
+  // chunk c = 4t + q: row t, quarter q of 64 words; quarters past the row are skipped
+  const uint32_t nq = (uint32_t)(nw + 63) >> 6, nch = T * nq;
+  constexpr int kB = 4;  // chunks per batch
+  uint32_t d0[kB][16];   // the first batch, loaded before the setup (it needs none of it)
+  {
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t c = min(wave + b * nwaves, nch - 1), t = c / nq, q = c - t * nq;
+      const __half *src = f.x + t * f.ldx + 32 * min((int)(64 * q) + lane, nw - 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * k);
+        d0[b][4 * k] = u.x;
+        d0[b][4 * k + 1] = u.y;
+        d0[b][4 * k + 2] = u.z;
+        d0[b][4 * k + 3] = u.w;
+      }
+    }
+  }
+  // the first outlier indices of each thread, loaded beside the rows
+  const int oi0 = tid < n_out ? f.oidx[tid] : -1;
+  const v4u zero4 = {0u, 0u, 0u, 0u};
+  for (uint32_t i = tid; i < T * pa / 16; i += nthr) reinterpret_cast<v4u *>(xs)[i] = zero4;
+  for (int i = tid; i < 256; i += nthr) omask[i] = 0u;
+  if (tid < 16) rlo[tid] = rhi[tid] = 0u;
+  __syncthreads();
+  if (oi0 >= 0 && oi0 < K) atomicOr(&omask[oi0 >> 5], 1u << (oi0 & 31));
+  for (int j = tid + nthr; j < n_out; j += nthr) {
+    const int c = f.oidx[j];
+    if (c >= 0 && c < K) atomicOr(&omask[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  // word 64q + lane: its outlier bits m[q] and the outliers left of it
+  uint32_t m[4];
+  int before[4], base = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int w = 64 * q + lane;
+    m[q] = w < nw ? omask[w] : 0u;
+    const int cnt = __popc(m[q]);
+    const int incl = wave_scan_dpp(cnt);
+    before[q] = base + incl - cnt;
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  const int nset = min(base, n_out);
+  if (wave == 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t mo = m[q];
+      for (int r = before[q]; mo; ++r, mo &= mo - 1)
+        if (r < n_out) ocol[r] = (uint16_t)(32 * (64 * q + lane) + __ffs(mo) - 1);
+      // words past the row are zeroed whole
+      const uint32_t mk = 64 * q + lane < nw ? m[q] : 0xFFFFFFFFu;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        keepl[4 * q + c][lane] = v4u{keep_mask(mk, 4 * c), keep_mask(mk, 4 * c + 1), keep_mask(mk, 4 * c + 2),
+                                     keep_mask(mk, 4 * c + 3)};
+    }
+  __syncthreads();
+  prologue();
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto load_chunk = [&](uint32_t c, uint32_t (&d)[16]) {  // raw fp16 pairs of chunk c
+    const uint32_t t = c / nq, q = c - t * nq;
+    const __half *src = f.x + t * f.ldx + 32 * min((int)(64 * q) + lane, nw - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * k);
+      d[4 * k] = u.x;
+      d[4 * k + 1] = u.y;
+      d[4 * k + 2] = u.z;
+      d[4 * k + 3] = u.w;
+    }
+  };
+  auto mask_chunk = [&](uint32_t c, uint32_t (&d)[16]) {  // zero its outlier halves
+    const uint32_t q = c - (c / nq) * nq;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v4u km = keepl[4 * q + k][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * k + e] &= km[e];
+    }
+  };
+  // Chunks go four at a time, their loads issued together; past the end a
+  // batch repeats its wave's last chunk and skips its work.
+  // pass 1: the rows' min / max
+  for (uint32_t c0 = wave; c0 < nch; c0 += kB * nwaves) {
+    uint32_t d[kB][16];
+    if (c0 == (uint32_t)wave) {
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[b][e] = d0[b][e];
+    } else {
+#pragma unroll
+      for (int b = 0; b < kB; ++b) load_chunk(min(c0 + b * nwaves, nch - 1), d[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t c = c0 + b * nwaves;
+      if (c >= nch) break;
+      mask_chunk(c, d[b]);
+      f16x2 mn2 = {0, 0}, mx2 = {0, 0};
+      word_minmax(d[b], ASYM, mn2, mx2);
+      const float mn = wave_min_dpp(fminf((float)mn2.x, (float)mn2.y));
+      const float mx = wave_max_dpp(fmaxf((float)mx2.x, (float)mx2.y));
+      if (lane == 0) {
+        // both >= 0 (0 - v and v + 0 turn a -0 into +0): their bits order as the values
+        const uint32_t t = c / nq;
+        atomicMax(&rlo[t], __float_as_uint(0.0f - mn));
+        atomicMax(&rhi[t], __float_as_uint(mx + 0.0f));
+      }
+    }
+  }
+  __syncthreads();
+  // pass 2: codes (and the outlier values) with each row's parameters
+  for (uint32_t c0 = wave; c0 < nch; c0 += kB * nwaves) {
+    uint32_t d[kB][16];
+    unsigned short ov[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t c = min(c0 + b * nwaves, nch - 1), t = c / nq, q = c - t * nq;
+      if (c0 == (uint32_t)wave) {  // the first batch is still in registers
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[b][e] = d0[b][e];
+      } else {
+        load_chunk(c, d[b]);
+      }
+      // rank 64q + lane of this row's outliers, loaded beside the chunk
+      int oc = 0;  // past the list (or with none): column 0, loaded but not stored
+      if (nk && nset > 0) oc = ocol[min((int)(64 * q) + lane, nset - 1)];
+      ov[b] = reinterpret_cast<const unsigned short *>(f.x + t * f.ldx)[oc];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t c = c0 + b * nwaves;
+      if (c >= nch) break;
+      const uint32_t t = c / nq, q = c - t * nq;
+      mask_chunk(c, d[b]);
+      const float mn = -__uint_as_float(rlo[t]), mx = __uint_as_float(rhi[t]);
+      const RowQuant rq = row_quant(ASYM, f.clip, wave_uniform(mn), wave_uniform(mx));
+      if (64 * q + lane < nw) {
+        // q is uniform: m[q] and before[q] by selects, not an indexed load
+        uint32_t mq = m[0];
+        int bq = before[0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+          if (q == (uint32_t)k) {
+            mq = m[k];
+            bq = before[k];
+          }
+        quant_word(d[b], mq, 32 * (64 * q + lane) - bq, ASYM, rq, reinterpret_cast<uint32_t *>(xs + t * pa));
+      }
+      if (q == 0 && lane == 0) {
+        sxl[t] = rq.s;
+        zxl[t] = rq.zp;
+      }
+      if (nk) {
+        unsigned short *xrow = reinterpret_cast<unsigned short *>(xs + xo_base + t * po);
+        const int r = 64 * q + lane;
+        if (r < nset) xrow[r] = ov[b];
+        if (q == 0) {  // beyond the 64 nq ranks the quarters cover
+          const unsigned short *rowh = reinterpret_cast<const unsigned short *>(f.x + t * f.ldx);
+          for (int r2 = 64 * (int)nq + lane; r2 < nset; r2 += 64) xrow[r2] = rowh[ocol[r2]];
+        }
+      }
+    }
+  }
+}
+
 template <bool XU, int MODE, int G>
-__global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p) {
+__global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   extern __shared__ __align__(16) uint8_t xs[];
+  __shared__ float sxl[16];  // G = 0: the rows' scales and zero points
+  __shared__ int zxl[16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, l16 = lane & 15;
@@ -189,7 +392,9 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p) {
   const int nk = MODE == 2 ? p.n_out / 32 : 0;  // outlier steps
   const int S = nsteps + nk;
   const uint32_t T = (uint32_t)p.T;
-  const uint32_t pa = d16_pitch(Kb), po = d16_pitch(2 * (int64_t)p.n_out);
+  // G = 0 rows have room for all K codes, so that a list with repeated
+  // indices (fewer distinct outliers) cannot run a row into the next one
+  const uint32_t pa = d16_pitch(G == 0 ? (int64_t)f.K / 2 : Kb), po = d16_pitch(2 * (int64_t)p.n_out);
   const uint32_t xo_base = T * pa;
 
   // weight stream of this lane: INT4 row, then its outlier row
@@ -200,49 +405,56 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p) {
     return j < nsteps ? bp + 64 * (int64_t)j : wp + 64 * (int64_t)min(j - nsteps, nk - 1);
   };
 
-  // Staging: 16-byte chunks c < na are activation codes (row c / ka), the
-  // next no are x_out halves (row (c - na) / ko); 8G per thread.
-  const uint32_t ka = (uint32_t)(Kb >> 4), ko = (uint32_t)p.n_out >> 3;
-  const uint32_t na = T * ka, no = nk ? T * ko : 0;
-  const uint8_t *xo = reinterpret_cast<const uint8_t *>(p.xo);
-  // G groups of 8 loads in registers (G fixed at launch: a branch here makes
-  // the compiler wait for every load at its join); a lane past the end
-  // reloads the last chunk (one shared line per instruction).
-  const uint32_t nt = na + no;
-  v4u s0[8], s1[8];
-  auto sload = [&](v4u (&v)[8], int h) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = min(nthr * (8 * h + i) + tid, nt - 1);
-      v[i] = *reinterpret_cast<const v4u *>(c < na ? p.qx + 16 * (int64_t)c : xo + 16 * (int64_t)(c - na));
-    }
-  };
-  sload(s0, 0);
-  if (G == 2) sload(s1, 1);
-  // the weight ring's prologue goes out behind the staging loads, so waiting
-  // for the latter below leaves it in flight
-  __builtin_amdgcn_sched_barrier(0);
   uint4 rb[kD16];
+  if constexpr (G == 0) {
+    stage_fused<XU>(p, f, xs, pa, po, xo_base, T, nk, sxl, zxl, [&] {
 #pragma unroll
-  for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
-    auto sstore = [&](const v4u (&v)[8], int h) {
+      for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
+    });
+  } else {
+    // Staging: 16-byte chunks c < na are activation codes (row c / ka), the
+    // next no are x_out halves (row (c - na) / ko); 8G per thread.
+    const uint32_t ka = (uint32_t)(Kb >> 4), ko = (uint32_t)p.n_out >> 3;
+    const uint32_t na = T * ka, no = nk ? T * ko : 0;
+    const uint8_t *xo = reinterpret_cast<const uint8_t *>(p.xo);
+    // G groups of 8 loads in registers (G fixed at launch: a branch here makes
+    // the compiler wait for every load at its join); a lane past the end
+    // reloads the last chunk (one shared line per instruction).
+    const uint32_t nt = na + no;
+    v4u s0[8], s1[8];
+    auto sload = [&](v4u (&v)[8], int h) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t c = nthr * (8 * h + i) + tid;
-        if (c < na) {
-          const uint32_t r = __umulhi(c, ma);
-          *reinterpret_cast<v4u *>(xs + r * pa + 16 * (c - r * ka)) = v[i];
-        } else if (c < nt) {
-          const uint32_t c2 = c - na, r = __umulhi(c2, mo);
-          *reinterpret_cast<v4u *>(xs + xo_base + r * po + 16 * (c2 - r * ko)) = v[i];
-        }
+        const uint32_t c = min(nthr * (8 * h + i) + tid, nt - 1);
+        v[i] = *reinterpret_cast<const v4u *>(c < na ? p.qx + 16 * (int64_t)c : xo + 16 * (int64_t)(c - na));
       }
     };
-    sstore(s0, 0);
-    if (G == 2) sstore(s1, 1);
+    sload(s0, 0);
+    if (G == 2) sload(s1, 1);
+    // the weight ring's prologue goes out behind the staging loads, so waiting
+    // for the latter below leaves it in flight
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
+      auto sstore = [&](const v4u (&v)[8], int h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t c = nthr * (8 * h + i) + tid;
+          if (c < na) {
+            const uint32_t r = __umulhi(c, ma);
+            *reinterpret_cast<v4u *>(xs + r * pa + 16 * (c - r * ka)) = v[i];
+          } else if (c < nt) {
+            const uint32_t c2 = c - na, r = __umulhi(c2, mo);
+            *reinterpret_cast<v4u *>(xs + xo_base + r * po + 16 * (c2 - r * ko)) = v[i];
+          }
+        }
+      };
+      sstore(s0, 0);
+      if (G == 2) sstore(s1, 1);
+    }
   }
   __syncthreads();
   if (n0 >= p.N) return;  // whole wavefront past the last channel (after its share of the staging)
@@ -293,15 +505,16 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p) {
   }
   const int64_t gnc = min(gn, p.N - 1);
   const float swn = p.sw[gnc];
-  const int32_t rsn = (MODE == 2 && p.zx) ? p.rowsum[gnc] : 0;
+  const bool has_zx = G == 0 ? XU : p.zx != nullptr;
+  const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
   __half *out = reinterpret_cast<__half *>(p.out);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t gm = 4 * kg + r;
     const int64_t gmc = min(gm, p.T - 1);
     int32_t v = (acc0[r] + acc1[r]) >> kShift;
-    if (MODE == 2 && p.zx) v -= p.zx[gmc] * rsn;
-    const float y = (float)v * p.sx[gmc] * swn + fo[r];
+    if (MODE == 2 && has_zx) v -= (G == 0 ? zxl[gmc] : p.zx[gmc]) * rsn;
+    const float y = (float)v * (G == 0 ? sxl[gmc] : p.sx[gmc]) * swn + fo[r];
     if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(y);
   }
 }
@@ -320,7 +533,7 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
     const dim3 grid((unsigned)((rb + w - 1) / w)), block(64 * w);
     const bool g2 = d16_chunks(p.T, p.Kb, n_out) > 8 * 64 * w;
     const size_t lds = d16_lds(p.T, p.Kb, n_out);
-    void (*k)(GemmArgs);
+    void (*k)(GemmArgs, FuseArgs);
     if (g2)
       k = mode == 0   ? (x_unsigned ? gemm_decode16<true, 0, 2> : gemm_decode16<false, 0, 2>)
           : mode == 1 ? gemm_decode16<false, 1, 2>
@@ -334,7 +547,7 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    k<<<grid, block, lds, st>>>(p);
+    k<<<grid, block, lds, st>>>(p, FuseArgs{});
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((p.N + 127) / 128)), block(256);
@@ -347,6 +560,34 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
     if (x_unsigned) gemm_decode<true, 2><<<grid, block, 0, st>>>(p);
     else gemm_decode<false, 2><<<grid, block, 0, st>>>(p);
   }
+  return hipGetLastError();
+}
+
+// Fused decode: the kernel's LDS is the code rows (room for all K codes),
+// the x_out rows and the outlier column list.
+static size_t fused_lds(int64_t T, int64_t K, int64_t n_out) {
+  return (size_t)T * d16_pitch(K / 2) + (n_out ? (size_t)T * d16_pitch(2 * n_out) + 2 * (size_t)n_out : 0);
+}
+
+bool decode_fused_fits(const GemmArgs &p, const FuseArgs &f) {
+  return p.T >= 1 && p.T <= 16 && f.K % 32 == 0 && f.K <= 8192 && p.Kb % 64 == 0 && p.Kb >= 64 &&
+         2 * p.Kb + p.n_out == f.K && fused_lds(p.T, f.K, p.n_out) <= 96 * 1024;
+}
+
+hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f, bool asym, int mode, hipStream_t st) {
+  const int64_t rb = (p.N + 15) / 16;
+  const int w = (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
+  const dim3 grid((unsigned)((rb + w - 1) / w)), block(64 * w);
+  const size_t lds = fused_lds(p.T, f.K, mode == 2 ? p.n_out : 0);
+  void (*k)(GemmArgs, FuseArgs) = mode == 1 ? gemm_decode16<false, 1, 0>
+                                  : asym    ? gemm_decode16<true, 2, 0>
+                                            : gemm_decode16<false, 2, 0>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k<<<grid, block, lds, st>>>(p, f);
   return hipGetLastError();
 }
 

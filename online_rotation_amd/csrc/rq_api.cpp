@@ -214,6 +214,38 @@ rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int3
   return hip_status(rq::launch_gemm(p, zx != nullptr, 2, (hipStream_t)stream), "gemm launch");
 }
 
+rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_quant_desc *qd,
+                                 const uint8_t *qw, const float *sw, const int32_t *w_rowsum, int64_t N,
+                                 const void *w_out, void *y, int64_t ldy, void *stream) {
+  if (!qd) return fail(RQ_EINVAL, "the quantizer descriptor is required");
+  if (T < 0 || K <= 0 || N < 1) return fail(RQ_EINVAL, "need T >= 0, K > 0, N >= 1");
+  const int n_out = qd->n_out;
+  if (n_out < 0 || n_out >= K || n_out % 32) return fail(RQ_ESHAPE, "n_out=%d must be a multiple of 32 below K", n_out);
+  if (n_out > 0 && !qd->outlier_idx) return fail(RQ_EINVAL, "outlier_idx is NULL with n_out > 0");
+  if (!(qd->clip_ratio > 0.0f && qd->clip_ratio <= 1.0f)) return fail(RQ_EINVAL, "clip_ratio must be in (0, 1]");
+  if (qd->asymmetric && qd->clip_ratio != 1.0f) return fail(RQ_EINVAL, "asymmetric quantization takes clip_ratio 1");
+  if (T > 16) return fail(RQ_ESHAPE, "the fused decode form takes T <= 16 (T=%lld)", (long long)T);
+  if (K % 32 || K > 8192 || (K - n_out) % 128)
+    return fail(RQ_ESHAPE, "the fused decode form needs K %% 32 == 0, K <= 8192, (K - n_out) %% 128 == 0 (K=%lld)", (long long)K);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(RQ_EALIGN, "x is required, 16-byte aligned");
+  if (ldx < K || ldx % 8) return fail(RQ_EALIGN, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!qw || !aligned(qw, 16)) return fail(RQ_EALIGN, "qw is required, 16-byte aligned");
+  if (!sw || !aligned(sw, 4)) return fail(RQ_EINVAL, "sw is required (4-byte aligned)");
+  if (qd->asymmetric && (!w_rowsum || !aligned(w_rowsum, 4))) return fail(RQ_EINVAL, "asymmetric codes need w_rowsum (4-byte aligned)");
+  if (n_out > 0 && (!w_out || !aligned(w_out, 16))) return fail(RQ_EINVAL, "w_out is required (16-byte aligned) when n_out > 0");
+  if (n_out > 0 && !aligned(qd->outlier_idx, 4)) return fail(RQ_EALIGN, "outlier_idx must be 4-byte aligned");
+  if (!y || !aligned(y, 2)) return fail(RQ_EALIGN, "y is required, 2-byte aligned");
+  if (ldy < N) return fail(RQ_EALIGN, "leading dimension %lld must be >= N=%lld", (long long)ldy, (long long)N);
+  const bool asym = qd->asymmetric != 0;
+  const int mode = (asym || n_out > 0) ? 2 : 1;
+  rq::GemmArgs p{nullptr, qw, T, N, (K - n_out) / 2, nullptr, sw, nullptr, asym ? w_rowsum : nullptr,
+                 nullptr, (const __half *)w_out, n_out, y, ldy};
+  rq::FuseArgs f{(const __half *)x, ldx, (int)K, qd->clip_ratio, qd->outlier_idx};
+  if (!rq::decode_fused_fits(p, f)) return fail(RQ_ESHAPE, "T=%lld, K=%lld do not fit the fused decode form", (long long)T, (long long)K);
+  return hip_status(rq::launch_decode_fused(p, f, asym, mode, (hipStream_t)stream), "fused decode launch");
+}
+
 rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K, const uint8_t *qw,
                            int64_t N, int32_t *acc, int64_t ldacc, void *stream) {
   rq_status s = check_gemm(qx, T, K, qw, N, acc, ldacc, 4);

@@ -42,6 +42,53 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// Wave-wide max / min / inclusive prefix sum on the DPP paths (no LDS
+// crossbar round trips): quad and mirror permutations within rows of 16
+// lanes, then the row-15 and row-31 broadcasts (gfx9 encodings).  max and
+// min return the wave's value in a scalar register.
+#define RQ_DPP(old, v, ctrl, rows) __builtin_amdgcn_update_dpp((old), (v), (ctrl), (rows), 0xF, false)
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  int x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0xB1, 0xF)));   // quad_perm [1,0,3,2]
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0x4E, 0xF)));   // quad_perm [2,3,0,1]
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0x141, 0xF)));  // row_half_mirror
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0x140, 0xF)));  // row_mirror: every lane holds its row's max
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0x142, 0xA)));  // row_bcast:15 into rows 1, 3
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(RQ_DPP(x, x, 0x143, 0xC)));  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_min_dpp(float v) {
+  int x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0xB1, 0xF)));
+  x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0x4E, 0xF)));
+  x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0x141, 0xF)));
+  x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0x140, 0xF)));
+  x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0x142, 0xA)));
+  x = __float_as_int(v);
+  v = fminf(v, __int_as_float(RQ_DPP(x, x, 0x143, 0xC)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// inclusive prefix sum over the lanes; lanes without a source add 0
+__device__ __forceinline__ int wave_scan_dpp(int x) {
+  x += RQ_DPP(0, x, 0x111, 0xF);  // row_shr:1
+  x += RQ_DPP(0, x, 0x112, 0xF);  // row_shr:2
+  x += RQ_DPP(0, x, 0x114, 0xF);  // row_shr:4
+  x += RQ_DPP(0, x, 0x118, 0xF);  // row_shr:8: every lane holds its row prefix
+  x += RQ_DPP(0, x, 0x142, 0xA);  // row_bcast:15 into rows 1, 3
+  x += RQ_DPP(0, x, 0x143, 0xC);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+#undef RQ_DPP
+
 // Eight fp16 values (one 16-byte load) to fp32, exactly.
 __device__ __forceinline__ void h8_to_f32(uint4 raw, float *out) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};

@@ -24,6 +24,16 @@ struct GemmArgs {
   int64_t ldo;
 };
 
+// The fused decode form (quantizer + linear in one launch): the unrotated
+// fp16 rows and their quantizer.
+struct FuseArgs {
+  const __half *x;       // [T, ldx] fp16 rows
+  int64_t ldx;
+  int K;                 // columns of x (K - n_out = 2 * GemmArgs::Kb)
+  float clip;            // symmetric clip ratio (1 when asymmetric)
+  const int32_t *oidx;   // [n_out] outlier columns, or null when n_out == 0
+};
+
 hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int span_log2,
                            float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                            hipStream_t st);
@@ -45,6 +55,9 @@ hipError_t launch_kron_inverse_t(const float *p1, int n1, float *o1, const float
 // mode 0: raw int32 accumulator; 1: symmetric fp16 output; 2: mixed fp16 output
 bool gemm_decode_fits(const GemmArgs &p);
 hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
+// fused decode: p.qx, p.sx, p.zx and p.xo unused; the codes are made in the kernel
+bool decode_fused_fits(const GemmArgs &p, const FuseArgs &f);
+hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f, bool asym, int mode, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);

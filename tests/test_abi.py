@@ -120,6 +120,24 @@ def test_gemm_validation():
                                      256, FAKE, 16, None) == rq.RQ_EINVAL                    # outliers
 
 
+def test_quant_decode_linear_validation():
+    L = rq.lib()
+    f = L.rq_quant_decode_linear
+    qd, qa = _qd(), _qd(asym=1, idx=FAKE, n_out=256)
+    args = lambda T, K, qd, rowsum=FAKE, w_out=FAKE, ldy=16: (FAKE, T, K, K, ctypes.byref(qd), FAKE, FAKE, rowsum,
+                                                             16, w_out, FAKE, ldy, None)
+    assert f(*args(0, 4096, qd)) == rq.RQ_OK                       # T == 0
+    assert f(*args(17, 4096, qd)) == rq.RQ_ESHAPE                  # T > 16: the two calls
+    assert f(*args(8, 16384, qd)) == rq.RQ_ESHAPE                  # K > 8192
+    assert f(*args(8, 4160, qd)) == rq.RQ_ESHAPE                   # K % 128 with n_out = 0
+    assert f(*args(8, 8192, qa, rowsum=None)) == rq.RQ_EINVAL      # asymmetric without w_rowsum
+    assert f(*args(8, 8192, qa, w_out=None)) == rq.RQ_EINVAL       # outliers without w_out
+    assert f(*args(8, 8192, qa, ldy=12)) == rq.RQ_EALIGN           # ldy < N
+    assert f(*args(8, 8192, _qd(asym=1, idx=FAKE, n_out=100))) == rq.RQ_ESHAPE  # n_out % 32
+    assert f(*args(8, 8192, _qd(asym=1, clip=0.9))) == rq.RQ_EINVAL             # asymmetric clip
+    assert f(FAKE, 8, 4096, 4096, None, FAKE, FAKE, None, 16, None, FAKE, 16, None) == rq.RQ_EINVAL
+
+
 def test_prepare_weights_validation_and_workspace():
     L = rq.lib()
     kron = _rot("kron", n1=64, n2=64, p1=FAKE, p2=FAKE)

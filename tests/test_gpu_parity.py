@@ -231,6 +231,65 @@ def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     check_y(host(y), ref)
 
 
+# ----------------------------------------------------------------------------- fused decode
+
+# The fused decode form against the two calls it replaces, which here run the
+# same 16-channel decode kernel on staged codes: equal bit for bit.  Shapes:
+# the QUIK decode rows, T = 1 and the T = 16 maximum (at K = 8192 its LDS
+# exceeds 64 KB), asymmetric and symmetric, with and without outliers, a
+# clustered outlier run, small K, ragged N and N > 16384 (more than 4
+# wavefronts per workgroup).
+FUSED_CASES = [
+    # T, N, K, n_out, asym, pattern
+    (8, 300, 8192, 256, True, "workload"), (1, 64, 8192, 256, True, "workload"),
+    (16, 130, 8192, 0, True, "workload"), (16, 130, 4096, 256, True, "clustered"),
+    (5, 257, 4096, 0, True, "workload"),
+    (7, 100, 4096, 0, False, "workload"), (3, 70, 2048, 128, False, "clustered"),
+    (12, 16500, 1024, 128, True, "workload"), (16, 33, 128, 0, False, "workload"),
+]
+
+
+@pytest.mark.parametrize("T,N,K,n_out,asym,pattern", FUSED_CASES)
+def test_quant_decode_linear_equals_two_calls(T, N, K, n_out, asym, pattern):
+    note(f"[fused decode] T={T} N={N} K={K} n_out={n_out} asym={asym} {pattern}")
+    inp = workloads.make_inputs("quik_prefill", T=T, K=K, with_weights=False)
+    x = inp["x"]
+    idx = _outlier_pattern(inp, K, n_out, pattern) if n_out else None
+    w = (np.random.default_rng(N + K).standard_normal((N, K)) * 0.02).astype(np.float16)
+    xd, wd = dev(x), dev(w)
+    idxd = dev(idx) if n_out else None
+    wq = rq.rq_prepare_weights(wd, rq.Rotation("none"), outlier_idx=idxd)
+    xq = rq.rq_rotate_quant(xd, rq.Rotation("none"), asym=asym, outlier_idx=idxd)
+    if asym or n_out:
+        y2 = rq.rq_mixed_outlier_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"],
+                                        wq["rowsum"] if asym else None, xq["x_out"], wq["w_out"])
+    else:
+        y2 = rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"])
+    y1 = rq.rq_quant_decode_linear(xd, wq["q"], wq["scale"], wq["rowsum"] if asym else None,
+                                   wq["w_out"], asym=asym, outlier_idx=idxd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_quant_decode_linear_exact_ties():
+    """Rows with exact rounding ties take the exact-quotient path inside the
+    fused kernel too."""
+    note("[fused decode] exact ties")
+    sym, asy = _exact_tie_rows(K=1024)
+    w = (np.random.default_rng(3).standard_normal((96, 1024)) * 0.02).astype(np.float16)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"))
+    for rows, asym in ((sym[:16], False), (sym[16:], False), (asy[:8], True), (asy[8:], True)):
+        xd = dev(np.ascontiguousarray(rows))
+        xq = rq.rq_rotate_quant(xd, rq.Rotation("none"), asym=asym)
+        if asym:
+            y2 = rq.rq_mixed_outlier_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"], wq["rowsum"])
+        else:
+            y2 = rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"])
+        y1 = rq.rq_quant_decode_linear(xd, wq["q"], wq["scale"], wq["rowsum"] if asym else None, asym=asym)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+
+
 # ----------------------------------------------------------------------------- end to end
 
 E2E_CASES = [
@@ -356,6 +415,11 @@ def test_full_size_quik_sampled(wl):
     fx = check_asym_quant(host(xq["q"])[ts], host(xq["scale"])[ts], host(xq["zero"])[ts], xr)
     fw = check_sym_quant(host(wq["q"])[ns], host(wq["scale"])[ns], wr, what="w")
     check_y(host(y)[np.ix_(ts, ns)], yr, extra=flip_allowance(xr["scale"], wr["scale"], fx, fw))
+    if T <= 16:  # the fused decode form of the same step
+        yf = rq.rq_quant_decode_linear(dev(x), wq["q"], wq["scale"], wq["rowsum"], wq["w_out"],
+                                       asym=True, outlier_idx=dev(idx))
+        torch.cuda.synchronize()
+        assert torch.equal(yf, y)
 
 
 @pytest.mark.parametrize("T,N,K", [(2048, 4096, 4096), (4096, 28672, 7936)])
