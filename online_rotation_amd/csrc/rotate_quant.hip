@@ -298,11 +298,8 @@ __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo) {
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
-  return v;
-}
+// max over the wave of values below 2^24 (exact as floats)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return (uint32_t)wave_max((float)v); }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 

@@ -24,23 +24,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
-
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
 
 // Wave-wide max / min / inclusive prefix sum on the DPP paths (no LDS
 // crossbar round trips): quad and mirror permutations within rows of 16
@@ -88,6 +71,11 @@ __device__ __forceinline__ int wave_scan_dpp(int x) {
   return x;
 }
 #undef RQ_DPP
+
+// The wave's max / min / sum, in every lane (a scalar register).
+__device__ __forceinline__ float wave_max(float v) { return wave_max_dpp(v); }
+__device__ __forceinline__ float wave_min(float v) { return wave_min_dpp(v); }
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_scan_dpp(v), 63); }
 
 // Eight fp16 values (one 16-byte load) to fp32, exactly.
 __device__ __forceinline__ void h8_to_f32(uint4 raw, float *out) {
