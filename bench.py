@@ -55,8 +55,10 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_kernel(T, Kb):
+def gemm_kernel(T, Kb, n_out=0):
     """The GEMM kernel the library dispatches to (launch_gemm's rules)."""
+    if Kb % 64 == 0 and T <= 16 and T * (Kb // 16 + n_out // 8) <= 4096:
+        return "gemm_decode16"
     if Kb % 64 == 0 and T <= 32:
         return "gemm_decode"
     if Kb % 64 == 0 and T >= 256:
@@ -184,7 +186,7 @@ def main():
             step(i % sc)
         torch.cuda.synchronize()
         print(json.dumps({"counters": "done", "workload": wl.name, "calib_bytes": CALIB_BYTES,
-                          "gemm_kernel": gemm_kernel(T, Kq // 2), "quant_kernel": quant_kernel(wl)}),
+                          "gemm_kernel": gemm_kernel(T, Kq // 2, n_out), "quant_kernel": quant_kernel(wl)}),
               flush=True)
         return
 
@@ -253,8 +255,8 @@ def main():
     gemm_tops = ops / gemm_s / 1e12
     rq_gbs = rq_bytes / rot_s / 1e9
     gemm_bytes = w_bytes + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
-    gk, qk = gemm_kernel(T, Kq // 2), quant_kernel(wl)
-    decode = gk == "gemm_decode"
+    gk, qk = gemm_kernel(T, Kq // 2, n_out), quant_kernel(wl)
+    decode = gk.startswith("gemm_decode")
     traffic = prof.read_traffic(os.path.join(ROOT, "profiles", f"{gk}_{wl.name}_traffic.txt"), gk)
     if decode:
         roof = {"bound": "hbm", "achieved": round(gemm_bytes / gemm_s / 1e9, 1), "peak": HBM_PEAK_GBS,

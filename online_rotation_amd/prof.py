@@ -29,15 +29,18 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel name -> the sources it is built from (for the staleness hash)
+_DECODE = ["csrc/gemm_decode.hip", "csrc/gemm_common.h", "csrc/rq_device.h", "csrc/split_common.h"]
+_QUANT = ["csrc/rotate_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"]
 KERNEL_SOURCES = {
     "gemm_ra": ["csrc/gemm_ra.hip", "csrc/gemm_common.h", "csrc/rq_device.h"],
-    "gemm_decode": ["csrc/gemm_decode.hip", "csrc/gemm_common.h", "csrc/rq_device.h"],
+    "gemm_decode": _DECODE,
+    "gemm_decode16": _DECODE,
     "gemm_w4a4": ["csrc/gemm_w4a4.hip", "csrc/gemm_common.h", "csrc/rq_device.h"],
-    "fwht4096_mfma": ["csrc/rotate_quant.hip", "csrc/rq_device.h"],
-    "split_quant": ["csrc/rotate_quant.hip", "csrc/rq_device.h"],
-    "rowlds_quant": ["csrc/rotate_quant.hip", "csrc/rq_device.h"],
+    "fwht4096_mfma": _QUANT,
+    "split_quant": _QUANT,
+    "rowlds_quant": _QUANT,
     "kron64_mfma": ["csrc/kron.hip", "csrc/rq_device.h"],
-    "kron_quant": ["csrc/rotate_quant.hip", "csrc/rq_device.h"],
+    "kron_quant": _QUANT,
 }
 
 
