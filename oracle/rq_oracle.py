@@ -350,6 +350,32 @@ def rotate_quant(x16: np.ndarray, kind: str, clip: float = 1.0, asym: bool = Fal
     return out
 
 
+def kv_rotate_quant(x16: np.ndarray, group: int = 128, rotate: bool = True) -> dict:
+    """The KV-cache path: R3, then group-wise asymmetric INT4.
+
+    [SQR] second reviewer, A2: R3 rotates the KV cache before its
+    quantization, and (W_q R3)(W_k R3)^T = W_q W_k^T, so the rotation cancels
+    in the attention scores.  Reading: R3 is the normalized Walsh-Hadamard of
+    one head's `group` channels, applied to every head (blockdiag(H_group, ...)).
+    [FQ] section 3 (quantization setting, after QuaRot): the KV cache is
+    quantized group-wise asymmetric with groups of 128; each group takes the
+    asymmetric min-max form of reading c4 (quantize_asym, one scale and zero
+    point per group).  Codes are packed as in pack_int4.
+
+    Returns q [T, K] uint8, scale and zero [T, K/group], the fp64 rotated
+    values xr, pre-round values pre [T, K] and zpre [T, K/group], packed.
+    """
+    x = np.asarray(x16, np.float16).astype(np.float64)          # exact upcast
+    T, K = x.shape
+    assert K % group == 0
+    if rotate:
+        x = x @ block_diag(hadamard(group), K // group)
+    q, s, z, pre, zpre = quantize_asym(x.reshape(T * (K // group), group))
+    q = q.reshape(T, K)
+    return {"q": q, "scale": s.reshape(T, K // group), "zero": z.reshape(T, K // group), "xr": x,
+            "pre": pre.reshape(T, K), "zpre": zpre.reshape(T, K // group), "packed": pack_int4(q)}
+
+
 def prepare_weights(w16: np.ndarray, kind: str, clip: float = 1.0, outlier_idx=None,
                     block: int = 0, p1=None, p2=None, chan_scale=None) -> dict:
     """Offline weight side: W' = W . R^{-T}, then per-output-channel symmetric RTN.

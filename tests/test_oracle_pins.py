@@ -421,3 +421,102 @@ def test_affine_pipeline_small():
     assert np.all(np.abs(wq["q"] * sw - wr) <= sw / 2 * (1 + 1e-6))
     y = o.linear(xq, wq)["y"]
     np.testing.assert_array_equal(y, ((xq["q"] * sx) @ (wq["q"] * sw).T).astype(np.float16))
+
+
+# ----------------------------------------------------------------------------- KV-cache path (R3 + g128)
+
+def _sylvester(n):
+    """H_n by the recursion H_2n = [[H, H], [H, -H]] / sqrt(2), built with loops."""
+    h = [[1.0]]
+    while len(h) < n:
+        m = len(h)
+        h = [[h[i % m][j % m] * (-1.0 if (i >= m and j >= m) else 1.0) for j in range(2 * m)]
+             for i in range(2 * m)]
+    return [[v / math.sqrt(n) for v in row] for row in h]
+
+
+def test_kv_rotate_quant_matches_bruteforce_loops():
+    """Tiny case with every step written as plain loops: per group, rotate by
+    the recursively built Hadamard, then asymmetric min-max with a zero point."""
+    rng = np.random.default_rng(21)
+    T, K, g = 3, 16, 4
+    x = (rng.standard_normal((T, K)) * 2).astype(np.float16)
+    x[1, 4:8] = [0, 0, 0, 0]                       # an all-zero group: scale 0, zero 0, codes 0
+    h = _sylvester(g)
+    ref = o.kv_rotate_quant(x, group=g)
+    for t in range(T):
+        for gi in range(K // g):
+            xs = [float(x[t, gi * g + i]) for i in range(g)]
+            xr = [sum(xs[i] * h[i][j] for i in range(g)) for j in range(g)]
+            lo, hi = min(min(xr), 0.0), max(max(xr), 0.0)
+            s = float(np.float32((hi - lo) / 15))
+            z = int(min(max(round(-lo / s), 0), 15)) if s > 0 else 0
+            assert ref["scale"][t, gi] == np.float32(s) and ref["zero"][t, gi] == z
+            for j in range(g):
+                c = 0 if s == 0 else int(min(max(round(xr[j] / s) + z, 0), 15))   # round(): ties to even
+                pre = 0.0 if s == 0 else xr[j] / s
+                if abs(pre - math.floor(pre) - 0.5) > 1e-9:                         # away from ties
+                    assert ref["q"][t, gi * g + j] == c
+
+
+def test_kv_rotate_quant_one_hot_closed_form():
+    """x = c e_i inside group g: that group becomes c H_128[i, :] = +-a with
+    a = |c|/sqrt(128).  For i > 0 both signs occur: S = 2a/15 and s = fp32(S), so
+    -lo/s = a/s = 7.5 S/s.  Above 7.5 (s < S) or at 7.5 (ties to even): zero 8,
+    codes 15 / 0; below (s > S): zero 7, codes 14 / 0.  Row 0 of H is all +1
+    (c > 0): scale fp32(a/15), zero 0, codes 15.  Every other group is all zero
+    (scale 0, codes 0)."""
+    K, g = 512, 128
+    for i, gi, c in ((0, 0, 3.0), (77, 2, -1.5), (127, 3, 0.25)):
+        x = np.zeros((1, K), np.float16)
+        x[0, gi * g + i] = c
+        r = o.kv_rotate_quant(x, group=g)
+        signs = np.array([(-1.0) ** bin(i & j).count("1") for j in range(g)]) * np.sign(c)
+        a = abs(c) / math.sqrt(g)
+        S = (2 * a if i else a) / 15
+        sf = float(np.float32(S))
+        assert r["scale"][0, gi] == np.float32(S)
+        hi_code = 15 if (not i or sf <= S) else 14
+        np.testing.assert_array_equal(r["q"][0, gi * g:(gi + 1) * g], np.where(signs > 0, hi_code, 0))
+        assert r["zero"][0, gi] == ((8 if sf <= S else 7) if i else 0)
+        others = [k for k in range(K // g) if k != gi]
+        assert np.all(r["scale"][0, others] == 0) and np.all(r["q"][0, [k * g + j for k in others for j in range(g)]] == 0)
+
+
+def test_kv_rotate_quant_groups_are_independent_and_roundtrip():
+    """Changing one group changes only that group's outputs; dequantized values
+    rotated back (H is an involution) recover x within sqrt(g) * s / 2 per group."""
+    rng = np.random.default_rng(22)
+    T, K, g = 4, 1024, 128
+    x = (rng.standard_normal((T, K)) * 3).astype(np.float16)
+    r0 = o.kv_rotate_quant(x, group=g)
+    x2 = x.copy()
+    x2[2, 3 * g:4 * g] *= np.float16(-2)
+    r1 = o.kv_rotate_quant(x2, group=g)
+    diff = np.argwhere(r0["q"] != r1["q"])
+    assert diff.size and np.all(diff[:, 0] == 2) and np.all(diff[:, 1] // g == 3)
+    assert np.array_equal(np.argwhere(r0["scale"] != r1["scale"]), [[2, 3]])
+    h = o.hadamard(g)
+    for t in range(T):
+        for gi in range(K // g):
+            q = r0["q"][t, gi * g:(gi + 1) * g].astype(np.float64)
+            s, z = float(r0["scale"][t, gi]), int(r0["zero"][t, gi])
+            back = ((q - z) * s) @ h                   # H = H^T = H^{-1}
+            err = np.linalg.norm(back - x[t, gi * g:(gi + 1) * g].astype(np.float64))
+            assert err <= math.sqrt(g) * s / 2 * (1 + 1e-6)
+
+
+def test_kv_rotate_quant_without_rotation_is_groupwise_asymmetric():
+    """rotate=False: each group quantized on its own fp16 values; with a single
+    group per row it is the per-token asymmetric quantizer."""
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((5, 256)) * 2).astype(np.float16)
+    one = o.kv_rotate_quant(x, group=256, rotate=False)
+    ref = o.rotate_quant(x, "none", asym=True)
+    np.testing.assert_array_equal(one["q"], ref["q"])
+    np.testing.assert_array_equal(one["scale"][:, 0], ref["scale"])
+    np.testing.assert_array_equal(one["zero"][:, 0], ref["zero"])
+    two = o.kv_rotate_quant(x, group=128, rotate=False)
+    for gi in range(2):
+        part = o.rotate_quant(np.ascontiguousarray(x[:, gi * 128:(gi + 1) * 128]), "none", asym=True)
+        np.testing.assert_array_equal(two["q"][:, gi * 128:(gi + 1) * 128], part["q"])
