@@ -18,6 +18,11 @@ its bound: INT8 MFMA dense peak, or HBM at decode sizes (T <= 32);
 when one exists for this kernel, workload and kernel source, else null.
 `--counters` instead launches calibration kernels of known traffic and the
 two calls a few times, for `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` runs.
+
+`--workload kv` measures the KV-cache quantizer instead: one step quantizes
+one attention layer's keys (R3, a 128-point Walsh-Hadamard per head) and
+values, group-wise asymmetric INT4 with groups of 128 channels; the line
+reports GB/s, with the keys launch as the roofline kernel.
 """
 from __future__ import annotations
 
@@ -45,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode"])
+                    choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode", "kv"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled per step (0: >640 MB)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,6 +111,168 @@ def cpu_baseline(inp, wl, seconds):
                       f"rotate+quantize+INT GEMM+dequant, {runs} runs in {el:.1f} s; weight prep untimed"}
 
 
+KV_METRIC = "KV-cache quantizer GB/s (R3 on keys + group-wise asymmetric INT4 of keys and values), % HBM roofline"
+
+
+def kv_bytes(T, K, g):
+    """Algorithmic HBM bytes of one KV quantizer launch: fp16 in, packed codes,
+    fp32 scale and int32 zero point per group out."""
+    return T * K * 2 + T * K // 2 + T * (K // g) * 8
+
+
+def cpu_baseline_kv(inp, wl, seconds):
+    """The oracle on a bounded sample of the kv workload's tokens."""
+    from oracle import rq_oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ts = min(256, inp["x"].shape[0])
+    xs, vs = inp["x"][:ts], inp["v"][:ts]
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        o.kv_rotate_quant(xs, group=wl.block, rotate=True)
+        o.kv_rotate_quant(vs, group=wl.block, rotate=False)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    nbytes = 2 * kv_bytes(ts, wl.K, wl.block) * runs
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{ts} of {inp['x'].shape[0]} tokens of the kv workload (keys with R3, values without, "
+                      f"4096 channels, g={wl.block}), {runs} runs in {el:.1f} s"}
+
+
+def main_kv(args, torch, rq, prof, workloads):
+    """One step = the KV-cache quantization of one attention layer over the
+    batch: keys rotated by R3 (per-head Walsh-Hadamard) and values, each
+    quantized group-wise asymmetric INT4 (two rq_kv_rotate_quant calls)."""
+    dev = torch.device("cuda:0")
+    wl = workloads.get("kv")
+    inp = workloads.make_inputs("kv", with_weights=False)
+    T, K, g = wl.T, wl.K, wl.block
+    per = kv_bytes(T, K, g)
+    S = args.sets if args.sets > 0 else max(2, -(-(640 << 20) // (2 * per)))
+    ks = [torch.from_numpy(inp["x"]).to(dev) for _ in range(S)]
+    vs = [torch.from_numpy(inp["v"]).to(dev) for _ in range(S)]
+
+    def bufs():
+        return (torch.empty((T, K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((T, K // g), dtype=torch.float32, device=dev),
+                torch.empty((T, K // g), dtype=torch.int32, device=dev))
+    kq = [bufs() for _ in range(S)]
+    vq = [bufs() for _ in range(S)]
+
+    def keys(i):
+        rq.rq_kv_rotate_quant(ks[i], group=g, rotate=True, out=kq[i])
+
+    def values(i):
+        rq.rq_kv_rotate_quant(vs[i], group=g, rotate=False, out=vq[i])
+
+    def step(i):
+        keys(i)
+        values(i)
+
+    kernel = f"group_quant<{g // 4}, true>"
+    if args.counters:
+        calib = torch.empty(CALIB_BYTES // 8, dtype=torch.float64, device=dev)
+        for _ in range(3):
+            calib.fill_(1.0)
+        for _ in range(3):
+            calib.sum()
+        sc = min(S, 16)
+        for i in range(4 * sc):
+            step(i % sc)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters": "done", "workload": wl.name, "calib_bytes": CALIB_BYTES,
+                          "quant_kernel": kernel}), flush=True)
+        return
+
+    for i in range(max(args.warmup, S)):
+        step(i % S)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in kq[0] + vq[0]]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def capture(fn, count):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gr, stream=stream):
+                for j in range(count):
+                    fn(j % S)
+        torch.cuda.synchronize()
+        return gr
+
+    g_step = capture(step, args.steps)
+    reps_per_graph = max(S, 32)
+    g_keys = capture(keys, reps_per_graph)
+    g_vals = capture(values, reps_per_graph)
+    for _ in range(2):   # graph replays reproduce the eager result
+        for t in kq[0] + vq[0]:
+            t.zero_()
+        torch.cuda.synchronize()
+        g_step.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(kq[0] + vq[0], eager)), "graph replay differs from eager"
+
+    def timed(gr, launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = []
+        gr.replay()
+        torch.cuda.synchronize()
+        for _ in range(args.reps):
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                gr.replay()
+                e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) / 1e3 / launches)
+        return float(np.median(out))
+
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g_step.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    step_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    key_s = timed(g_keys, reps_per_graph)
+    val_s = timed(g_vals, reps_per_graph)
+    gbs = per / key_s / 1e9
+    traffic = prof.read_traffic(os.path.join(ROOT, "profiles", f"group_quant_{wl.name}_traffic.txt"), "group_quant")
+    rec = {
+        "metric": KV_METRIC,
+        "value": round(2 * per / step_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"kv: keys fp16 [{T},{K}] -> R3 ({g}-point Walsh-Hadamard per head) + "
+                               f"group-wise asymmetric INT4 (g={g}); values fp16 [{T},{K}] -> group-wise INT4",
+                   "T": T, "K": K, "group": g, "buffer_sets": S, "footprint_MB": round(S * 2 * per / 2**20)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                     "algorithmic_bytes_per_launch": per, "avg_launch_us": round(key_s * 1e6, 3)},
+        "values_launch": {"kernel": f"group_quant<{g // 4}, false>", "avg_launch_us": round(val_s * 1e6, 3),
+                          "achieved": round(per / val_s / 1e9, 1), "unit": "GB/s",
+                          "frac": round(per / val_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_kv(inp, wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +286,8 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "kv":
+        return main_kv(args, torch, rq, prof, workloads)
     dev = torch.device("cuda:0")
     wl = workloads.get(args.workload)
     inp = workloads.make_inputs(args.workload)

@@ -189,6 +189,32 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
                                  const int32_t *w_rowsum, int64_t N, const void *w_out,
                                  void *y, int64_t ldy, void *stream);
 
+/* rq_kv_rotate_quant -- the KV-cache quantizer: R3, a normalized
+ * Walsh-Hadamard transform over each head's `group` channels (SpinQuant
+ * OpenReview: the authors' answer on the number of rotation matrices, R3
+ * rotates the KV cache before its quantization; first reviewer Q2/A2, the
+ * rotation of queries and keys cancels in the attention product), then
+ * group-wise asymmetric INT4 with one scale and
+ * zero point per group (FlatQuant article, section 3: KV cache group-wise
+ * asymmetric, group size 128).  For token t and group j of channels
+ * [j*group, (j+1)*group):
+ *   v        = x[t, group j] . H_group / sqrt(group)   (rotate != 0; else x)
+ *   lo, hi   = min(min v, 0), max(max v, 0)
+ *   scale    = fp32((hi - lo) / 15),  zero = clamp(rne(-lo / scale), 0, 15)
+ *   code     = clamp(rne(v / scale) + zero, 0, 15);  v ~ (code - zero) * scale
+ * H_group is the Sylvester Hadamard matrix (natural order).  The transform
+ * runs in fp32 and is rounded once per value, so with rotate != 0 a code
+ * whose v / scale lies within fp32 rounding of a half-integer may differ by
+ * one from an exact evaluation; with rotate == 0 the result is exact.
+ *   x        fp16 [T, ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned
+ *   group    64, 128 or 256; K % group == 0, K <= 2^21
+ *   q        out uint8 [T, K/2] packed codes, 4-byte aligned
+ *   scale    out fp32 [T, K/group];  zero out int32 [T, K/group]
+ * T == 0 is a no-op. */
+rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
+                             int32_t rotate, uint8_t *q, float *scale, int32_t *zero,
+                             void *stream);
+
 /* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
  * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
  * otherwise signed.  acc int32 [T, ldacc], ldacc >= N. */

@@ -22,13 +22,13 @@ RQ_OK, RQ_EINVAL, RQ_ESHAPE, RQ_EALIGN, RQ_EHIP = range(5)
 ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
-           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_w4a4_gemm_i32",
-           "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
+           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
+           "rq_w4a4_gemm_i32", "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
-           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_w4a4_gemm_i32",
-           "rq_status_string", "rq_last_error", "rq_abi_version")
+           "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
+           "rq_w4a4_gemm_i32", "rq_status_string", "rq_last_error", "rq_abi_version")
 
 
 class RqError(RuntimeError):
@@ -72,8 +72,9 @@ def lib() -> ctypes.CDLL:
         L.rq_w4a4_gemm_i32.argtypes = [vp, i32, i64, i64, vp, i64, vp, i64, vp]
         L.rq_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), vp, vp,
                                              vp, i64, vp, vp, i64, vp]
-        for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear",
-                   "rq_mixed_outlier_linear", "rq_w4a4_gemm_i32", "rq_quant_decode_linear"):
+        L.rq_kv_rotate_quant.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+        for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear", "rq_mixed_outlier_linear",
+                   "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant"):
             getattr(L, fn).restype = ctypes.c_int
         L.rq_status_string.argtypes = [ctypes.c_int]
         L.rq_status_string.restype = ctypes.c_char_p
@@ -287,6 +288,31 @@ def rq_quant_decode_linear(x, qw, sw, w_rowsum=None, w_out=None, asym: bool = Fa
                                       _stream(x.device))
     _check(st, "rq_quant_decode_linear")
     return y
+
+
+def rq_kv_rotate_quant(x, group: int = 128, rotate: bool = True, out=None):
+    """KV-cache quantizer: per-group normalized Walsh-Hadamard (rotate) and
+    group-wise asymmetric INT4.  x fp16 [T, K] -> (q uint8 [T, K/2],
+    scale fp32 [T, K/group], zero int32 [T, K/group])."""
+    import torch
+    _gpu(x, *(out or ()))
+    T, K = x.shape
+    _want(x, "x", torch.float16, dense=False)
+    if out is None:
+        G = K // group if group > 0 else 0
+        out = (torch.empty((T, K // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((T, G), dtype=torch.float32, device=x.device),
+               torch.empty((T, G), dtype=torch.int32, device=x.device))
+    q, sc, zp = out
+    _want(q, "q", torch.uint8, (T, K // 2))
+    _want(sc, "scale", torch.float32)
+    _want(zp, "zero", torch.int32, tuple(sc.shape))
+    if K % group == 0 and tuple(sc.shape) != (T, K // group):
+        raise ValueError(f"rq: scale must have shape {(T, K // group)}")
+    st = lib().rq_kv_rotate_quant(_ptr(x), T, K, x.stride(0), int(group), 1 if rotate else 0,
+                                  _ptr(q), _ptr(sc), _ptr(zp), _stream(x.device))
+    _check(st, "rq_kv_rotate_quant")
+    return q, sc, zp
 
 
 def rq_w4a4_gemm_i32(qx, qw, x_unsigned: bool = False, out=None):

@@ -246,6 +246,23 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
   return hip_status(rq::launch_decode_fused(p, f, asym, mode, (hipStream_t)stream), "fused decode launch");
 }
 
+rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
+                             int32_t rotate, uint8_t *q, float *scale, int32_t *zero, void *stream) {
+  if (T < 0 || K <= 0) return fail(RQ_EINVAL, "need T >= 0, K > 0");
+  if (group != 64 && group != 128 && group != 256) return fail(RQ_ESHAPE, "group=%d must be 64, 128 or 256", group);
+  if (K % group) return fail(RQ_ESHAPE, "K=%lld must be a multiple of group=%d", (long long)K, group);
+  if (K > (int64_t(1) << 21)) return fail(RQ_ESHAPE, "K=%lld is above 2^21 channels", (long long)K);
+  if (T > (int64_t(1) << 40) / (K / group)) return fail(RQ_ESHAPE, "T=%lld is too large", (long long)T);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(RQ_EALIGN, "x is required, 16-byte aligned");
+  if (ldx < K || ldx % 8) return fail(RQ_EALIGN, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!q || !aligned(q, 4)) return fail(RQ_EALIGN, "q is required, 4-byte aligned");
+  if (!scale || !aligned(scale, 4)) return fail(RQ_EALIGN, "scale is required, 4-byte aligned");
+  if (!zero || !aligned(zero, 4)) return fail(RQ_EALIGN, "zero is required, 4-byte aligned");
+  return hip_status(rq::launch_group_quant(x, T, K, ldx, group, rotate != 0, q, scale, zero, (hipStream_t)stream),
+                    "kv quantizer launch");
+}
+
 rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K, const uint8_t *qw,
                            int64_t N, int32_t *acc, int64_t ldacc, void *stream) {
   rq_status s = check_gemm(qx, T, K, qw, N, acc, ldacc, 4);

@@ -58,6 +58,10 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
 // fused decode: p.qx, p.sx, p.zx and p.xo unused; the codes are made in the kernel
 bool decode_fused_fits(const GemmArgs &p, const FuseArgs &f);
 hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f, bool asym, int mode, hipStream_t st);
+
+// kv_quant.hip: per-group Walsh-Hadamard (optional) + group-wise asymmetric INT4
+hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int group, bool rotate,
+                              uint8_t *q, float *scale, int32_t *zero, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);

@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "rowlds_quant": _QUANT,
     "kron64_mfma": ["csrc/kron.hip", "csrc/rq_device.h"],
     "kron_quant": _QUANT,
+    "group_quant": ["csrc/kv_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"],
 }
 
 

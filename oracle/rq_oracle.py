@@ -353,8 +353,9 @@ def rotate_quant(x16: np.ndarray, kind: str, clip: float = 1.0, asym: bool = Fal
 def kv_rotate_quant(x16: np.ndarray, group: int = 128, rotate: bool = True) -> dict:
     """The KV-cache path: R3, then group-wise asymmetric INT4.
 
-    [SQR] second reviewer, A2: R3 rotates the KV cache before its
-    quantization, and (W_q R3)(W_k R3)^T = W_q W_k^T, so the rotation cancels
+    [SQR] the authors' answer on the number of rotation matrices: R3 rotates
+    the KV cache before its quantization; [SQR] first reviewer Q2/A2 (the two
+    R3 of Figure 1): (W_q R3)(W_k R3)^T = W_q W_k^T, so the rotation cancels
     in the attention scores.  Reading: R3 is the normalized Walsh-Hadamard of
     one head's `group` channels, applied to every head (blockdiag(H_group, ...)).
     [FQ] section 3 (quantization setting, after QuaRot): the KV cache is

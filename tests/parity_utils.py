@@ -9,6 +9,9 @@ Tolerances (fixed for this path):
   - Scales: within 1e-6 relative.
   - fp16 outputs: |y - y_ref| <= 1e-3 + 2e-3 |y_ref|; end-to-end comparisons
     widen this by the effect of the tolerated code flips.
+  - KV-cache quantizer (group-wise asymmetric, check_kv_quant): bit-exact
+    without rotation; with rotation, windows derived from the fp32 error of
+    the butterfly transform (see kv_error_bound).
 """
 import sys
 
@@ -107,3 +110,85 @@ def flip_allowance(sx, sw, flips_x, flips_w, qmax_x=15, qmax_w=7):
     sx = np.asarray(sx, np.float64)[:, None]
     sw = np.asarray(sw, np.float64)[None, :]
     return sx * sw * (qmax_w * np.asarray(flips_x)[:, None] + qmax_x * np.asarray(flips_w)[None, :]) * 1.001
+
+
+U32 = 2.0 ** -24
+
+
+def kv_error_bound(x16, group, rotate):
+    """Per-group bound on |v_gpu - v_exact| for the KV quantizer's transform.
+
+    The GPU evaluates the Walsh-Hadamard of a group by butterflies in fp32:
+    every output is a tree of log2(group) rounded additions of +-x_i, then
+    one rounded multiply by fp32(1/sqrt(group)).  The tree sum errs by at
+    most log2(group) u sum|x_i| (u = 2^-24); the constant and the multiply
+    add 2u |v|, and |v| <= sum|x_i| / sqrt(group).  Without rotation v is the
+    fp16 input itself: no error.
+    """
+    x = np.abs(np.asarray(x16, np.float64))
+    T, K = x.shape
+    if not rotate:
+        return np.zeros(T * (K // group))
+    d = int(np.log2(group))
+    return (d + 3) * U32 * x.reshape(T * (K // group), group).sum(axis=1) / np.sqrt(group)
+
+
+def check_kv_quant(q_packed_gpu, s_gpu, z_gpu, ref, x16, group, rotate, what="kv"):
+    """Compare the KV quantizer's output with the oracle's kv_rotate_quant.
+
+    Without rotation the result must be identical.  With rotation, lo and hi
+    move by at most E (kv_error_bound), so the scale moves by at most
+    2E/(hi - lo) + 2u relative (two fp32 roundings); a pre-round quantity p
+    (v/scale or -lo/scale) moves by E/scale + |p| (that + 3u), the 3u for a
+    reciprocal of the scale within two units and one product rounded before
+    the final one; a zero point or a code may differ by one only where p lies
+    within twice that window of a rounding boundary.
+    Where a zero point flipped, codes clamped at 0 or 15 on either side are
+    exempt (the clamp moves with the zero point).  Returns the flips per group.
+    """
+    q_gpu = o.unpack_int4(np.asarray(q_packed_gpu), signed=False).astype(np.int64)
+    T, K = ref["q"].shape
+    G = T * (K // group)
+    s_gpu = np.asarray(s_gpu, np.float64).reshape(G)
+    z_gpu = np.asarray(z_gpu, np.int64).reshape(G)
+    if not rotate:
+        assert np.array_equal(np.asarray(q_packed_gpu), ref["packed"]), f"{what}: codes differ"
+        assert np.array_equal(s_gpu, ref["scale"].reshape(G).astype(np.float64)), f"{what}: scales differ"
+        assert np.array_equal(z_gpu, ref["zero"].reshape(G)), f"{what}: zero points differ"
+        return np.zeros(G, np.int64)
+    E = kv_error_bound(x16, group, rotate)
+    s_ref = ref["scale"].reshape(G).astype(np.float64)
+    z_ref = ref["zero"].reshape(G).astype(np.int64)
+    pre = ref["pre"].reshape(G, group)
+    zpre = ref["zpre"].reshape(G)
+    q_ref = ref["q"].reshape(G, group).astype(np.int64)
+    q_gpu = q_gpu.reshape(G, group)
+    pos = s_ref > 0
+    safe = np.where(pos, s_ref, 1.0)
+    rel = np.where(pos, 2 * E / (15 * safe), 0.0) + 2 * U32   # the scale's relative error
+    # a zero range in exact arithmetic means an all-zero group, which the
+    # butterflies keep exactly zero
+    assert np.all(s_gpu[~pos] == 0), f"{what}: all-zero groups got a scale"
+    srel = np.abs(s_gpu - s_ref) / safe
+    assert np.all(srel[pos] <= 2 * rel[pos]), f"{what}: scale off by {srel[pos].max():.3g} relative"
+    rel = rel + 3 * U32
+
+    def dist(p):
+        return np.abs(p - (np.floor(p) + 0.5))
+
+    zwin = 2 * (E / safe + np.abs(zpre) * rel)
+    zd = z_gpu != z_ref
+    zbad = zd & ~((dist(zpre) <= zwin) & (np.abs(z_gpu - z_ref) <= 1))
+    assert not zbad.any(), f"{what}: {int(zbad.sum())} zero points differ away from a boundary"
+    win = 2 * (E[:, None] / safe[:, None] + np.abs(pre) * rel[:, None])
+    rel_gpu = q_gpu - z_gpu[:, None]
+    rel_ref = q_ref - z_ref[:, None]
+    ignore = zd[:, None] & ((q_gpu == 0) | (q_gpu == 15) | (q_ref == 0) | (q_ref == 15))
+    diff = (rel_gpu != rel_ref) & ~ignore
+    bad = diff & ~((dist(pre) <= win) & (np.abs(rel_gpu - rel_ref) <= 1))
+    if bad.any():
+        g, j = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} codes differ outside the fp32 window; first group {g} "
+                             f"col {j}: gpu={rel_gpu[g, j]} ref={rel_ref[g, j]} pre={pre[g, j]!r} "
+                             f"window={win[g, j]:.3g}")
+    return diff.sum(axis=1) + ignore.sum(axis=1)

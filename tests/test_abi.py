@@ -138,6 +138,24 @@ def test_quant_decode_linear_validation():
     assert f(FAKE, 8, 4096, 4096, None, FAKE, FAKE, None, 16, None, FAKE, 16, None) == rq.RQ_EINVAL
 
 
+def test_kv_rotate_quant_validation():
+    L = rq.lib()
+    f = L.rq_kv_rotate_quant
+    ok = lambda T=8, K=4096, ldx=4096, g=128, x=FAKE, q=FAKE, s=FAKE, z=FAKE: f(x, T, K, ldx, g, 1, q, s, z, None)
+    assert ok(T=0) == rq.RQ_OK                              # empty batch: nothing launched
+    assert ok(T=-1) == rq.RQ_EINVAL
+    assert ok(g=96) == rq.RQ_ESHAPE                         # group not 64 / 128 / 256
+    assert ok(g=32) == rq.RQ_ESHAPE
+    assert ok(K=4160) == rq.RQ_ESHAPE                       # K % group
+    assert ok(ldx=4090) == rq.RQ_EALIGN                     # ldx < K
+    assert ok(ldx=4100) == rq.RQ_EALIGN                     # ldx % 8
+    assert ok(x=None) == rq.RQ_EALIGN
+    assert ok(x=FAKE + 2) == rq.RQ_EALIGN                   # x 16-byte aligned
+    assert ok(q=FAKE + 2) == rq.RQ_EALIGN                   # q 4-byte aligned
+    assert ok(s=None) == rq.RQ_EALIGN
+    assert ok(z=FAKE + 1) == rq.RQ_EALIGN
+
+
 def test_prepare_weights_validation_and_workspace():
     L = rq.lib()
     kron = _rot("kron", n1=64, n2=64, p1=FAKE, p2=FAKE)

@@ -8,7 +8,7 @@ import pytest
 
 import workloads
 from oracle import rq_oracle as o
-from parity_utils import (check_asym_quant, check_scales, check_sym_quant, check_y, dev,
+from parity_utils import (check_asym_quant, check_kv_quant, check_scales, check_sym_quant, check_y, dev,
                           flip_allowance, host, note)
 
 pytestmark = pytest.mark.gpu
@@ -568,3 +568,129 @@ def test_deterministic_reruns():
     a = _e2e(inp, "gsr", 64, 0.9)
     b = _e2e(inp, "gsr", 64, 0.9)
     assert torch.equal(a[0]["q"], b[0]["q"]) and torch.equal(a[2], b[2])
+
+
+# ----------------------------------------------------------------------------- KV cache
+
+KV_CASES = [
+    # name, T, K, group, rotate, tensor
+    ("g128-rot-ragged", 301, 4096, 128, True, "x"),
+    ("g64-rot", 37, 4096, 64, True, "x"),
+    ("g256-rot", 37, 4096, 256, True, "x"),
+    ("g128-values-rot", 41, 4096, 128, True, "v"),
+    ("g128-plain", 301, 4096, 128, False, "x"),
+    ("g64-plain", 19, 1024, 64, False, "x"),
+    ("g256-plain-values", 19, 2048, 256, False, "v"),
+    ("one-group", 1, 128, 128, True, "x"),
+    ("one-group-plain", 1, 64, 64, False, "x"),
+    ("three-groups", 3, 384, 128, True, "x"),
+    ("wide-8192", 5, 8192, 128, True, "x"),
+    ("24-groups-per-row", 77, 3072, 128, True, "x"),
+    ("21-groups-per-row", 50, 1344, 64, True, "v"),
+    ("21-groups-per-row-plain", 50, 1344, 64, False, "x"),
+]
+
+
+@pytest.mark.parametrize("case", KV_CASES, ids=[c[0] for c in KV_CASES])
+def test_kv_rotate_quant_matches_oracle(case):
+    name, T, K, g, rot, which = case
+    note(f"[kv_rotate_quant] {name} T={T} K={K} group={g} rotate={rot}")
+    x = workloads.make_inputs("kv", T=T, K=K, with_weights=False)[which]
+    ref = o.kv_rotate_quant(x, group=g, rotate=rot)
+    out = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=rot)
+    torch.cuda.synchronize()
+    check_kv_quant(*(host(t) for t in out), ref, x, g, rot)
+
+
+def test_kv_rotate_quant_strided_rows_and_degenerate_groups():
+    note("[kv_rotate_quant] strided ldx, zero / constant / one-signed groups")
+    T, K, g = 6, 1024, 128
+    x = workloads.make_inputs("kv", T=T, K=K, with_weights=False)["x"].copy()
+    x[0] = 0                      # all-zero rows: scale 0, zero point 0, codes 0
+    x[1] = 1.5                    # constant: one nonzero value after R3
+    x[2] = -2.0                   # constant negative
+    x[3, :g] = np.abs(x[3, :g])   # one-signed groups
+    x[4, g:2 * g] = -np.abs(x[4, g:2 * g])
+    big = np.zeros((T, K + 64), np.float16)
+    big[:, :K] = x
+    xt = dev(big)[:, :K]
+    assert xt.stride(0) == K + 64
+    for rot in (True, False):
+        ref = o.kv_rotate_quant(x, group=g, rotate=rot)
+        out = rq.rq_kv_rotate_quant(xt, group=g, rotate=rot)
+        torch.cuda.synchronize()
+        check_kv_quant(*(host(t) for t in out), ref, x, g, rot)
+        assert np.all(host(out[1])[0] == 0) and np.all(host(out[2])[0] == 0)
+
+
+def _tie_inputs(g, s, rng):
+    """fp16 rows whose R3 image v is sparse on the grid of odd multiples of
+    s/2 with hi - lo = 15 s, so that every nonzero v / scale is an exact tie,
+    and whose values x = v . H / sqrt(g) are exact in fp16 (g = 64, 256:
+    1/sqrt(g) is a power of two)."""
+    from scipy.linalg import hadamard
+    rows = []
+    for _ in range(8):
+        v = np.zeros(g)
+        idx = rng.choice(g, 14, replace=False)
+        v[idx[:12]] = s * (rng.integers(-7, 7, 12) + 0.5)
+        v[idx[12]], v[idx[13]] = 7.5 * s, -7.5 * s
+        x = v @ hadamard(g) / np.sqrt(g)
+        assert np.array_equal(x.astype(np.float16).astype(np.float64), x)
+        rows.append(x)
+    return np.array(rows).reshape(2, 4 * g).astype(np.float16)
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_kv_rotate_quant_exact_ties(g):
+    """Every nonzero rotated value is a tie; the fp32 butterflies are exact on
+    these inputs, so the codes must round half to even exactly as the oracle."""
+    note(f"[kv_rotate_quant] exact ties group={g}")
+    rng = np.random.default_rng(g)
+    x = _tie_inputs(g, 0.5 if g == 64 else 1.0, rng)
+    ref = o.kv_rotate_quant(x, group=g, rotate=True)
+    assert (np.abs(ref["pre"] - np.floor(ref["pre"]) - 0.5) == 0).sum() > 50
+    q, s, z = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), ref["packed"])
+    assert np.array_equal(host(s), ref["scale"]) and np.array_equal(host(z), ref["zero"])
+    # the same ties without the transform (the inputs on a half-step grid)
+    xp = (np.round(x.astype(np.float64) * 2) / 2).astype(np.float16)
+    refp = o.kv_rotate_quant(xp, group=g, rotate=False)
+    q, s, z = rq.rq_kv_rotate_quant(dev(xp), group=g, rotate=False)
+    torch.cuda.synchronize()
+    check_kv_quant(host(q), host(s), host(z), refp, xp, g, False)
+
+
+def test_kv_rotate_quant_full_size_sampled():
+    """The kv workload at its full size (2048 tokens x 4096 channels, g=128),
+    in the launch the benchmark times: sampled token rows against the oracle,
+    the values (no rotation) against it in full."""
+    inp = workloads.make_inputs("kv", with_weights=False)
+    x, v = inp["x"], inp["v"]
+    note(f"[kv_rotate_quant] full size {x.shape}")
+    out = rq.rq_kv_rotate_quant(dev(x), group=128, rotate=True)
+    outv = rq.rq_kv_rotate_quant(dev(v), group=128, rotate=False)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, x.shape[0] - 1, np.random.default_rng(7).choice(x.shape[0], 125, replace=False)])
+    ref = o.kv_rotate_quant(x[rows], group=128, rotate=True)
+    check_kv_quant(host(out[0])[rows], host(out[1])[rows], host(out[2])[rows], ref, x[rows], 128, True)
+    check_kv_quant(*(host(t) for t in outv), o.kv_rotate_quant(v, group=128, rotate=False), v, 128, False)
+
+
+def test_kv_rotate_quant_grid_stride():
+    """More groups than one grid step covers (2048 wavefronts x 16 groups):
+    the grid-stride loop, rows that wrap inside a set (24 groups per row, a
+    step of 32768 groups is 1365 rows + 8 groups) and the clamped last set;
+    then 64 groups per row over 8200 rows."""
+    for T, K, g in ((1500, 3072, 128), (8200, 4096, 64)):
+        note(f"[kv_rotate_quant] grid stride T={T} K={K} group={g}")
+        x = workloads.make_inputs("kv", T=T, K=K, with_weights=False)["v"]
+        q, s, z = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=False)
+        torch.cuda.synchronize()
+        check_kv_quant(host(q), host(s), host(z), o.kv_rotate_quant(x, group=g, rotate=False), x, g, False)
+        rows = np.r_[0:3, 1364:1368, T - 3:T]
+        q, s, z = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=True)
+        torch.cuda.synchronize()
+        check_kv_quant(host(q)[rows], host(s)[rows], host(z)[rows], o.kv_rotate_quant(x[rows], group=g), x[rows],
+                       g, True)

@@ -20,11 +20,16 @@ token, the failure case FlatQuant's article describes in its section 2.2):
   quik     X [T, 8192] N(0,1), 256 outlier columns x40 kept in fp16, T = 4096
            (prefill) or the first 8 rows of it (decode); W [28672, 8192];
            asymmetric per-token INT4 on the 7936 normal columns.
+  kv       the KV cache of one LLaMA-2-7B attention layer over 2048 tokens,
+           32 heads of 128 channels: keys [2048, 4096] N(0,1) with 16
+           outlier channels x30, values [2048, 4096] N(0,1); keys take R3
+           (a 128-point Walsh-Hadamard per head), both are quantized
+           group-wise asymmetric INT4 with groups of 128 channels.
 
 Draw order per workload (numpy Generator, PCG64): outlier channel indices
 (choice without replacement, sorted), X (standard normal, scaled, cast to fp16
 once with round-to-nearest-even), W (standard normal x 0.02, cast to fp16),
-then the affine factors and channel scales for "flat".
+then the affine factors and channel scales for "flat", the values for "kv".
 """
 from __future__ import annotations
 
@@ -43,8 +48,8 @@ class Workload:
     T: int
     K: int
     N: int
-    rot: str                      # "hadamard" | "gsr" | "kron" | "none"
-    block: int = 0                # GSR block size
+    rot: str                      # "hadamard" | "gsr" | "kron" | "none" | "r3"
+    block: int = 0                # GSR block size; r3: head size = quantization group
     n1: int = 0                   # Kronecker factor sizes (K == n1 * n2)
     n2: int = 0
     clip_x: float = 1.0           # activation clip ratio
@@ -79,6 +84,8 @@ WORKLOADS = {
     "quik_decode": Workload("quik_decode", 4, 4096, 8192, 28672, "none",
                             asym=True, n_outlier_ch=256, outlier_mult=40.0,
                             n_out=256, decode_rows=8),
+    "kv": Workload("kv", 5, 2048, 4096, 0, "r3", block=128, asym=True,
+                   n_outlier_ch=16, outlier_mult=30.0),
 }
 
 
@@ -151,4 +158,6 @@ def make_inputs(name: str, T: int | None = None, K: int | None = None,
         out["w"] = make_weights(wl, N=N, K=K, rng=rng)
     if wl.rot == "kron":
         out["p1"], out["p2"], out["s"] = make_affine(wl, rng, n1, n2)
+    if wl.rot == "r3":
+        out["v"] = rng.standard_normal(x.shape).astype(np.float16)
     return out
