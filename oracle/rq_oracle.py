@@ -38,6 +38,21 @@ import numpy as np
 
 QMAX_SYM4 = 7       # symmetric INT4 range [-7, 7]   ([SQR] Q1/A1, reading c1)
 QMAX_ASYM4 = 15     # asymmetric INT4 range [0, 15]  ([QUIK] part 1, reading c4)
+QMAX_SYM8 = 127     # the same forms at 8 bits (QUIK-8B; reading r22)
+QMAX_ASYM8 = 255
+
+
+def code_max(bits: int, asym: bool) -> int:
+    """Code range of the min-max quantizers at 4 or 8 bits.
+
+    [SQR] Q1/A1: symmetric codes span +-(2^{N-1} - 1); asymmetric codes span
+    [0, 2^N - 1] ([QUIK] part 1 form, reading c4).  [QUIK] "QUIK量化" part 3
+    and the QUIK-8B experiments: the sensitive down projection runs with
+    8-bit weights and activations (reading r22).
+    """
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    return (1 << bits) - 1 if asym else (1 << (bits - 1)) - 1
 
 
 # --------------------------------------------------------------------------
@@ -203,6 +218,14 @@ def quantize_asym(x: np.ndarray, qmax: int = QMAX_ASYM4):
     return q, scale, zero, pre, zpre
 
 
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Codes as stored: two per byte at 4 bits (pack_int4), one byte each at
+    8 bits (signed codes as 8-bit two's complement)."""
+    if bits == 4:
+        return pack_int4(q)
+    return np.asarray(q).astype(np.int16).astype(np.uint8)
+
+
 def pack_int4(q: np.ndarray) -> np.ndarray:
     """Two 4-bit codes per byte: element 2j in the low nibble, 2j+1 in the high.
 
@@ -325,11 +348,13 @@ def select_outlier_columns(x: np.ndarray, count: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def rotate_quant(x16: np.ndarray, kind: str, clip: float = 1.0, asym: bool = False,
-                 outlier_idx=None, block: int = 0, p1=None, p2=None, chan_scale=None) -> dict:
-    """Online transform + per-token INT4 quantization of activations.
+                 outlier_idx=None, block: int = 0, p1=None, p2=None, chan_scale=None,
+                 bits: int = 4) -> dict:
+    """Online transform + per-token INT4 (or INT8) quantization of activations.
 
     Returns codes (unpacked and packed), scale, zero (asymmetric), the fp16
     outlier columns, and the fp64 pre-round values for tolerance checks.
+    bits = 8 is QUIK-8B's form for the down projection (reading r22).
     """
     x = np.asarray(x16, np.float16).astype(np.float64)          # exact upcast
     x_out = np.zeros((x.shape[0], 0), np.float16)
@@ -341,12 +366,12 @@ def rotate_quant(x16: np.ndarray, kind: str, clip: float = 1.0, asym: bool = Fal
         x = x @ rotation(kind, K, block, p1, p2, chan_scale)
     out = {"x_out": x_out, "xr": x}
     if asym:
-        q, s, z, pre, zpre = quantize_asym(x)
+        q, s, z, pre, zpre = quantize_asym(x, code_max(bits, True))
         out.update(q=q, scale=s, zero=z, pre=pre, zpre=zpre)
     else:
-        q, s, pre = quantize_sym(x, clip)
+        q, s, pre = quantize_sym(x, clip, code_max(bits, False))
         out.update(q=q, scale=s, zero=None, pre=pre)
-    out["packed"] = pack_int4(q)
+    out["packed"] = pack_codes(q, bits)
     return out
 
 
@@ -378,7 +403,7 @@ def kv_rotate_quant(x16: np.ndarray, group: int = 128, rotate: bool = True) -> d
 
 
 def prepare_weights(w16: np.ndarray, kind: str, clip: float = 1.0, outlier_idx=None,
-                    block: int = 0, p1=None, p2=None, chan_scale=None) -> dict:
+                    block: int = 0, p1=None, p2=None, chan_scale=None, bits: int = 4) -> dict:
     """Offline weight side: W' = W . R^{-T}, then per-output-channel symmetric RTN.
 
     [QS] sections 1-2 (rotation folded into the weights), [FQ] section 3
@@ -394,8 +419,8 @@ def prepare_weights(w16: np.ndarray, kind: str, clip: float = 1.0, outlier_idx=N
     K = w.shape[1]
     if kind != "none":
         w = w @ weight_transform(kind, K, block, p1, p2, chan_scale)
-    q, s, pre = quantize_sym(w, clip)
-    return {"q": q, "scale": s, "pre": pre, "packed": pack_int4(q),
+    q, s, pre = quantize_sym(w, clip, code_max(bits, False))
+    return {"q": q, "scale": s, "pre": pre, "packed": pack_codes(q, bits),
             "rowsum": q.astype(np.int64).sum(axis=1).astype(np.int32), "w_out": w_out,
             "wr": w}
 

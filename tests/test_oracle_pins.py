@@ -520,3 +520,107 @@ def test_kv_rotate_quant_without_rotation_is_groupwise_asymmetric():
     for gi in range(2):
         part = o.rotate_quant(np.ascontiguousarray(x[:, gi * 128:(gi + 1) * 128]), "none", asym=True)
         np.testing.assert_array_equal(two["q"][:, gi * 128:(gi + 1) * 128], part["q"])
+
+
+# ---------------------------------------------------------------- 8-bit (QUIK-8B)
+
+from fractions import Fraction
+
+
+def _fp32_round(fr):
+    """Correct rounding of an exact rational to fp32 (ties to even), without
+    going through fp64: the two fp32 neighbours, compared exactly."""
+    f = np.float32(float(fr))
+    cands = {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+    best = sorted(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best[0])
+
+
+def _rne(fr):
+    return round(fr)   # Fraction rounding is round-half-to-even
+
+
+def _exact_asym8(row):
+    xs = [Fraction(float(v)) for v in row]
+    lo, hi = min(min(xs), Fraction(0)), max(max(xs), Fraction(0))
+    s = _fp32_round((hi - lo) / 255)
+    if s == 0:
+        return [0] * len(xs), s, 0
+    sf = Fraction(float(s))
+    z = min(max(_rne(-lo / sf), 0), 255)
+    return [min(max(_rne(x / sf) + z, 0), 255) for x in xs], s, z
+
+
+def _exact_sym8(row, clip=1.0):
+    xs = [Fraction(float(v)) for v in row]
+    amax = max(abs(x) for x in xs)
+    s = _fp32_round(Fraction(float(np.float32(clip))) * amax / 127)
+    if s == 0:
+        return [0] * len(xs), s
+    sf = Fraction(float(s))
+    return [min(max(_rne(x / sf), -127), 127) for x in xs], s
+
+
+def test_8bit_quantizers_match_exact_rational_arithmetic():
+    """Per-token asymmetric INT8 activations and per-channel symmetric INT8
+    weights against exact rational arithmetic: workload rows with outlier
+    columns split off, a row of exact ties (scale 2^-6 exactly), a zero row."""
+    inp = workloads.make_inputs("quik_prefill", T=6, K=512, N=5)
+    x, w, idx = inp["x"].copy(), inp["w"], inp["outlier_ch"][:32]
+    keep = np.setdiff1d(np.arange(512), idx)
+    ties = (np.arange(len(keep)) % 255) * 2.0 ** -6 + 2.0 ** -7   # (k + 1/2) s with s = 2^-6
+    ties[0], ties[1] = 0.0, 255 * 2.0 ** -6                         # lo = 0, hi = 255 s
+    x[4, keep] = ties.astype(np.float16)
+    x[5] = 0
+    xq = o.rotate_quant(x, "none", asym=True, outlier_idx=idx, bits=8)
+    for t in range(6):
+        q, s, z = _exact_asym8(x[t, keep].astype(np.float64))
+        assert xq["scale"][t] == s and xq["zero"][t] == z
+        np.testing.assert_array_equal(xq["q"][t], q)
+    assert np.array_equal(xq["packed"], xq["q"].astype(np.uint8))
+    assert len(set(xq["q"][4][2:].tolist()) & {0, 2, 4}) and xq["scale"][4] == 2.0 ** -6
+    np.testing.assert_array_equal(xq["x_out"], x[:, idx])
+    wq = o.prepare_weights(w, "none", outlier_idx=idx, bits=8)
+    for n in range(5):
+        q, s = _exact_sym8(w[n, keep].astype(np.float64))
+        assert wq["scale"][n] == s
+        np.testing.assert_array_equal(wq["q"][n], q)
+    assert np.array_equal(wq["packed"].view(np.int8), wq["q"].astype(np.int8))
+    assert np.array_equal(wq["rowsum"], wq["q"].astype(np.int64).sum(1))
+
+
+def test_8bit_lossless_pipeline_and_bounds():
+    """Operands already on their 8-bit grids go through exactly, and the
+    mixed 8-bit pipeline reproduces (q - z) s (qw sw)^T + X_out W_out^T."""
+    rng = np.random.default_rng(11)
+    T, N, K = 5, 7, 256
+    sx = 2.0 ** -3
+    qx = rng.integers(0, 256, (T, K)); qx[:, 0], qx[:, 1] = 0, 255   # lo = -z s, hi = (255 - z) s
+    z = 100
+    x = (qx - z) * sx
+    qw = rng.integers(-127, 128, (N, K)); qw[:, 0] = 127
+    sw = 2.0 ** -9
+    w = qw * sw
+    x16, w16 = x.astype(np.float16), w.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x) and np.array_equal(w16.astype(np.float64), w)
+    xq = o.rotate_quant(x16, "none", asym=True, bits=8)
+    wq = o.prepare_weights(w16, "none", bits=8)
+    np.testing.assert_array_equal(xq["q"], qx)
+    assert np.all(xq["zero"] == z) and np.all(xq["scale"] == sx)
+    np.testing.assert_array_equal(wq["q"], qw)
+    y = o.linear(xq, wq)["y"]
+    np.testing.assert_array_equal(y, (x @ w.T).astype(np.float16))
+    # workload data: codes in range, half-step round trip, int32 accumulators fit
+    inp = workloads.make_inputs("quik_prefill", T=8, K=1024, N=6)
+    idx = inp["outlier_ch"][:64]
+    xq = o.rotate_quant(inp["x"], "none", asym=True, outlier_idx=idx, bits=8)
+    wq = o.prepare_weights(inp["w"], "none", outlier_idx=idx, bits=8)
+    assert xq["q"].min() >= 0 and xq["q"].max() <= 255
+    assert wq["q"].min() >= -127 and wq["q"].max() <= 127
+    xn, _ = o.split_outliers(inp["x"].astype(np.float64), idx)
+    xd = (xq["q"].astype(np.float64) - xq["zero"][:, None]) * xq["scale"].astype(np.float64)[:, None]
+    assert np.all(np.abs(xd - xn) <= xq["scale"].astype(np.float64)[:, None] * 0.5 * (1 + 1e-6) + 1e-12)
+    acc = o.linear(xq, wq)["acc"]
+    np.testing.assert_array_equal(acc, o.int_gemm_bruteforce(xq["q"], wq["q"]))
+    with pytest.raises(ValueError):
+        o.code_max(6, True)
