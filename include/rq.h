@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 1
+#define RQ_ABI_VERSION 2
 
 typedef enum {
   RQ_OK = 0,
@@ -82,7 +82,7 @@ typedef struct {
   const float *chan_scale;
 } rq_rot_desc;
 
-/* Per-row quantizer.
+/* Per-row quantizer, at bits = 4 (the default; 0 means 4) or bits = 8.
  *   asymmetric == 0: scale = fp32(clip_ratio * max|x'| / 7),
  *                    code = clamp(rne(x'/scale), -7, 7)
  *                    (SpinQuant OpenReview, first reviewer Q1/A1: min-max onto
@@ -97,17 +97,24 @@ typedef struct {
  *   parts 1 and 3).  Must be distinct and in [0, K); order does not matter:
  *   outlier columns are emitted in ascending column order, the other K - n_out
  *   columns keep their relative order.  Violating this gives unspecified
- *   values but never an out-of-bounds access.  n_out = 0: no split. */
+ *   values but never an out-of-bounds access.  n_out = 0: no split.
+ *   bits == 8 (QUIK-8B, for the sensitive down projection: QUIK blog,
+ *   "QUIK量化" part 3; the 8-bit layers take more outliers, experiments part 1
+ *   and end-to-end speedup): the same forms with 127 in place of 7 and 255 in
+ *   place of 15, one byte per code (signed codes as 8-bit two's complement);
+ *   only without a rotation (kind NONE).  Other values of bits: RQ_EINVAL. */
 typedef struct {
   int32_t asymmetric;
   float clip_ratio;
   const int32_t *outlier_idx;
   int32_t n_out;
+  int32_t bits;
 } rq_quant_desc;
 
 /* rq_rotate_quant -- online transform + per-token INT4 quantization + packing.
  *   x        fp16 [T, ldx] (row t starts at x + t*ldx elements; ldx >= K, ldx % 8 == 0)
- *   q        out uint8 [T, (K - n_out)/2] packed codes (dense rows)
+ *   q        out uint8 [T, (K - n_out)/2] packed codes (dense rows); at
+ *            bits == 8, [T, K - n_out], one byte per code
  *   scale    out fp32 [T]
  *   zero     out int32 [T] (asymmetric only; NULL for symmetric)
  *   code_sum out int32 [T] sum of each row's codes (NULL to skip); the
@@ -183,7 +190,7 @@ rq_status rq_mixed_outlier_linear(const uint8_t *qx, const float *sx, const int3
  *            as written by rq_prepare_weights with the same outlier_idx
  *   y        out fp16 [T, ldy], ldy >= N
  * Shapes: 1 <= T <= 16 (T == 0 is a no-op), K % 32 == 0, K <= 8192,
- * (K - n_out) % 128 == 0; otherwise RQ_ESHAPE (use the two calls). */
+ * (K - n_out) % 128 == 0, 4-bit codes; otherwise RQ_ESHAPE (use the two calls). */
 rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ldx,
                                  const rq_quant_desc *qd, const uint8_t *qw, const float *sw,
                                  const int32_t *w_rowsum, int64_t N, const void *w_out,
@@ -214,6 +221,32 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
 rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
                              int32_t rotate, uint8_t *q, float *scale, int32_t *zero,
                              void *stream);
+
+/* rq_w8a8_linear -- the 8-bit form of rq_mixed_outlier_linear (QUIK-8B's
+ * down projection: QUIK blog, "QUIK量化" part 3 and the QUIK-8B experiments;
+ * INT32 accumulation, part 4; the FP16 outlier product added before the one
+ * rounding, part 1):
+ *   y[t][n] = fp16( (acc[t][n] - zx[t]*w_rowsum[n]) * sx[t] * sw[n]
+ *                   + sum_j x_out[t][j] * w_out[n][j] ),
+ *   acc = sum_k qx[t][k] * qw[n][k] over K_int one-byte codes.
+ *   qx uint8 [T, K_int]: unsigned codes in [0, 255] with zero points zx int32
+ *   [T]; zx NULL: signed codes in [-127, 127] (two's complement), w_rowsum
+ *   may then be NULL.  qw/sw/w_rowsum as written by rq_prepare_weights with
+ *   bits = 8.  x_out fp16 [T, n_out], w_out fp16 [N, n_out] (n_out % 32 == 0,
+ *   may be 0 with NULL pointers).  K_int % 64 == 0, 0 < K_int <= 32768. */
+rq_status rq_w8a8_linear(const uint8_t *qx, const float *sx, const int32_t *zx, int64_t T,
+                         int64_t K_int, const uint8_t *qw, const float *sw,
+                         const int32_t *w_rowsum, int64_t N, const void *x_out,
+                         const void *w_out, int32_t n_out, void *y, int64_t ldy, void *stream);
+
+/* rq_w8a8_gemm_i32 -- the raw INT32 accumulator of one-byte codes,
+ * acc[t][n] = sum_k qx[t][k]*qw[n][k], for bit-exact tests.  x_unsigned != 0:
+ * qx codes are unsigned [0, 255] and w_rowsum (int32 [N], the row sums of qw)
+ * is required; otherwise signed.  acc int32 [T, ldacc], ldacc >= N;
+ * K % 64 == 0, K <= 32768. */
+rq_status rq_w8a8_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K,
+                           const uint8_t *qw, const int32_t *w_rowsum, int64_t N, int32_t *acc,
+                           int64_t ldacc, void *stream);
 
 /* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
  * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];

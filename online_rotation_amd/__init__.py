@@ -23,12 +23,14 @@ ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w4a4_gemm_i32", "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
+           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_w4a4_gemm_i32", "rq_status_string",
+           "rq_last_error", "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w4a4_gemm_i32", "rq_status_string", "rq_last_error", "rq_abi_version")
+           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_w4a4_gemm_i32", "rq_status_string",
+           "rq_last_error", "rq_abi_version")
 
 
 class RqError(RuntimeError):
@@ -45,7 +47,7 @@ class _RotDesc(ctypes.Structure):
 
 class _QuantDesc(ctypes.Structure):
     _fields_ = [("asymmetric", ctypes.c_int32), ("clip_ratio", ctypes.c_float),
-                ("outlier_idx", ctypes.c_void_p), ("n_out", ctypes.c_int32)]
+                ("outlier_idx", ctypes.c_void_p), ("n_out", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,8 +75,11 @@ def lib() -> ctypes.CDLL:
         L.rq_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), vp, vp,
                                              vp, i64, vp, vp, i64, vp]
         L.rq_kv_rotate_quant.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.rq_w8a8_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, vp, i64, vp]
+        L.rq_w8a8_gemm_i32.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp, i64, vp]
         for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear", "rq_mixed_outlier_linear",
-                   "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant"):
+                   "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_w8a8_linear",
+                   "rq_w8a8_gemm_i32"):
             getattr(L, fn).restype = ctypes.c_int
         L.rq_status_string.argtypes = [ctypes.c_int]
         L.rq_status_string.restype = ctypes.c_char_p
@@ -160,29 +165,32 @@ class Rotation:
                         _ptr(self.p2), _ptr(self.chan_scale))
 
 
-def _qdesc(asym: bool, clip: float, outlier_idx):
+def _qdesc(asym: bool, clip: float, outlier_idx, bits: int = 4):
     n_out = 0 if outlier_idx is None else int(outlier_idx.numel())
-    return _QuantDesc(1 if asym else 0, float(clip), _ptr(outlier_idx), n_out), n_out
+    return _QuantDesc(1 if asym else 0, float(clip), _ptr(outlier_idx), n_out, int(bits)), n_out
 
 
 def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
-                    outlier_idx=None, code_sum: bool = False, out: dict | None = None) -> dict:
-    """x fp16 [T, K] (row stride x.stride(0)) -> dict(q, scale, zero, code_sum, x_out)."""
+                    outlier_idx=None, code_sum: bool = False, out: dict | None = None,
+                    bits: int = 4) -> dict:
+    """x fp16 [T, K] (row stride x.stride(0)) -> dict(q, scale, zero, code_sum, x_out).
+    bits = 8: one byte per code (rotation none only)."""
     import torch
     _gpu(x, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
     T, K = x.shape
     _want(x, "x", torch.float16, dense=False)
     _want(outlier_idx, "outlier_idx", torch.int32)
     rot.check(K)
-    qd, n_out = _qdesc(asym, clip, outlier_idx)
+    qd, n_out = _qdesc(asym, clip, outlier_idx, bits)
     dev = x.device
+    qb = (K - n_out) if bits == 8 else (K - n_out) // 2
     o = dict(out or {})
-    o.setdefault("q", torch.empty((T, (K - n_out) // 2), dtype=torch.uint8, device=dev))
+    o.setdefault("q", torch.empty((T, qb), dtype=torch.uint8, device=dev))
     o.setdefault("scale", torch.empty((T,), dtype=torch.float32, device=dev))
     o.setdefault("zero", torch.empty((T,), dtype=torch.int32, device=dev) if asym else None)
     o.setdefault("code_sum", torch.empty((T,), dtype=torch.int32, device=dev) if code_sum else None)
     o.setdefault("x_out", torch.empty((T, n_out), dtype=torch.float16, device=dev) if n_out else None)
-    _want(o["q"], "q", torch.uint8, (T, (K - n_out) // 2))
+    _want(o["q"], "q", torch.uint8, (T, qb))
     _want(o["scale"], "scale", torch.float32, (T,))
     _want(o["zero"], "zero", torch.int32, (T,))
     _want(o["code_sum"], "code_sum", torch.int32, (T,))
@@ -196,20 +204,21 @@ def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
     return o
 
 
-def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None) -> dict:
-    """w fp16 [N, K] -> dict(q, scale, rowsum, w_out): rotated, per-channel INT4."""
+def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None, bits: int = 4) -> dict:
+    """w fp16 [N, K] -> dict(q, scale, rowsum, w_out): rotated, per-channel INT4
+    (bits = 8: INT8, one byte per code, rotation none only)."""
     import torch
     _gpu(w, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
     N, K = w.shape
     _want(w, "w", torch.float16, dense=False)
     _want(outlier_idx, "outlier_idx", torch.int32)
     rot.check(K)
-    qd, n_out = _qdesc(False, clip, outlier_idx)
+    qd, n_out = _qdesc(False, clip, outlier_idx, bits)
     dev = w.device
     rd = rot.desc()
     ws_bytes = lib().rq_prepare_weights_workspace_bytes(ctypes.byref(rd))
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
-    o = {"q": torch.empty((N, (K - n_out) // 2), dtype=torch.uint8, device=dev),
+    o = {"q": torch.empty((N, (K - n_out) if bits == 8 else (K - n_out) // 2), dtype=torch.uint8, device=dev),
          "scale": torch.empty((N,), dtype=torch.float32, device=dev),
          "rowsum": torch.empty((N,), dtype=torch.int32, device=dev),
          "w_out": torch.empty((N, n_out), dtype=torch.float16, device=dev) if n_out else None}
@@ -313,6 +322,49 @@ def rq_kv_rotate_quant(x, group: int = 128, rotate: bool = True, out=None):
                                   _ptr(q), _ptr(sc), _ptr(zp), _stream(x.device))
     _check(st, "rq_kv_rotate_quant")
     return q, sc, zp
+
+
+def rq_w8a8_linear(qx, sx, zx, qw, sw, w_rowsum, x_out=None, w_out=None, out=None):
+    """8-bit mixed linear (QUIK-8B): one-byte codes, dequantized INT8 part +
+    fp16 outlier product.  zx None: signed activation codes."""
+    import torch
+    _gpu(qx, sx, zx, qw, sw, w_rowsum, x_out, w_out, out)
+    T, K = qx.shape
+    N = qw.shape[0]
+    n_out = 0 if x_out is None else int(x_out.shape[1])
+    _want(qx, "qx", torch.uint8)
+    _want(qw, "qw", torch.uint8, (N, K))
+    _want(sx, "sx", torch.float32, (T,))
+    _want(zx, "zx", torch.int32, (T,))
+    _want(sw, "sw", torch.float32, (N,))
+    _want(w_rowsum, "w_rowsum", torch.int32, (N,))
+    _want(x_out, "x_out", torch.float16, (T, n_out))
+    if (x_out is None) != (w_out is None):
+        raise ValueError("rq: x_out and w_out come together")
+    _want(w_out, "w_out", torch.float16, (N, n_out))
+    y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=qx.device)
+    _want(y, "out", torch.float16, (T, N), dense=False)
+    st = lib().rq_w8a8_linear(_ptr(qx), _ptr(sx), _ptr(zx), T, K, _ptr(qw), _ptr(sw), _ptr(w_rowsum), N,
+                              _ptr(x_out), _ptr(w_out), n_out, _ptr(y), y.stride(0), _stream(qx.device))
+    _check(st, "rq_w8a8_linear")
+    return y
+
+
+def rq_w8a8_gemm_i32(qx, qw, x_unsigned: bool = False, w_rowsum=None, out=None):
+    """Raw INT32 accumulator [T, N] of one-byte codes (for bit-exact tests)."""
+    import torch
+    _gpu(qx, qw, w_rowsum, out)
+    T, K = qx.shape
+    N = qw.shape[0]
+    _want(qx, "qx", torch.uint8)
+    _want(qw, "qw", torch.uint8, (N, K))
+    _want(w_rowsum, "w_rowsum", torch.int32, (N,))
+    acc = out if out is not None else torch.empty((T, N), dtype=torch.int32, device=qx.device)
+    _want(acc, "out", torch.int32, (T, N), dense=False)
+    st = lib().rq_w8a8_gemm_i32(_ptr(qx), 1 if x_unsigned else 0, T, K, _ptr(qw), _ptr(w_rowsum), N,
+                                _ptr(acc), acc.stride(0), _stream(qx.device))
+    _check(st, "rq_w8a8_gemm_i32")
+    return acc
 
 
 def rq_w4a4_gemm_i32(qx, qw, x_unsigned: bool = False, out=None):

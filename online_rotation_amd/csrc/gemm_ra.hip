@@ -58,9 +58,15 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
 
 }  // namespace
 
-template <bool XU, int MODE>
+// BITS = 8: the operands are int8 codes (QUIK-8B's down projection), used by
+// the MFMAs as they are; a k-step is then 64 codes (still 64 bytes per row),
+// two MFMA groups, slot 2g + c in lane group g.  Unsigned activation codes
+// (XU) are moved to signed by flipping bit 7 (u - 128), and the epilogue adds
+// back 128 * rowsum.
+template <bool XU, int MODE, int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
+  constexpr int kGroups = BITS == 8 ? 2 : 4;  // MFMA groups per k-step
   __shared__ __align__(16) uint8_t Bs[kRaNB * kRaBuf];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -81,13 +87,13 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   const int br = tid >> 2, bq = tid & 3;
   const uint8_t *bp0 = p.qw + min(n0 + br, p.N - 1) * Kb + 16 * bq;
   const uint8_t *bp1 = p.qw + min(n0 + 64 + br, p.N - 1) * Kb + 16 * bq;
-  const int ws0 = ra_off(br, 2 * bq), ws1 = ra_off(br, 2 * bq + 1);
-  const int ws2 = ra_off(br + 64, 2 * bq), ws3 = ra_off(br + 64, 2 * bq + 1);
+  const int ws0 = ra_off(br, BITS == 8 ? bq : 2 * bq), ws1 = ra_off(br, 2 * bq + 1);
+  const int ws2 = ra_off(br + 64, BITS == 8 ? bq : 2 * bq), ws3 = ra_off(br + 64, 2 * bq + 1);
   // fragment of block j, MFMA c: row 32j + l32, slot 4g + c.  ((32j + l32) >> 1) & 7
   // does not depend on j, so the offset is j * 32 * kRaRow + rs[c].
   int rs[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) rs[c] = l32 * kRaRow + (((4 * g + c) ^ ((l32 >> 1) & 7)) << 4);
+  for (int c = 0; c < 4; ++c) rs[c] = l32 * kRaRow + (((kGroups * g + c) ^ ((l32 >> 1) & 7)) << 4);
 
   uint4 ra[kRaD][4], rb[kRaD][2];
   auto gload = [&](int s, int kb) {
@@ -103,8 +109,12 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   auto bstore = [&](int buf, int s, int h) {
     uint8_t *B = Bs + buf * kRaBuf;
     const uint4 &w = rb[s][h];
-    *reinterpret_cast<v4i *>(B + (h ? ws2 : ws0)) = widen_signed(w.x, w.y);
-    *reinterpret_cast<v4i *>(B + (h ? ws3 : ws1)) = widen_signed(w.z, w.w);
+    if (BITS == 8) {
+      *reinterpret_cast<uint4 *>(B + (h ? ws2 : ws0)) = w;
+    } else {
+      *reinterpret_cast<v4i *>(B + (h ? ws2 : ws0)) = widen_signed(w.x, w.y);
+      *reinterpret_cast<v4i *>(B + (h ? ws3 : ws1)) = widen_signed(w.z, w.w);
+    }
   };
   v4i bf[2][4];  // B fragments, double-buffered across MFMA groups
   auto bread = [&](int f, int buf, int c) {
@@ -113,6 +123,18 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     for (int j = 0; j < 4; ++j) bf[f][j] = *reinterpret_cast<const v4i *>(B + j * 32 * kRaRow + rs[c]);
   };
   auto awiden = [&](int s, int c, v4i *aw) {
+    if (BITS == 8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 &w = ra[s][2 * i + c];
+        const uint32_t f = XU ? 0x80808080u : 0u;
+        aw[i][0] = (int)(w.x ^ f);
+        aw[i][1] = (int)(w.y ^ f);
+        aw[i][2] = (int)(w.z ^ f);
+        aw[i][3] = (int)(w.w ^ f);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint4 &w = ra[s][2 * i + (c >> 1)];
@@ -159,6 +181,25 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       const int ub = v % kRaNB, nb = (v + 1) % kRaNB;  // LDS buffers of steps kb, kb+1
       const bool live = !decltype(tail)::value || kb < nsteps;
       v4i aw[2];
+      if (BITS == 8) {
+        // group 0, then B(kb+1) into its buffer and the barrier; group 1
+        // reads step kb+1's first fragments and refills A's load slot
+        bread(1, ub, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        awiden(u, 0, aw);
+        if (live) mfma8(aw, 0);
+        bstore(nb, us, 0);
+        bstore(nb, us, 1);
+        __syncthreads();
+        awiden(u, 1, aw);
+        __builtin_amdgcn_sched_barrier(0);
+        gload(u, min(kb + kRaD, last));
+        bread(0, nb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (live) mfma8(aw, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
       // (sched_barrier: keep each group's fragment reads ahead of its MFMAs;
       // the scheduler otherwise sinks them next to their first use)
       // group 0
@@ -201,7 +242,9 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
-  constexpr int kShift = XU ? 4 : 8;
+  constexpr int kShift = BITS == 8 ? 0 : (XU ? 4 : 8);
+  // 8-bit unsigned codes went in as u - 128: sum (u - z) w = acc - (z - 128) rowsum
+  constexpr int kZoff = (BITS == 8 && XU) ? 128 : 0;
   const int64_t row0 = m0 + wave * 64, col0 = n0;
   if (MODE == 0) {
     int32_t *out = reinterpret_cast<int32_t *>(p.out);
@@ -210,10 +253,11 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t gn = col0 + 32 * j + l32;
+        const int32_t rsj = kZoff ? p.rowsum[min(gn, p.N - 1)] : 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = acc[i][j][r] >> kShift;
+          if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = (acc[i][j][r] >> kShift) + kZoff * rsj;
         }
       }
     return;
@@ -224,7 +268,7 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   for (int j = 0; j < 4; ++j) {
     const int64_t gn = min(col0 + 32 * j + l32, p.N - 1);
     swn[j] = p.sw[gn];
-    rsn[j] = (MODE == 2 && p.zx) ? p.rowsum[gn] : 0;
+    rsn[j] = ((MODE == 2 && p.zx) || kZoff) ? p.rowsum[gn] : 0;
   }
   v16f f[2][4];
 #pragma unroll
@@ -233,11 +277,11 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     for (int r = 0; r < 16; ++r) {
       const int64_t gm = min(row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3), p.T - 1);
       const float sxm = p.sx[gm];
-      const int32_t zxm = (MODE == 2 && p.zx) ? p.zx[gm] : 0;
+      const int32_t zxm = ((MODE == 2 && p.zx) ? p.zx[gm] : 0) - kZoff;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int32_t v = acc[i][j][r] >> kShift;
-        if (MODE == 2) v -= zxm * rsn[j];
+        if (MODE == 2 || kZoff) v -= zxm * rsn[j];
         f[i][j][r] = (float)v * sxm * swn[j];
       }
     }
@@ -326,13 +370,28 @@ hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStrea
   const int nt_m = (int)((p.T + kRaBM - 1) / kRaBM), nt_n = (int)((p.N + kRaBN - 1) / kRaBN);
   const dim3 grid((unsigned)(nt_m * nt_n)), block(256);
   if (mode == 0) {
-    if (x_unsigned) gemm_ra<true, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-    else gemm_ra<false, 0><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    if (x_unsigned) gemm_ra<true, 0, 4><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 0, 4><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   } else if (mode == 1) {
-    gemm_ra<false, 1><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    gemm_ra<false, 1, 4><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   } else {
-    if (x_unsigned) gemm_ra<true, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
-    else gemm_ra<false, 2><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    if (x_unsigned) gemm_ra<true, 2, 4><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 2, 4><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  const int nt_m = (int)((p.T + kRaBM - 1) / kRaBM), nt_n = (int)((p.N + kRaBN - 1) / kRaBN);
+  const dim3 grid((unsigned)(nt_m * nt_n)), block(256);
+  if (mode == 0) {
+    if (x_unsigned) gemm_ra<true, 0, 8><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 0, 8><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else if (mode == 1) {
+    gemm_ra<false, 1, 8><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+  } else {
+    if (x_unsigned) gemm_ra<true, 2, 8><<<grid, block, 0, st>>>(p, nt_m, nt_n);
+    else gemm_ra<false, 2, 8><<<grid, block, 0, st>>>(p, nt_m, nt_n);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,240 @@
+// quant8.hip -- per-row INT8 quantization of unrotated rows with the QUIK
+// outlier split, for the 8-bit down projection (QUIK blog, "QUIK量化" part 3:
+// the sensitive down projection is quantized to INT8; experiments, part 1:
+// its outlier count grows with the layer's input width; end-to-end speedup:
+// more than 600 outliers there).  Activations take per-token asymmetric codes
+// in [0, 255] (part 1's form at 8 bits), weights per-channel symmetric codes
+// in [-127, 127]; one byte per code.
+//
+// One workgroup per row, grid-stride over rows.  At start the workgroup turns
+// the outlier list into a bit mask and, per 8-column chunk, the output offset
+// of its first kept column (a block prefix scan), both in LDS.  Per row, two
+// passes of 16-byte loads over 8-column chunks (the second from L2): masked
+// fp16 min / max (or |x| max) and the block reduction, then codes written
+// byte by byte into an LDS copy of the packed row at their compacted
+// positions, outlier values to x_out, and the row stored with 16-byte writes.
+#include "rq_device.h"
+#include "rq_kernels.h"
+
+namespace rq {
+
+namespace {
+
+constexpr int kQ8Threads = 256;
+
+// rne(x / s) for s > 0, exactly, whenever |x / s| < 2^22 and x - b s below is
+// either 0 or at least 2^-62 in magnitude (true for fp16 x and the scales made
+// from fp16 ranges).  c is the integer nearest x * inv, b the half-integer
+// between c and its neighbour on the side of x * inv; the sign of x - b s is
+// exact in one fma, and zero only at a tie, where rint(b) goes to even.
+__device__ __forceinline__ float rne_div(float x, float s, float inv) {
+  const float t = x * inv;
+  const float c = __builtin_rintf(t);
+  const float b = c + __builtin_copysignf(0.5f, t - c);
+  const float d = __builtin_fmaf(-b, s, x);
+  return __builtin_rintf(b + __builtin_amdgcn_fmed3f(d * 0x1p64f, -0.25f, 0.25f));
+}
+
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_min(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kQ8Threads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : fminf(r, red[w]);
+  return r;
+}
+
+struct Q8Args {
+  const __half *x;
+  int64_t T, ldx;
+  int K, nch;              // columns, 8-column chunks (K / 8)
+  int kint;                // K - n_out: codes per row
+  float clip;
+  const int32_t *oidx;
+  int n_out;
+  uint8_t *q;              // [T, kint]
+  float *scale;
+  int32_t *zero;           // asymmetric only
+  int32_t *code_sum;       // or null
+  __half *x_out;           // [T, n_out] or null
+};
+
+template <bool ASYM>
+__global__ __launch_bounds__(kQ8Threads) void split_quant8(Q8Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t *mask = reinterpret_cast<uint32_t *>(smem);           // [K / 32] outlier bits
+  int32_t *cbase = reinterpret_cast<int32_t *>(smem + a.K / 8);  // [K / 8] first kept position per chunk
+  uint8_t *row = smem + ((a.K / 8 + a.K / 2 + 15) & ~15);       // [K] bytes: the packed row
+  __shared__ float red[2][kQ8Threads / 64];
+  __shared__ int ired[kQ8Threads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // ---- outlier mask, then per chunk the output offset of its first kept column
+  for (int i = tid; i < a.K / 32; i += kQ8Threads) mask[i] = 0u;
+  __syncthreads();
+  for (int j = tid; j < a.n_out; j += kQ8Threads) {
+    const int col = a.oidx[j];
+    if (col >= 0 && col < a.K) atomicOr(&mask[col >> 5], 1u << (col & 31));
+  }
+  __syncthreads();
+  auto cmask = [&](int c) { return (mask[c >> 2] >> (8 * (c & 3))) & 0xFFu; };
+  // block exclusive scan of the kept counts over contiguous chunk ranges
+  const int cpt = (a.nch + kQ8Threads - 1) / kQ8Threads;
+  int kept = 0;
+  for (int i = 0; i < cpt; ++i) {
+    const int c = tid * cpt + i;
+    if (c < a.nch) kept += 8 - __builtin_popcount(cmask(c));
+  }
+  const int incl = wave_scan_dpp(kept);  // inclusive prefix within the wave
+  if (lane == 63) ired[wave] = incl;
+  __syncthreads();
+  int base = incl - kept;
+  for (int w = 0; w < wave; ++w) base += ired[w];
+  for (int i = 0; i < cpt; ++i) {
+    const int c = tid * cpt + i;
+    if (c < a.nch) {
+      cbase[c] = base;
+      base += 8 - __builtin_popcount(cmask(c));
+    }
+  }
+  __syncthreads();
+
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  for (int64_t r = blockIdx.x; r < a.T; r += gridDim.x) {
+    const __half *src = a.x + r * a.ldx;
+    // pass 1: masked min / max of the kept columns (outliers count as 0,
+    // which the range [min(x, 0), max(x, 0)] already contains), or |x| max
+    h2 mn2 = {0, 0}, mx2 = {0, 0};
+#pragma unroll 4
+    for (int c = tid; c < a.nch; c += kQ8Threads) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(src + 8 * c);
+      const uint32_t m = cmask(c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = ((m >> (2 * e)) & 1u ? 0u : 0x0000FFFFu) | ((m >> (2 * e + 1)) & 1u ? 0u : 0xFFFF0000u);
+        const uint32_t d = w[e] & keep;
+        h2 h;
+        __builtin_memcpy(&h, &d, 4);
+        if (!ASYM) h = __builtin_elementwise_abs(h);
+        mn2 = __builtin_elementwise_min(mn2, h);
+        mx2 = __builtin_elementwise_max(mx2, h);
+      }
+    }
+    float s, inv, zf = 0.0f, lo_c, hi_c;
+    if (ASYM) {
+      const float mn = block_reduce(fminf((float)mn2[0], (float)mn2[1]), red[0], false);
+      const float mx = block_reduce(fmaxf((float)mx2[0], (float)mx2[1]), red[1], true);
+      const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
+      // the scale is the exact quotient rounded once to fp32: formed in fp64
+      // (hi - lo is exact) and converted, as a single rounding would be
+      // except where the fp64 quotient itself falls on an fp32 midpoint
+      s = (float)((double)(hi - lo) / 255.0);
+      inv = s > 0.0f ? 1.0f / s : 0.0f;
+      if (s > 0.0f) zf = __builtin_amdgcn_fmed3f(rne_div(-lo, s, inv), 0.0f, 255.0f);
+      lo_c = 0.0f;
+      hi_c = 255.0f;
+    } else {
+      const float mx = block_reduce(fmaxf((float)mx2[0], (float)mx2[1]), red[1], true);
+      s = (float)((double)a.clip * (double)mx / 127.0);  // the product is exact in fp64
+      inv = s > 0.0f ? 1.0f / s : 0.0f;
+      lo_c = -127.0f;
+      hi_c = 127.0f;
+    }
+    // pass 2 (the row again, from L2): codes into the LDS row at their
+    // compacted positions; outlier values to x_out
+    int csum = 0;
+#pragma unroll 2
+    for (int c = tid; c < a.nch; c += kQ8Threads) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(src + 8 * c);
+      const uint32_t m = cmask(c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      int kpos = cbase[c];
+      if (m == 0u) {  // no outlier in the chunk: eight consecutive codes
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 f2 = __half22float2(*reinterpret_cast<const __half2 *>(&w[e >> 1]));
+          const float f = (e & 1) ? f2.y : f2.x;
+          const int ci = (int)__builtin_amdgcn_fmed3f(s > 0.0f ? rne_div(f, s, inv) + zf : 0.0f, lo_c, hi_c);
+          csum += ci;
+          if (kpos + e < a.kint) row[kpos + e] = (uint8_t)ci;
+        }
+      } else {
+        int opos = 8 * c - kpos;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+          if ((m >> e) & 1u) {
+            if (opos < a.n_out) reinterpret_cast<uint16_t *>(a.x_out)[r * a.n_out + opos] = (uint16_t)bits;
+            ++opos;
+          } else {
+            const float f = __half2float(__ushort_as_half((unsigned short)bits));
+            const int ci = (int)__builtin_amdgcn_fmed3f(s > 0.0f ? rne_div(f, s, inv) + zf : 0.0f, lo_c, hi_c);
+            csum += ci;
+            if (kpos < a.kint) row[kpos] = (uint8_t)ci;
+            ++kpos;
+          }
+        }
+      }
+    }
+    if (a.code_sum) {
+      const int cs = wave_sum(csum);
+      if (lane == 0) ired[wave] = cs;
+      __syncthreads();
+      if (tid == 0) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kQ8Threads / 64; ++w) t += ired[w];
+        a.code_sum[r] = t;
+      }
+    }
+    if (tid == 0) {
+      a.scale[r] = s;
+      if (ASYM) a.zero[r] = (int)zf;
+    }
+    __syncthreads();
+    uint8_t *dst = a.q + r * (int64_t)a.kint;
+    for (int o = 16 * tid; o < a.kint; o += 16 * kQ8Threads)
+      *reinterpret_cast<uint4 *>(dst + o) = *reinterpret_cast<const uint4 *>(row + o);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t split8_smem_bytes(int64_t K) { return (((size_t)(K / 8) + (size_t)(K / 2) + 15) & ~(size_t)15) + (size_t)K; }
+
+hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
+                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
+                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
+  Q8Args a;
+  a.x = (const __half *)x;
+  a.T = T;
+  a.ldx = ldx;
+  a.K = (int)K;
+  a.nch = (int)(K / 8);
+  a.kint = (int)(K - n_out);
+  a.clip = clip;
+  a.oidx = outlier_idx;
+  a.n_out = n_out;
+  a.q = q;
+  a.scale = scale;
+  a.zero = zero;
+  a.code_sum = code_sum;
+  a.x_out = (__half *)x_out;
+  const size_t lds = split8_smem_bytes(K);
+  const dim3 g((unsigned)(T < 2048 ? T : 2048)), b(kQ8Threads);
+  const void *k = asym ? reinterpret_cast<const void *>(split_quant8<true>)
+                       : reinterpret_cast<const void *>(split_quant8<false>);
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (asym) split_quant8<true><<<g, b, lds, st>>>(a);
+  else split_quant8<false><<<g, b, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace rq

@@ -55,7 +55,9 @@ rq_status check_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq
   if ((K - qd->n_out) % 64) return fail(RQ_ESHAPE, "K - n_out = %lld is not a multiple of 64", (long long)(K - qd->n_out));
   if (!(qd->clip_ratio > 0.0f && qd->clip_ratio <= 1.0f)) return fail(RQ_EINVAL, "clip_ratio must be in (0, 1]");
   if (qd->asymmetric && qd->clip_ratio != 1.0f) return fail(RQ_EINVAL, "asymmetric quantization takes clip_ratio 1");
+  if (qd->bits != 0 && qd->bits != 4 && qd->bits != 8) return fail(RQ_EINVAL, "bits=%d must be 4 or 8", qd->bits);
   if (rot->kind < RQ_ROT_NONE || rot->kind > RQ_ROT_KRON) return fail(RQ_EINVAL, "unknown rotation kind %d", rot->kind);
+  if (qd->bits == 8 && rot->kind != RQ_ROT_NONE) return fail(RQ_ESHAPE, "8-bit codes are only supported without a rotation");
   if (rot->kind != RQ_ROT_NONE && qd->n_out) return fail(RQ_ESHAPE, "outlier split is only supported without a rotation");
   if (rot->kind != RQ_ROT_NONE && qd->asymmetric) return fail(RQ_ESHAPE, "asymmetric codes are only supported without a rotation");
   if (rot->kind == RQ_ROT_HADAMARD && !(pow2(K) && K >= 64)) return fail(RQ_ESHAPE, "HADAMARD needs a power-of-two K >= 64 (K=%lld)", (long long)K);
@@ -102,6 +104,11 @@ rq_status run_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_r
   if (K == 4096 && (rot->kind == RQ_ROT_HADAMARD || rot->kind == RQ_ROT_GSR) && !qd->asymmetric && qd->n_out == 0) {
     e = rq::launch_fwht4096(x, T, ldx, gsr, span_log2, norm, qd->clip_ratio, q, scale, code_sum, st);
     return hip_status(e, "fwht4096_quant launch");
+  }
+  if (rot->kind == RQ_ROT_NONE && qd->bits == 8) {
+    e = rq::launch_split8(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
+                          qd->n_out, q, scale, zero, code_sum, x_out, st);
+    return hip_status(e, "split_quant8 launch");
   }
   if (rot->kind == RQ_ROT_NONE) {
     e = rq::launch_split(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
@@ -224,6 +231,7 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
   if (n_out > 0 && !qd->outlier_idx) return fail(RQ_EINVAL, "outlier_idx is NULL with n_out > 0");
   if (!(qd->clip_ratio > 0.0f && qd->clip_ratio <= 1.0f)) return fail(RQ_EINVAL, "clip_ratio must be in (0, 1]");
   if (qd->asymmetric && qd->clip_ratio != 1.0f) return fail(RQ_EINVAL, "asymmetric quantization takes clip_ratio 1");
+  if (qd->bits != 0 && qd->bits != 4) return fail(RQ_ESHAPE, "the fused decode form takes 4-bit codes");
   if (T > 16) return fail(RQ_ESHAPE, "the fused decode form takes T <= 16 (T=%lld)", (long long)T);
   if (K % 32 || K > 8192 || (K - n_out) % 128)
     return fail(RQ_ESHAPE, "the fused decode form needs K %% 32 == 0, K <= 8192, (K - n_out) %% 128 == 0 (K=%lld)", (long long)K);
@@ -261,6 +269,34 @@ rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, i
   if (!zero || !aligned(zero, 4)) return fail(RQ_EALIGN, "zero is required, 4-byte aligned");
   return hip_status(rq::launch_group_quant(x, T, K, ldx, group, rotate != 0, q, scale, zero, (hipStream_t)stream),
                     "kv quantizer launch");
+}
+
+rq_status rq_w8a8_linear(const uint8_t *qx, const float *sx, const int32_t *zx, int64_t T, int64_t K_int,
+                         const uint8_t *qw, const float *sw, const int32_t *w_rowsum, int64_t N,
+                         const void *x_out, const void *w_out, int32_t n_out, void *y, int64_t ldy,
+                         void *stream) {
+  rq_status s = check_gemm(qx, T, K_int, qw, N, y, ldy, 2);
+  if (s != RQ_OK) return s;
+  if (K_int > 32768) return fail(RQ_ESHAPE, "8-bit K_int=%lld exceeds 32768", (long long)K_int);
+  if (n_out < 0 || n_out % 32) return fail(RQ_ESHAPE, "n_out=%d must be a non-negative multiple of 32", n_out);
+  if (T == 0) return ok();
+  if (!sx || !sw || !aligned(sx, 4) || !aligned(sw, 4)) return fail(RQ_EINVAL, "sx and sw are required (4-byte aligned)");
+  if (zx && (!w_rowsum || !aligned(zx, 4) || !aligned(w_rowsum, 4))) return fail(RQ_EINVAL, "asymmetric codes need zx and w_rowsum (4-byte aligned)");
+  if (n_out > 0 && (!x_out || !w_out || !aligned(x_out, 16) || !aligned(w_out, 16))) return fail(RQ_EINVAL, "x_out and w_out are required (16-byte aligned) when n_out > 0");
+  rq::GemmArgs p{qx, qw, T, N, K_int, sx, sw, zx, w_rowsum, (const __half *)x_out,
+                 (const __half *)w_out, n_out, y, ldy};
+  return hip_status(rq::launch_gemm_ra8(p, zx != nullptr, 2, (hipStream_t)stream), "gemm launch");
+}
+
+rq_status rq_w8a8_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K, const uint8_t *qw,
+                           const int32_t *w_rowsum, int64_t N, int32_t *acc, int64_t ldacc, void *stream) {
+  rq_status s = check_gemm(qx, T, K, qw, N, acc, ldacc, 4);
+  if (s != RQ_OK) return s;
+  if (K > 32768) return fail(RQ_ESHAPE, "8-bit K=%lld exceeds 32768", (long long)K);
+  if (T == 0) return ok();
+  if (x_unsigned && (!w_rowsum || !aligned(w_rowsum, 4))) return fail(RQ_EINVAL, "unsigned codes need w_rowsum (4-byte aligned)");
+  rq::GemmArgs p{qx, qw, T, N, K, nullptr, nullptr, nullptr, x_unsigned ? w_rowsum : nullptr, nullptr, nullptr, 0, acc, ldacc};
+  return hip_status(rq::launch_gemm_ra8(p, x_unsigned != 0, 0, (hipStream_t)stream), "gemm launch");
 }
 
 rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K, const uint8_t *qw,

@@ -64,6 +64,13 @@ hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, 
                               uint8_t *q, float *scale, int32_t *zero, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
+// one-byte codes (Kb = K bytes per row); x_unsigned: codes in [0, 255], p.rowsum required
+hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
+// quant8.hip: unrotated per-row INT8 with the outlier split
+size_t split8_smem_bytes(int64_t K);
+hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
+                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
+                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 
 }  // namespace rq

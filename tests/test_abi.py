@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rq.rq_abi_version() == 1
+    assert rq.rq_abi_version() == 2
     assert rq.rq_status_string(0) == "RQ_OK"
     for s in range(1, 5):
         assert rq.rq_status_string(s).startswith("RQ_E")
@@ -176,3 +176,24 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros((4, 4096), dtype=torch.float16)
     with pytest.raises(ValueError):
         rq.rq_rotate_quant(x, rq.Rotation("hadamard"))
+
+
+def test_8bit_validation():
+    L = rq.lib()
+    q8 = rq._QuantDesc(1, 1.0, FAKE, 256, 8)
+    bad_bits = rq._QuantDesc(0, 1.0, None, 0, 6)
+    assert _rotate_quant(8, 8192, 8192, _rot("none"), bad_bits) == rq.RQ_EINVAL          # bits 6
+    assert _rotate_quant(8, 4096, 4096, _rot("hadamard"), rq._QuantDesc(0, 1.0, None, 0, 8)) == rq.RQ_ESHAPE
+    assert _rotate_quant(0, 8192, 8192, _rot("none"), q8, zero=FAKE, x_out=FAKE) == rq.RQ_OK
+    f = L.rq_w8a8_linear
+    assert f(FAKE, FAKE, FAKE, 8, 40000, FAKE, FAKE, FAKE, 16, None, None, 0, FAKE, 16, None) == rq.RQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, 8, 1000, FAKE, FAKE, FAKE, 16, None, None, 0, FAKE, 16, None) == rq.RQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, 8, 1024, FAKE, FAKE, None, 16, None, None, 0, FAKE, 16, None) == rq.RQ_EINVAL
+    assert f(FAKE, FAKE, None, 8, 1024, FAKE, FAKE, None, 16, None, None, 32, FAKE, 16, None) == rq.RQ_EINVAL
+    assert f(FAKE, FAKE, None, 0, 1024, FAKE, FAKE, None, 16, None, None, 0, FAKE, 16, None) == rq.RQ_OK
+    g = L.rq_w8a8_gemm_i32
+    assert g(FAKE, 1, 8, 1024, FAKE, None, 16, FAKE, 16, None) == rq.RQ_EINVAL            # unsigned without rowsum
+    assert g(FAKE, 0, 8, 40960, FAKE, None, 16, FAKE, 16, None) == rq.RQ_ESHAPE
+    d = L.rq_quant_decode_linear
+    assert d(FAKE, 8, 4096, 4096, ctypes.byref(rq._QuantDesc(0, 1.0, None, 0, 8)), FAKE, FAKE, FAKE, 16, None,
+             FAKE, 16, None) == rq.RQ_ESHAPE

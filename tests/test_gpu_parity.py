@@ -694,3 +694,128 @@ def test_kv_rotate_quant_grid_stride():
         torch.cuda.synchronize()
         check_kv_quant(host(q)[rows], host(s)[rows], host(z)[rows], o.kv_rotate_quant(x[rows], group=g), x[rows],
                        g, True)
+
+
+# ----------------------------------------------------------------------------- 8-bit (QUIK-8B)
+
+Q8_CASES = [
+    # name, T, K, n_out, pattern, asym, clip
+    ("asym-64", 37, 2048, 64, "workload", True, 1.0),
+    ("asym-clustered-192", 19, 4096, 192, "clustered", True, 1.0),
+    ("sym-clip", 23, 1024, 0, "workload", False, 0.9),
+    ("asym-down-proj-width", 5, 28672, 896, "workload", True, 1.0),
+    ("sym-32768", 3, 32768, 0, "workload", False, 1.0),
+    ("asym-more-rows-than-grid", 2100, 512, 64, "workload", True, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", Q8_CASES, ids=[c[0] for c in Q8_CASES])
+def test_rotate_quant_8bit_matches_oracle(case):
+    name, T, K, n_out, pattern, asym, clip = case
+    note(f"[rotate_quant 8-bit] {name} T={T} K={K} n_out={n_out}")
+    inp = workloads.make_inputs("quik8_down", T=T, K=K, with_weights=False)
+    x = inp["x"].copy()
+    if T >= 4:  # a zero row, a constant row and a row of exact ties (scale 2^-6)
+        x[1] = 0
+        x[2] = 0.75
+        x[3] = ((np.arange(K) % 255) * 2.0 ** -6 + 2.0 ** -7).astype(np.float16)
+    idx = _outlier_pattern(inp, K, n_out, pattern) if n_out else None
+    if idx is not None and T >= 4:
+        keep = np.setdiff1d(np.arange(K), idx)
+        x[3, keep[0]], x[3, keep[1]] = 0.0, 255 * 2.0 ** -6
+    ref = o.rotate_quant(x, "none", clip=clip, asym=asym, outlier_idx=idx, bits=8)
+    out = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), clip=clip, asym=asym,
+                             outlier_idx=None if idx is None else dev(idx), code_sum=True, bits=8)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["q"]), ref["packed"]), "codes differ"
+    assert np.array_equal(host(out["scale"]), ref["scale"]), "scales differ"
+    if asym:
+        assert np.array_equal(host(out["zero"]), ref["zero"]), "zero points differ"
+    assert np.array_equal(host(out["code_sum"]), ref["q"].astype(np.int64).sum(axis=1))
+    if n_out:
+        assert np.array_equal(host(out["x_out"]), ref["x_out"])
+
+
+def test_prepare_weights_8bit_matches_oracle():
+    note("[prepare_weights 8-bit] N=70 K=2048 n_out=64")
+    inp = workloads.make_inputs("quik8_down", T=4, K=2048, N=70)
+    idx = inp["outlier_ch"][:64].astype(np.int32)
+    ref = o.prepare_weights(inp["w"], "none", outlier_idx=idx, bits=8)
+    wq = rq.rq_prepare_weights(dev(inp["w"]), rq.Rotation("none"), outlier_idx=dev(idx), bits=8)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(wq["q"]), ref["packed"])
+    assert np.array_equal(host(wq["scale"]), ref["scale"])
+    assert np.array_equal(host(wq["rowsum"]), ref["rowsum"])
+    assert np.array_equal(host(wq["w_out"]), ref["w_out"])
+
+
+GEMM8_SHAPES = [(300, 1024, 200), (5, 64, 33), (257, 27776, 130), (1, 128, 1), (513, 2048, 257)]
+
+
+@pytest.mark.parametrize("shape", GEMM8_SHAPES, ids=[f"{t}x{k}x{n}" for t, k, n in GEMM8_SHAPES])
+@pytest.mark.parametrize("unsigned", [True, False], ids=["u8", "s8"])
+def test_w8a8_gemm_i32_bit_exact(shape, unsigned):
+    T, K, N = shape
+    note(f"[w8a8_gemm_i32] T={T} K={K} N={N} unsigned={unsigned}")
+    rng = np.random.default_rng(T * 7 + K + N)
+    qx = rng.integers(0, 256, (T, K)) if unsigned else rng.integers(-127, 128, (T, K))
+    qw = rng.integers(-127, 128, (N, K))
+    qx[0, :] = 255 if unsigned else 127   # extremes in the first row and column
+    qw[0, :] = -127
+    ref = o.int_gemm(qx, qw)
+    rowsum = qw.sum(axis=1).astype(np.int32)
+    acc = rq.rq_w8a8_gemm_i32(dev(qx.astype(np.int16).astype(np.uint8)), dev(qw.astype(np.int16).astype(np.uint8)),
+                              x_unsigned=unsigned, w_rowsum=dev(rowsum) if unsigned else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), ref)
+
+
+@pytest.mark.parametrize("n_out", [64, 0])
+def test_w8a8_linear_end_to_end(n_out):
+    note(f"[w8a8_linear] T=70 K=2048 N=96 n_out={n_out}")
+    inp = workloads.make_inputs("quik8_down", T=70, K=2048, N=96)
+    x, w = inp["x"], inp["w"]
+    idx = inp["outlier_ch"][:n_out].astype(np.int32) if n_out else None
+    xr = o.rotate_quant(x, "none", asym=True, outlier_idx=idx, bits=8)
+    wr = o.prepare_weights(w, "none", outlier_idx=idx, bits=8)
+    yr = o.linear(xr, wr)["y"]
+    didx = dev(idx) if n_out else None
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=didx, bits=8)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=didx, bits=8)
+    y = rq.rq_w8a8_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"], wq["rowsum"],
+                          xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(xq["q"]), xr["packed"]) and np.array_equal(host(wq["q"]), wr["packed"])
+    check_y(host(y), yr)
+    # symmetric activations (signed codes, no zero point)
+    xs = o.rotate_quant(x, "none", outlier_idx=idx, bits=8)
+    xqs = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), outlier_idx=didx, bits=8)
+    ys = rq.rq_w8a8_linear(xqs["q"], xqs["scale"], None, wq["q"], wq["scale"], wq["rowsum"],
+                           xqs["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    check_y(host(ys), o.linear(xs, wr)["y"])
+
+
+def test_quik8_full_size_sampled():
+    """The quik8_down workload at full size (T=4096, K=28672, N=8192, 896
+    outliers) in the benchmark's calls: sampled token rows and weight rows
+    against the oracle, and y at their crossings."""
+    inp = workloads.make_inputs("quik8_down")
+    x, w = inp["x"], inp["w"]
+    idx = inp["outlier_ch"].astype(np.int32)
+    note(f"[quik8 full size] x {x.shape} w {w.shape} n_out {idx.size}")
+    didx = dev(idx)
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=didx, bits=8)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=didx, bits=8)
+    y = rq.rq_w8a8_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"], wq["rowsum"],
+                          xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    ts = np.unique(np.r_[0, x.shape[0] - 1, rng.choice(x.shape[0], 22, replace=False)])
+    ns = np.unique(np.r_[0, w.shape[0] - 1, rng.choice(w.shape[0], 30, replace=False)])
+    xr = o.rotate_quant(x[ts], "none", asym=True, outlier_idx=idx, bits=8)
+    wr = o.prepare_weights(w[ns], "none", outlier_idx=idx, bits=8)
+    assert np.array_equal(host(xq["q"])[ts], xr["packed"])
+    assert np.array_equal(host(xq["zero"])[ts], xr["zero"]) and np.array_equal(host(xq["scale"])[ts], xr["scale"])
+    assert np.array_equal(host(wq["q"])[ns], wr["packed"]) and np.array_equal(host(wq["rowsum"])[ns], wr["rowsum"])
+    check_y(host(y)[np.ix_(ts, ns)], o.linear(xr, wr)["y"])

@@ -25,6 +25,10 @@ token, the failure case FlatQuant's article describes in its section 2.2):
            outlier channels x30, values [2048, 4096] N(0,1); keys take R3
            (a 128-point Walsh-Hadamard per head), both are quantized
            group-wise asymmetric INT4 with groups of 128 channels.
+  quik8_down  the LLaMA-2-70B down projection in QUIK's 8-bit form:
+           X [4096, 28672] N(0,1) with 896 outlier columns x40 kept in fp16
+           (256 per 8192 input features, scaled to 28672), W [8192, 28672];
+           per-token asymmetric INT8 activations, per-channel INT8 weights.
 
 Draw order per workload (numpy Generator, PCG64): outlier channel indices
 (choice without replacement, sorted), X (standard normal, scaled, cast to fp16
@@ -59,6 +63,7 @@ class Workload:
     outlier_mult: float = 1.0
     pivot_mult: float = 1.0       # token 0 multiplier
     n_out: int = 0                # fp16-kept outlier columns (QUIK)
+    bits: int = 4                 # code width of activations and weights
     decode_rows: int = 0          # >0: the decode variant keeps the first rows
     extra: dict = field(default_factory=dict)
 
@@ -86,6 +91,8 @@ WORKLOADS = {
                             n_out=256, decode_rows=8),
     "kv": Workload("kv", 5, 2048, 4096, 0, "r3", block=128, asym=True,
                    n_outlier_ch=16, outlier_mult=30.0),
+    "quik8_down": Workload("quik8_down", 6, 4096, 28672, 8192, "none", asym=True,
+                           n_outlier_ch=896, outlier_mult=40.0, n_out=896, bits=8),
 }
 
 
