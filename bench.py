@@ -19,6 +19,10 @@ when one exists for this kernel, workload and kernel source, else null.
 `--counters` instead launches calibration kernels of known traffic and the
 two calls a few times, for `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` runs.
 
+`--workload quik8_down` runs the same step at 8 bits (QUIK-8B's form for
+the LLaMA-2-70B down projection: T=4096, K=28672, N=8192, 896 fp16 outlier
+columns; rq_w8a8_linear on INT8 matrix cores).
+
 `--workload kv` measures the KV-cache quantizer instead: one step quantizes
 one attention layer's keys (R3, a 128-point Walsh-Hadamard per head) and
 values, group-wise asymmetric INT4 with groups of 128 channels; the line
@@ -38,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "W4A4 rotated-linear TOPS (T=2048,K=N=4096) + rotate-quant GB/s, % roofline"
+METRIC8 = "W8A8 QUIK-8B down-projection TOPS + INT8 quantizer GB/s, % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
 FP64_PEAK_TFLOPS = 78.6        # MI355X dense FP64 MFMA
@@ -50,7 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode", "kv"])
+                    choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode", "quik8_down",
+                             "kv"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled per step (0: >640 MB)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,8 +66,10 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_kernel(T, Kb, n_out=0):
+def gemm_kernel(T, Kb, n_out=0, bits=4):
     """The GEMM kernel the library dispatches to (launch_gemm's rules)."""
+    if bits == 8:
+        return "gemm_ra"
     if Kb % 64 == 0 and T <= 16 and T * (Kb // 16 + n_out // 8) <= 4096:
         return "gemm_decode16"
     if Kb % 64 == 0 and T <= 32:
@@ -73,6 +81,8 @@ def gemm_kernel(T, Kb, n_out=0):
 
 def quant_kernel(wl):
     """The quantizer kernel the library dispatches to (run_quant's rules)."""
+    if wl.bits == 8:
+        return "split_quant8"
     if wl.rot in ("hadamard", "gsr") and wl.K == 4096:
         return "fwht4096_mfma"
     if wl.rot == "kron":
@@ -93,13 +103,13 @@ def cpu_baseline(inp, wl, seconds):
     if kind == "kron":
         kw = {"p1": inp["p1"], "p2": inp["p2"], "chan_scale": inp["s"]}
     idx = inp["outlier_ch"] if wl.asym else None
-    wq = o.prepare_weights(inp["w"], kind, outlier_idx=idx, **kw)   # offline side, untimed
+    wq = o.prepare_weights(inp["w"], kind, outlier_idx=idx, bits=wl.bits, **kw)   # offline side, untimed
     ts = min(256, inp["x"].shape[0])
     xs = inp["x"][:ts]
     runs = 0
     t0 = time.perf_counter()
     while True:
-        xq = o.rotate_quant(xs, kind, clip=wl.clip_x, asym=wl.asym, outlier_idx=idx, **kw)
+        xq = o.rotate_quant(xs, kind, clip=wl.clip_x, asym=wl.asym, outlier_idx=idx, bits=wl.bits, **kw)
         o.linear(xq, wq)
         runs += 1
         el = time.perf_counter() - t0
@@ -305,20 +315,22 @@ def main():
     mixed = wl.asym
     idx = torch.from_numpy(inp["outlier_ch"]).to(dev) if mixed else None
     n_out = wl.n_out if mixed else 0
-    Kq = K - n_out                                       # codes per row through the INT4 path
-    wq0 = rq.rq_prepare_weights(w0, rot, outlier_idx=idx)  # offline weight side
+    Kq = K - n_out                                       # codes per row through the integer path
+    bits = wl.bits
+    Kqb = Kq if bits == 8 else Kq // 2                   # code bytes per row
+    wq0 = rq.rq_prepare_weights(w0, rot, outlier_idx=idx, bits=bits)  # offline weight side
     del w0
     torch.cuda.synchronize()
 
     # enough buffer sets that inputs come from HBM, not the 256 MB Infinity Cache
-    w_bytes = N * Kq // 2 + N * 4 + (N * 4 + N * n_out * 2 if mixed else 0)
-    x_bytes = T * K * 2 + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
+    w_bytes = N * Kqb + N * 4 + (N * 4 + N * n_out * 2 if mixed else 0)
+    x_bytes = T * K * 2 + T * Kqb + T * 8 + T * n_out * 2 + T * N * 2
     # (at most 512 sets: the tiny workload is latency-bound and would need thousands)
     S = args.sets if args.sets > 0 else min(512, max(2, -(-(640 << 20) // (w_bytes + x_bytes))))
     xs = [x0.clone() for _ in range(S)]
     wqs = [{k: (v.clone() if v is not None and k != "_workspace" else v) for k, v in wq0.items()}
            for _ in range(S)]
-    xq = [{"q": torch.empty((T, Kq // 2), dtype=torch.uint8, device=dev),
+    xq = [{"q": torch.empty((T, Kqb), dtype=torch.uint8, device=dev),
            "scale": torch.empty((T,), dtype=torch.float32, device=dev),
            "zero": torch.empty((T,), dtype=torch.int32, device=dev) if mixed else None,
            "x_out": torch.empty((T, n_out), dtype=torch.float16, device=dev) if mixed else None}
@@ -327,10 +339,13 @@ def main():
     footprint = S * (w_bytes + x_bytes)
 
     def rotate(i):
-        rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, asym=mixed, outlier_idx=idx, out=xq[i])
+        rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, asym=mixed, outlier_idx=idx, out=xq[i], bits=bits)
 
     def gemm(i):
-        if mixed:
+        if bits == 8:
+            rq.rq_w8a8_linear(xq[i]["q"], xq[i]["scale"], xq[i]["zero"], wqs[i]["q"], wqs[i]["scale"],
+                              wqs[i]["rowsum"], xq[i]["x_out"], wqs[i]["w_out"], out=ys[i])
+        elif mixed:
             rq.rq_mixed_outlier_linear(xq[i]["q"], xq[i]["scale"], xq[i]["zero"], wqs[i]["q"],
                                        wqs[i]["scale"], wqs[i]["rowsum"], xq[i]["x_out"],
                                        wqs[i]["w_out"], out=ys[i])
@@ -355,7 +370,7 @@ def main():
             step(i % sc)
         torch.cuda.synchronize()
         print(json.dumps({"counters": "done", "workload": wl.name, "calib_bytes": CALIB_BYTES,
-                          "gemm_kernel": gemm_kernel(T, Kq // 2, n_out), "quant_kernel": quant_kernel(wl)}),
+                          "gemm_kernel": gemm_kernel(T, Kqb, n_out, bits), "quant_kernel": quant_kernel(wl)}),
               flush=True)
         return
 
@@ -420,11 +435,11 @@ def main():
     gemm_s = timed(g_gemm, reps_per_graph, args.reps)
 
     ops = 2.0 * T * N * Kq + 2.0 * T * N * n_out      # INT4 part + fp16 outlier part
-    rq_bytes = T * K * 2 + T * (Kq // 2) + T * 4 + (T * 4 + T * n_out * 2 if mixed else 0)
+    rq_bytes = T * K * 2 + T * Kqb + T * 4 + (T * 4 + T * n_out * 2 if mixed else 0)
     gemm_tops = ops / gemm_s / 1e12
     rq_gbs = rq_bytes / rot_s / 1e9
-    gemm_bytes = w_bytes + T * Kq // 2 + T * 8 + T * n_out * 2 + T * N * 2
-    gk, qk = gemm_kernel(T, Kq // 2, n_out), quant_kernel(wl)
+    gemm_bytes = w_bytes + T * Kqb + T * 8 + T * n_out * 2 + T * N * 2
+    gk, qk = gemm_kernel(T, Kqb, n_out, bits), quant_kernel(wl)
     decode = gk.startswith("gemm_decode")
     traffic = prof.read_traffic(os.path.join(ROOT, "profiles", f"{gk}_{wl.name}_traffic.txt"), gk)
     if decode:
@@ -444,7 +459,7 @@ def main():
         quant["fp64_tflops"] = round(fl / rot_s / 1e12, 2)
         quant["fp64_frac"] = round(fl / rot_s / 1e12 / FP64_PEAK_TFLOPS, 4)
     rec = {
-        "metric": METRIC,
+        "metric": METRIC8 if bits == 8 else METRIC,
         "value": round(ops / step_s / 1e12, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -454,11 +469,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4",
+        "dtype": "int8" if bits == 8 else "int4",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: rotate({wl.rot}) + per-token INT4"
-                               f"{' asymmetric + fp16 outliers' if mixed else ''} + W4A4 linear, "
-                               f"X fp16 [{T},{K}], W int4 [{N},{Kq}]" + (f" + fp16 [{N},{n_out}]" if mixed else ""),
+        "config": {"workload": f"{wl.name}: rotate({wl.rot}) + per-token INT{bits}"
+                               f"{' asymmetric + fp16 outliers' if mixed else ''} + W{bits}A{bits} linear, "
+                               f"X fp16 [{T},{K}], W int{bits} [{N},{Kq}]" + (f" + fp16 [{N},{n_out}]" if mixed else ""),
                    "T": T, "K": K, "N": N, "rotation": wl.rot, "block": wl.block, "n_out": n_out,
                    "clip_x": wl.clip_x, "buffer_sets": S, "footprint_MB": round(footprint / 2**20)},
         "roofline": roof,

@@ -8,11 +8,12 @@
 //
 // One workgroup per row, grid-stride over rows.  At start the workgroup turns
 // the outlier list into a bit mask and, per 8-column chunk, the output offset
-// of its first kept column (a block prefix scan), both in LDS.  Per row, two
-// passes of 16-byte loads over 8-column chunks (the second from L2): masked
-// fp16 min / max (or |x| max) and the block reduction, then codes written
-// byte by byte into an LDS copy of the packed row at their compacted
-// positions, outlier values to x_out, and the row stored with 16-byte writes.
+// of its first kept column (a block prefix scan), both in LDS.  Per row, each
+// of the 1024 threads loads its (at most four) 8-column chunks with 16-byte
+// loads and keeps them for both passes: masked fp16 min / max (or |x| max)
+// and the block reduction, then codes written byte by byte into an LDS copy
+// of the packed row at their compacted positions, outlier values to x_out,
+// and the row stored with 16-byte writes.
 #include "rq_device.h"
 #include "rq_kernels.h"
 
@@ -20,7 +21,8 @@ namespace rq {
 
 namespace {
 
-constexpr int kQ8Threads = 256;
+constexpr int kQ8Threads = 1024;
+constexpr int kQ8MaxChunks = 4;  // 8-column chunks per thread: K <= 32768
 
 // rne(x / s) for s > 0, exactly, whenever |x / s| < 2^22 and x - b s below is
 // either 0 or at least 2^-62 in magnitude (true for fp16 x and the scales made
@@ -62,7 +64,7 @@ struct Q8Args {
 };
 
 template <bool ASYM>
-__global__ __launch_bounds__(kQ8Threads) void split_quant8(Q8Args a) {
+__global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8))) void split_quant8(Q8Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t *mask = reinterpret_cast<uint32_t *>(smem);           // [K / 32] outlier bits
   int32_t *cbase = reinterpret_cast<int32_t *>(smem + a.K / 8);  // [K / 8] first kept position per chunk
@@ -104,14 +106,21 @@ __global__ __launch_bounds__(kQ8Threads) void split_quant8(Q8Args a) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   for (int64_t r = blockIdx.x; r < a.T; r += gridDim.x) {
     const __half *src = a.x + r * a.ldx;
+    // the thread's chunks tid + 1024 i, loaded once (past the end: a clamped
+    // reload, never used)
+    uint4 v[kQ8MaxChunks];
+#pragma unroll
+    for (int i = 0; i < kQ8MaxChunks; ++i)
+      v[i] = *reinterpret_cast<const uint4 *>(src + 8 * min(tid + kQ8Threads * i, a.nch - 1));
     // pass 1: masked min / max of the kept columns (outliers count as 0,
     // which the range [min(x, 0), max(x, 0)] already contains), or |x| max
     h2 mn2 = {0, 0}, mx2 = {0, 0};
-#pragma unroll 4
-    for (int c = tid; c < a.nch; c += kQ8Threads) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(src + 8 * c);
+#pragma unroll
+    for (int i = 0; i < kQ8MaxChunks; ++i) {
+      const int c = tid + kQ8Threads * i;
+      if (c >= a.nch) continue;
       const uint32_t m = cmask(c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t keep = ((m >> (2 * e)) & 1u ? 0u : 0x0000FFFFu) | ((m >> (2 * e + 1)) & 1u ? 0u : 0xFFFF0000u);
@@ -143,14 +152,15 @@ __global__ __launch_bounds__(kQ8Threads) void split_quant8(Q8Args a) {
       lo_c = -127.0f;
       hi_c = 127.0f;
     }
-    // pass 2 (the row again, from L2): codes into the LDS row at their
-    // compacted positions; outlier values to x_out
+    // pass 2: codes into the LDS row at their compacted positions; outlier
+    // values to x_out
     int csum = 0;
-#pragma unroll 2
-    for (int c = tid; c < a.nch; c += kQ8Threads) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(src + 8 * c);
+#pragma unroll
+    for (int i = 0; i < kQ8MaxChunks; ++i) {
+      const int c = tid + kQ8Threads * i;
+      if (c >= a.nch) continue;
       const uint32_t m = cmask(c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       int kpos = cbase[c];
       if (m == 0u) {  // no outlier in the chunk: eight consecutive codes
 #pragma unroll
@@ -225,7 +235,7 @@ hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool 
   a.code_sum = code_sum;
   a.x_out = (__half *)x_out;
   const size_t lds = split8_smem_bytes(K);
-  const dim3 g((unsigned)(T < 2048 ? T : 2048)), b(kQ8Threads);
+  const dim3 g((unsigned)(T < 1024 ? T : 1024)), b(kQ8Threads);
   const void *k = asym ? reinterpret_cast<const void *>(split_quant8<true>)
                        : reinterpret_cast<const void *>(split_quant8<false>);
   if (lds > 48 * 1024) {

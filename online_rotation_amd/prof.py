@@ -42,6 +42,7 @@ KERNEL_SOURCES = {
     "kron64_mfma": ["csrc/kron.hip", "csrc/rq_device.h"],
     "kron_quant": _QUANT,
     "group_quant": ["csrc/kv_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"],
+    "split_quant8": ["csrc/quant8.hip", "csrc/rq_device.h"],
 }
 
 
