@@ -168,7 +168,7 @@ def weight_transform(kind: str, K: int, block: int = 0, p1=None, p2=None, chan_s
 # Quantizers
 # --------------------------------------------------------------------------
 
-def quantize_sym(xr: np.ndarray, clip: float = 1.0, qmax: int = QMAX_SYM4):
+def quantize_sym(xr: np.ndarray, clip=1.0, qmax: int = QMAX_SYM4):
     """Per-row symmetric min-max quantization.
 
     [SQR] Q1/A1: min-max scaling onto +-(2^{N-1}-1), so no clip is needed at
@@ -181,7 +181,7 @@ def quantize_sym(xr: np.ndarray, clip: float = 1.0, qmax: int = QMAX_SYM4):
     Returns (codes int8 [rows, K], scale fp32 [rows], pre-round value fp64).
     """
     xr = np.asarray(xr, np.float64)
-    clip64 = float(np.float32(clip))
+    clip64 = np.asarray(clip, np.float32).astype(np.float64)   # a scalar, or one ratio per row
     amax = np.max(np.abs(xr), axis=1) if xr.shape[1] else np.zeros(xr.shape[0])
     scale = (clip64 * amax / qmax).astype(np.float32)
     s64 = scale.astype(np.float64)[:, None]
@@ -400,6 +400,34 @@ def kv_rotate_quant(x16: np.ndarray, group: int = 128, rotate: bool = True) -> d
     q = q.reshape(T, K)
     return {"q": q, "scale": s.reshape(T, K // group), "zero": z.reshape(T, K // group), "xr": x,
             "pre": pre.reshape(T, K), "zpre": zpre.reshape(T, K // group), "packed": pack_int4(q)}
+
+
+def search_weight_clip(w16: np.ndarray, outlier_idx=None, bits: int = 4, steps: int = 100) -> dict:
+    """QUIK's weight clipping by linear search, per output channel.
+
+    [QUIK] "QUIK量化" part 2: before the weights are quantized, a linear
+    search picks the clipping threshold.  Reading r23: the candidates are the
+    ratios c = k / steps (rounded to fp32), k = steps, steps - 1, ..., 1; each
+    is scored by the squared error sum (w - s_c q_c)^2 of symmetric min-max
+    quantization with s_c = fp32(c * max|w| / qmax) over the row's normal
+    columns (outlier columns stay fp16 and are not clipped), and the first
+    minimum in that order is kept (ties go to the larger ratio).
+
+    Returns clip fp32 [N] and the error table err [N, steps] (column j is
+    k = steps - j).
+    """
+    w = np.asarray(w16, np.float16).astype(np.float64)
+    if outlier_idx is not None and len(outlier_idx):
+        w, _ = split_outliers(w, outlier_idx)
+    qm = code_max(bits, False)
+    ratios = [np.float32(k / steps) for k in range(steps, 0, -1)]
+    err = np.empty((w.shape[0], steps))
+    for j, c in enumerate(ratios):
+        q, s, _ = quantize_sym(w, c, qm)
+        err[:, j] = ((w - s.astype(np.float64)[:, None] * q) ** 2).sum(axis=1)
+    best = np.argmin(err, axis=1)          # first minimum = largest ratio among ties
+    clip = np.array([ratios[j] for j in best], np.float32)
+    return {"clip": clip, "err": err, "ratios": np.array(ratios, np.float32)}
 
 
 def prepare_weights(w16: np.ndarray, kind: str, clip: float = 1.0, outlier_idx=None,

@@ -624,3 +624,64 @@ def test_8bit_lossless_pipeline_and_bounds():
     np.testing.assert_array_equal(acc, o.int_gemm_bruteforce(xq["q"], wq["q"]))
     with pytest.raises(ValueError):
         o.code_max(6, True)
+
+
+# ---------------------------------------------------------------- QUIK clip search
+
+def _bruteforce_clip(row, steps, qmax):
+    """The linear search in exact rational arithmetic, one plain loop per candidate."""
+    xs = [Fraction(float(v)) for v in row]
+    amax = max(abs(x) for x in xs)
+    best, best_err = None, None
+    for k in range(steps, 0, -1):
+        c = np.float32(k / steps)
+        s = _fp32_round(Fraction(float(c)) * amax / qmax)
+        sf = Fraction(float(s))
+        err = Fraction(0)
+        for x in xs:
+            q = 0 if sf == 0 else min(max(_rne(x / sf), -qmax), qmax)
+            err += (x - sf * q) ** 2
+        if best_err is None or err < best_err:
+            best, best_err = c, err
+    return best
+
+
+def test_clip_search_matches_exact_bruteforce():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((4, 24)) * 0.02).astype(np.float16)
+    w[1, 3] = 0.2                                  # one large value: clipping pays
+    w[2] = 0                                       # zero row: every ratio ties, the first (1) stays
+    for bits, qm in ((4, 7), (8, 127)):
+        got = o.search_weight_clip(w, bits=bits, steps=20)["clip"]
+        for n in range(4):
+            assert got[n] == _bruteforce_clip(w[n].astype(np.float64), 20, qm), (bits, n)
+    assert o.search_weight_clip(w, steps=20)["clip"][2] == 1.0
+
+
+def test_clip_search_special_cases_and_invariances():
+    rng = np.random.default_rng(6)
+    # a row already on the c = 1 grid has zero error there, and ties keep 1
+    grid = (rng.integers(-7, 8, (3, 64)) * 2.0 ** -6).astype(np.float16)
+    grid[:, 0] = 7 * 2.0 ** -6
+    assert np.all(o.search_weight_clip(grid)["clip"] == 1.0)
+    # gaussian rows: clipping lowers the error (the choice is below 1 and
+    # strictly better than c = 1)
+    w = (rng.standard_normal((6, 4096)) * 0.02).astype(np.float16)
+    r = o.search_weight_clip(w)
+    assert np.all(r["clip"] < 1.0) and np.all(r["err"].min(axis=1) < r["err"][:, 0])
+    # power-of-two scaling and column permutation leave the choice unchanged
+    assert np.array_equal(o.search_weight_clip((w.astype(np.float64) * 8).astype(np.float16))["clip"], r["clip"])
+    perm = rng.permutation(4096)
+    assert np.array_equal(o.search_weight_clip(w[:, perm])["clip"], r["clip"])
+    # outlier columns take no part: a huge value there changes nothing
+    idx = np.array([5, 900], np.int32)
+    w2 = w.copy()
+    w2[:, idx] = 60.0
+    keep = np.setdiff1d(np.arange(4096), idx)
+    np.testing.assert_array_equal(o.search_weight_clip(w2, outlier_idx=idx)["clip"],
+                                  o.search_weight_clip(w[:, keep])["clip"])
+    # prepare_weights with the chosen per-row ratios equals per-row quantization
+    wq = o.prepare_weights(w, "none", clip=r["clip"])
+    for n in range(6):
+        q1 = o.prepare_weights(w[n:n + 1], "none", clip=float(r["clip"][n]))
+        assert np.array_equal(wq["q"][n], q1["q"][0]) and wq["scale"][n] == q1["scale"][0]
