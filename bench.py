@@ -23,6 +23,11 @@ two calls a few times, for `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` runs.
 the LLaMA-2-70B down projection: T=4096, K=28672, N=8192, 896 fp16 outlier
 columns; rq_w8a8_linear on INT8 matrix cores).
 
+`--weight-prep` (with quik_prefill, quik_decode or quik8_down) times QUIK's
+offline weight side instead: rq_search_weight_clip (the per-channel clip
+ratio by linear search over 100 ratios) and rq_prepare_weights with those
+ratios; the roofline is the search kernel's fp64 error arithmetic.
+
 `--workload kv` measures the KV-cache quantizer instead: one step quantizes
 one attention layer's keys (R3, a 128-point Walsh-Hadamard per head) and
 values, group-wise asymmetric INT4 with groups of 128 channels; the line
@@ -61,6 +66,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--weight-prep", action="store_true",
+                    help="time QUIK's offline weight side instead: clip linear search + per-channel quantization")
     ap.add_argument("--counters", action="store_true",
                     help="launch the calibration kernels and each call a few times, print one line")
     return ap.parse_args()
@@ -283,6 +290,103 @@ def main_kv(args, torch, rq, prof, workloads):
     print(json.dumps(rec), flush=True)
 
 
+FP64_VECTOR_PEAK_TFLOPS = 78.6  # MI355X fp64 vector
+
+
+def main_weight_prep(args, torch, rq, prof, workloads):
+    """QUIK's weight side on the GPU (unrotated workloads): the per-channel
+    clip ratio by linear search over 100 ratios, then per-channel symmetric
+    quantization of the normal columns with those ratios and the outlier
+    split.  One step = both calls on the workload's W."""
+    from oracle import rq_oracle as o
+    dev = torch.device("cuda:0")
+    wl = workloads.get(args.workload)
+    assert wl.rot == "none", "weight-prep timing is for the unrotated (QUIK) workloads"
+    inp = workloads.make_inputs(args.workload)
+    N, K, n_out, bits, steps = wl.N, wl.K, wl.n_out, wl.bits, 100
+    w = torch.from_numpy(inp["w"]).to(dev)
+    idx = torch.from_numpy(inp["outlier_ch"][:n_out].astype(np.int32)).to(dev) if n_out else None
+    clip = torch.empty((N,), dtype=torch.float32, device=dev)
+    wq = {}
+
+    def search():
+        rq.rq_search_weight_clip(w, outlier_idx=idx, bits=bits, steps=steps, out=clip)
+
+    def quant():
+        wq.update(rq.rq_prepare_weights(w, rq.Rotation("none"), outlier_idx=idx, bits=bits, row_clip=clip))
+
+    for _ in range(max(1, args.warmup // 10)):
+        search()
+        quant()
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    reps = max(1, min(args.steps, 10))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        search()
+        quant()
+    e1.record()
+    e1.synchronize()
+    step_s = e0.elapsed_time(e1) / 1e3 / reps
+    search_s = timed(search, reps)
+    quant_s = timed(quant, reps)
+    kint = K - n_out
+    flops = 4.0 * N * kint * steps      # per value and ratio: d = w - s q, d * d + acc, in fp64
+    w_bytes = N * K * 2
+    rec = {
+        "metric": "QUIK weight prep GB/s of fp16 weights (clip linear search over 100 ratios + per-channel quantization)",
+        "value": round(w_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": max(1, args.warmup // 10),
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} weights: W fp16 [{N},{K}], {n_out} fp16 outlier columns, "
+                               f"INT{bits} per channel, {steps} clip ratios", "N": N, "K": K, "n_out": n_out,
+                   "bits": bits, "ratios": steps},
+        "roofline": {"bound": "fp64", "achieved": round(flops / search_s / 1e12, 2),
+                     "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / search_s / 1e12 / FP64_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "clip_search", "flops_per_launch": flops, "avg_launch_us": round(search_s * 1e6, 1),
+                     "note": "4 fp64 flops per value and ratio (the error term); the exact fp32 codes beside them "
+                             "are not counted"},
+        "quantize": {"kernel": "split_quant8" if bits == 8 else "split_quant", "avg_launch_us": round(quant_s * 1e6, 1),
+                     "achieved_GBps": round((w_bytes + N * (kint if bits == 8 else kint // 2)) / quant_s / 1e9, 1)},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        rows = 64
+        t0 = time.perf_counter()
+        runs = 0
+        while True:
+            o.search_weight_clip(inp["w"][:rows], outlier_idx=inp["outlier_ch"][:n_out] if n_out else None,
+                                 bits=bits, steps=steps)
+            runs += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(rows * K * 2 * runs / el / 1e9, 4), "unit": "GB/s", "cores": os.cpu_count(),
+                               "kind": "oracle", "sample": f"{rows} of {N} weight rows, clip search only, "
+                                                           f"{runs} runs in {el:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -298,6 +402,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload == "kv":
         return main_kv(args, torch, rq, prof, workloads)
+    if args.weight_prep:
+        return main_weight_prep(args, torch, rq, prof, workloads)
     dev = torch.device("cuda:0")
     wl = workloads.get(args.workload)
     inp = workloads.make_inputs(args.workload)

@@ -109,6 +109,10 @@ typedef struct {
   const int32_t *outlier_idx;
   int32_t n_out;
   int32_t bits;
+  /* device fp32 [rows] per-row clip ratios in (0, 1], used instead of
+   * clip_ratio (symmetric codes without a rotation only; NULL: clip_ratio);
+   * rq_search_weight_clip writes them. */
+  const float *row_clip;
 } rq_quant_desc;
 
 /* rq_rotate_quant -- online transform + per-token INT4 quantization + packing.
@@ -145,6 +149,24 @@ rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw,
                              const rq_rot_desc *rot, const rq_quant_desc *qd,
                              uint8_t *qw, float *sw, int32_t *w_rowsum, void *w_out,
                              void *workspace, int64_t workspace_bytes, void *stream);
+
+/* rq_search_weight_clip -- QUIK's weight clipping by linear search (QUIK
+ * blog, "QUIK量化" part 2), per output channel.  For each row n of w, the
+ * candidate ratios c = fp32(k / steps), k = steps, ..., 1, are scored by
+ *   err(c) = sum_k (w[n][k] - s_c * q_c[k])^2 over the normal columns,
+ *   s_c = fp32(c * max|w[n][.]| / qmax), q_c = clamp(rne(w / s_c), -qmax, qmax),
+ * qmax = 7 (bits 4) or 127 (bits 8), with the error summed in fp64; the
+ * first minimum in that order (ties to the larger ratio) goes to
+ * clip_out[n].  Pass clip_out as qd->row_clip to rq_prepare_weights.
+ *   w        fp16 [N, ldw], ldw >= K, ldw % 8 == 0, 16-byte aligned
+ *   qd       symmetric (asymmetric == 0); bits; outlier_idx / n_out select
+ *            the fp16 columns, which take no part; clip_ratio, row_clip ignored
+ *   steps    1 .. 100000 (100: ratios 0.01 .. 1.00)
+ *   clip_out out fp32 [N]
+ * K % 32 == 0, K <= 32768.  N == 0 is a no-op. */
+rq_status rq_search_weight_clip(const void *w, int64_t N, int64_t K, int64_t ldw,
+                                const rq_quant_desc *qd, int32_t steps, float *clip_out,
+                                void *stream);
 
 /* rq_w4a4_linear -- y[t][n] = fp16( acc[t][n] * sx[t] * sw[n] ),
  * acc = sum_k qx[t][k] * qw[n][k] in INT32 (QUIK blog part 4), symmetric codes.

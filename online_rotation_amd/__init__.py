@@ -23,14 +23,14 @@ ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_w4a4_gemm_i32", "rq_status_string",
-           "rq_last_error", "rq_abi_version", "EXPORTS"]
+           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
+           "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_w4a4_gemm_i32", "rq_status_string",
-           "rq_last_error", "rq_abi_version")
+           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
+           "rq_status_string", "rq_last_error", "rq_abi_version")
 
 
 class RqError(RuntimeError):
@@ -47,7 +47,8 @@ class _RotDesc(ctypes.Structure):
 
 class _QuantDesc(ctypes.Structure):
     _fields_ = [("asymmetric", ctypes.c_int32), ("clip_ratio", ctypes.c_float),
-                ("outlier_idx", ctypes.c_void_p), ("n_out", ctypes.c_int32), ("bits", ctypes.c_int32)]
+                ("outlier_idx", ctypes.c_void_p), ("n_out", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("row_clip", ctypes.c_void_p)]
 
 
 _lib = None
@@ -77,9 +78,10 @@ def lib() -> ctypes.CDLL:
         L.rq_kv_rotate_quant.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
         L.rq_w8a8_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, vp, i64, vp]
         L.rq_w8a8_gemm_i32.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp, i64, vp]
+        L.rq_search_weight_clip.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), i32, vp, vp]
         for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear", "rq_mixed_outlier_linear",
                    "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_w8a8_linear",
-                   "rq_w8a8_gemm_i32"):
+                   "rq_w8a8_gemm_i32", "rq_search_weight_clip"):
             getattr(L, fn).restype = ctypes.c_int
         L.rq_status_string.argtypes = [ctypes.c_int]
         L.rq_status_string.restype = ctypes.c_char_p
@@ -165,9 +167,9 @@ class Rotation:
                         _ptr(self.p2), _ptr(self.chan_scale))
 
 
-def _qdesc(asym: bool, clip: float, outlier_idx, bits: int = 4):
+def _qdesc(asym: bool, clip: float, outlier_idx, bits: int = 4, row_clip=None):
     n_out = 0 if outlier_idx is None else int(outlier_idx.numel())
-    return _QuantDesc(1 if asym else 0, float(clip), _ptr(outlier_idx), n_out, int(bits)), n_out
+    return _QuantDesc(1 if asym else 0, float(clip), _ptr(outlier_idx), n_out, int(bits), _ptr(row_clip)), n_out
 
 
 def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
@@ -204,16 +206,19 @@ def rq_rotate_quant(x, rot: Rotation, clip: float = 1.0, asym: bool = False,
     return o
 
 
-def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None, bits: int = 4) -> dict:
+def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None, bits: int = 4,
+                       row_clip=None) -> dict:
     """w fp16 [N, K] -> dict(q, scale, rowsum, w_out): rotated, per-channel INT4
-    (bits = 8: INT8, one byte per code, rotation none only)."""
+    (bits = 8: INT8, one byte per code, rotation none only).  row_clip: fp32
+    [N] per-row clip ratios (rotation none), e.g. from rq_search_weight_clip."""
     import torch
-    _gpu(w, outlier_idx, rot.p1, rot.p2, rot.chan_scale)
+    _gpu(w, outlier_idx, rot.p1, rot.p2, rot.chan_scale, row_clip)
     N, K = w.shape
     _want(w, "w", torch.float16, dense=False)
     _want(outlier_idx, "outlier_idx", torch.int32)
+    _want(row_clip, "row_clip", torch.float32, (N,))
     rot.check(K)
-    qd, n_out = _qdesc(False, clip, outlier_idx, bits)
+    qd, n_out = _qdesc(False, clip, outlier_idx, bits, row_clip)
     dev = w.device
     rd = rot.desc()
     ws_bytes = lib().rq_prepare_weights_workspace_bytes(ctypes.byref(rd))
@@ -228,6 +233,22 @@ def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None, bi
     _check(st, "rq_prepare_weights")
     o["_workspace"] = ws   # keep alive until the stream has consumed it
     return o
+
+
+def rq_search_weight_clip(w, outlier_idx=None, bits: int = 4, steps: int = 100, out=None):
+    """QUIK's per-channel clip ratio by linear search: w fp16 [N, K] -> fp32 [N]."""
+    import torch
+    _gpu(w, outlier_idx, out)
+    N, K = w.shape
+    _want(w, "w", torch.float16, dense=False)
+    _want(outlier_idx, "outlier_idx", torch.int32)
+    clip = out if out is not None else torch.empty((N,), dtype=torch.float32, device=w.device)
+    _want(clip, "out", torch.float32, (N,))
+    qd, _ = _qdesc(False, 1.0, outlier_idx, bits)
+    st = lib().rq_search_weight_clip(_ptr(w), N, K, w.stride(0), ctypes.byref(qd), int(steps), _ptr(clip),
+                                     _stream(w.device))
+    _check(st, "rq_search_weight_clip")
+    return clip
 
 
 def rq_w4a4_linear(qx, sx, qw, sw, out=None):

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
 SOURCES = ["rq_api.cpp", "rotate_quant.hip", "kron.hip", "gemm_w4a4.hip", "gemm_ra.hip",
-           "gemm_decode.hip", "kv_quant.hip", "quant8.hip"]
+           "gemm_decode.hip", "kv_quant.hip", "quant8.hip",
+           "clip_search.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code.

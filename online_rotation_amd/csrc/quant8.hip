@@ -54,6 +54,7 @@ struct Q8Args {
   int K, nch;              // columns, 8-column chunks (K / 8)
   int kint;                // K - n_out: codes per row
   float clip;
+  const float *row_clip;   // per-row clip ratios (symmetric), or null
   const int32_t *oidx;
   int n_out;
   uint8_t *q;              // [T, kint]
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
       hi_c = 255.0f;
     } else {
       const float mx = block_reduce(fmaxf((float)mx2[0], (float)mx2[1]), red[1], true);
-      s = (float)((double)a.clip * (double)mx / 127.0);  // the product is exact in fp64
+      const float clip = a.row_clip ? a.row_clip[r] : a.clip;
+      s = (float)((double)clip * (double)mx / 127.0);  // the product is exact in fp64
       inv = s > 0.0f ? 1.0f / s : 0.0f;
       lo_c = -127.0f;
       hi_c = 127.0f;
@@ -217,8 +219,8 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
 size_t split8_smem_bytes(int64_t K) { return (((size_t)(K / 8) + (size_t)(K / 2) + 15) & ~(size_t)15) + (size_t)K; }
 
 hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
-                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
-                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
+                         const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
+                         float *scale, int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
   Q8Args a;
   a.x = (const __half *)x;
   a.T = T;
@@ -227,6 +229,7 @@ hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool 
   a.nch = (int)(K / 8);
   a.kint = (int)(K - n_out);
   a.clip = clip;
+  a.row_clip = row_clip;
   a.oidx = outlier_idx;
   a.n_out = n_out;
   a.q = q;

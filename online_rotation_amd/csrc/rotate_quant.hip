@@ -531,9 +531,9 @@ constexpr int kSplitThreads = 256;
 template <int WPT>
 __global__ __launch_bounds__(kSplitThreads) void split_quant(
     const __half *__restrict__ x, int64_t T, int K, int64_t ldx, int asym, float clip,
-    const int32_t *__restrict__ outlier_idx, int n_out, uint8_t *__restrict__ q,
-    float *__restrict__ scale, int32_t *__restrict__ zero, int32_t *__restrict__ code_sum,
-    __half *__restrict__ x_out) {
+    const float *__restrict__ row_clip, const int32_t *__restrict__ outlier_idx, int n_out,
+    uint8_t *__restrict__ q, float *__restrict__ scale, int32_t *__restrict__ zero,
+    int32_t *__restrict__ code_sum, __half *__restrict__ x_out) {
   constexpr int NW = kSplitThreads * WPT;
   __shared__ uint32_t mask[NW];
   __shared__ int wsum[4];
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     __syncthreads();
     mn = fminf(fminf(redf[0], redf[1]), fminf(redf[2], redf[3]));
     mx = fmaxf(fmaxf(redf[4], redf[5]), fmaxf(redf[6], redf[7]));
-    const RowQuant rqp = row_quant(asym, clip, wave_uniform(mn), wave_uniform(mx));
+    const RowQuant rqp = row_quant(asym, row_clip ? row_clip[t] : clip, wave_uniform(mn), wave_uniform(mx));
     int csum = 0;
 #pragma unroll
     for (int j = 0; j < WPT; ++j)
@@ -698,8 +698,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
 }
 
 hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
-                        const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
-                        int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
+                        const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
+                        float *scale, int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st) {
   const int64_t grid = T < 1024 ? T : 1024;
   const int words = (int)(K / 32);
   const dim3 g((unsigned)grid), b(kSplitThreads);
@@ -707,15 +707,15 @@ hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool a
   __half *xo = (__half *)x_out;
   const int a = asym ? 1 : 0;
   const size_t lds = (size_t)n_out * sizeof(uint16_t);  // the outlier column list
-  void (*k)(const __half *, int64_t, int, int64_t, int, float, const int32_t *, int, uint8_t *, float *,
-            int32_t *, int32_t *, __half *) =
+  void (*k)(const __half *, int64_t, int, int64_t, int, float, const float *, const int32_t *, int, uint8_t *,
+            float *, int32_t *, int32_t *, __half *) =
       words <= kSplitThreads ? split_quant<1> : words <= 2 * kSplitThreads ? split_quant<2> : split_quant<4>;
   if (lds > 32 * 1024) {  // beyond what the static arrays leave of the default 64 KB
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  k<<<g, b, lds, st>>>(xh, T, (int)K, ldx, a, clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
+  k<<<g, b, lds, st>>>(xh, T, (int)K, ldx, a, clip, row_clip, outlier_idx, n_out, q, scale, zero, code_sum, xo);
   return hipGetLastError();
 }
 

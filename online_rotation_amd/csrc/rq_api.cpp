@@ -58,6 +58,9 @@ rq_status check_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq
   if (qd->bits != 0 && qd->bits != 4 && qd->bits != 8) return fail(RQ_EINVAL, "bits=%d must be 4 or 8", qd->bits);
   if (rot->kind < RQ_ROT_NONE || rot->kind > RQ_ROT_KRON) return fail(RQ_EINVAL, "unknown rotation kind %d", rot->kind);
   if (qd->bits == 8 && rot->kind != RQ_ROT_NONE) return fail(RQ_ESHAPE, "8-bit codes are only supported without a rotation");
+  if (qd->row_clip && (rot->kind != RQ_ROT_NONE || qd->asymmetric))
+    return fail(RQ_ESHAPE, "per-row clip ratios are only supported for symmetric codes without a rotation");
+  if (qd->row_clip && !aligned(qd->row_clip, 4)) return fail(RQ_EALIGN, "row_clip must be 4-byte aligned");
   if (rot->kind != RQ_ROT_NONE && qd->n_out) return fail(RQ_ESHAPE, "outlier split is only supported without a rotation");
   if (rot->kind != RQ_ROT_NONE && qd->asymmetric) return fail(RQ_ESHAPE, "asymmetric codes are only supported without a rotation");
   if (rot->kind == RQ_ROT_HADAMARD && !(pow2(K) && K >= 64)) return fail(RQ_ESHAPE, "HADAMARD needs a power-of-two K >= 64 (K=%lld)", (long long)K);
@@ -106,12 +109,12 @@ rq_status run_quant(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_r
     return hip_status(e, "fwht4096_quant launch");
   }
   if (rot->kind == RQ_ROT_NONE && qd->bits == 8) {
-    e = rq::launch_split8(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
+    e = rq::launch_split8(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->row_clip, qd->outlier_idx,
                           qd->n_out, q, scale, zero, code_sum, x_out, st);
     return hip_status(e, "split_quant8 launch");
   }
   if (rot->kind == RQ_ROT_NONE) {
-    e = rq::launch_split(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->outlier_idx,
+    e = rq::launch_split(x, T, K, ldx, qd->asymmetric != 0, qd->clip_ratio, qd->row_clip, qd->outlier_idx,
                          qd->n_out, q, scale, zero, code_sum, x_out, st);
     return hip_status(e, "split_quant launch");
   }
@@ -178,6 +181,24 @@ rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw, c
   return run_quant(w, N, K, ldw, rot, qd, fa, fb, true, qw, sw, nullptr, w_rowsum, w_out, st);
 }
 
+rq_status rq_search_weight_clip(const void *w, int64_t N, int64_t K, int64_t ldw, const rq_quant_desc *qd,
+                                int32_t steps, float *clip_out, void *stream) {
+  if (!qd) return fail(RQ_EINVAL, "the quantizer descriptor is required");
+  if (qd->asymmetric) return fail(RQ_EINVAL, "weights are quantized symmetrically");
+  if (qd->bits != 0 && qd->bits != 4 && qd->bits != 8) return fail(RQ_EINVAL, "bits=%d must be 4 or 8", qd->bits);
+  if (steps < 1 || steps > 100000) return fail(RQ_EINVAL, "steps=%d must be in [1, 100000]", steps);
+  if (N < 0 || K <= 0) return fail(RQ_EINVAL, "need N >= 0, K > 0");
+  if (K % 32 || K > 32768) return fail(RQ_ESHAPE, "K=%lld must be a multiple of 32 and at most 32768", (long long)K);
+  if (qd->n_out < 0 || qd->n_out >= K) return fail(RQ_EINVAL, "n_out=%d out of range", qd->n_out);
+  if (qd->n_out > 0 && (!qd->outlier_idx || !aligned(qd->outlier_idx, 4))) return fail(RQ_EINVAL, "outlier_idx is required (4-byte aligned) with n_out > 0");
+  if (N == 0) return ok();
+  if (!w || !aligned(w, 16)) return fail(RQ_EALIGN, "w is required, 16-byte aligned");
+  if (ldw < K || ldw % 8) return fail(RQ_EALIGN, "ldw=%lld must be >= K and a multiple of 8", (long long)ldw);
+  if (!clip_out || !aligned(clip_out, 4)) return fail(RQ_EALIGN, "clip_out is required, 4-byte aligned");
+  return hip_status(rq::launch_clip_search(w, N, K, ldw, qd->outlier_idx, qd->n_out, qd->bits == 8 ? 8 : 4, steps,
+                                           clip_out, (hipStream_t)stream), "clip search launch");
+}
+
 static rq_status check_gemm(const uint8_t *qx, int64_t T, int64_t K, const uint8_t *qw, int64_t N,
                             const void *out, int64_t ldo, size_t out_elem) {
   if (T < 0 || K <= 0 || N < 1) return fail(RQ_EINVAL, "need T >= 0, K > 0, N >= 1");
@@ -232,6 +253,7 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
   if (!(qd->clip_ratio > 0.0f && qd->clip_ratio <= 1.0f)) return fail(RQ_EINVAL, "clip_ratio must be in (0, 1]");
   if (qd->asymmetric && qd->clip_ratio != 1.0f) return fail(RQ_EINVAL, "asymmetric quantization takes clip_ratio 1");
   if (qd->bits != 0 && qd->bits != 4) return fail(RQ_ESHAPE, "the fused decode form takes 4-bit codes");
+  if (qd->row_clip) return fail(RQ_ESHAPE, "the fused decode form takes one clip ratio");
   if (T > 16) return fail(RQ_ESHAPE, "the fused decode form takes T <= 16 (T=%lld)", (long long)T);
   if (K % 32 || K > 8192 || (K - n_out) % 128)
     return fail(RQ_ESHAPE, "the fused decode form needs K %% 32 == 0, K <= 8192, (K - n_out) %% 128 == 0 (K=%lld)", (long long)K);

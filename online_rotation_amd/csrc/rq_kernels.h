@@ -42,8 +42,8 @@ hipError_t launch_rowlds(const void *x, int64_t T, int64_t K, int64_t ldx, int s
                          float norm, float clip, uint8_t *q, float *scale, int32_t *code_sum,
                          hipStream_t st);
 hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
-                        const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
-                        int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
+                        const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
+                        float *scale, int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
 hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,
                          const float *chan_scale, bool divide, float clip, uint8_t *q, float *scale,
                          int32_t *code_sum, hipStream_t st);
@@ -69,8 +69,11 @@ hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStre
 // quant8.hip: unrotated per-row INT8 with the outlier split
 size_t split8_smem_bytes(int64_t K);
 hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
-                         const int32_t *outlier_idx, int n_out, uint8_t *q, float *scale,
-                         int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
+                         const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
+                         float *scale, int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
+// clip_search.hip: QUIK's per-row weight clip ratio by linear search
+hipError_t launch_clip_search(const void *w, int64_t N, int64_t K, int64_t ldw, const int32_t *outlier_idx,
+                              int n_out, int bits, int steps, float *clip_out, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 
 }  // namespace rq

@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "kron_quant": _QUANT,
     "group_quant": ["csrc/kv_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"],
     "split_quant8": ["csrc/quant8.hip", "csrc/rq_device.h"],
+    "clip_search": ["csrc/clip_search.hip", "csrc/rq_device.h"],
 }
 
 

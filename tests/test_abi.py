@@ -197,3 +197,24 @@ def test_8bit_validation():
     d = L.rq_quant_decode_linear
     assert d(FAKE, 8, 4096, 4096, ctypes.byref(rq._QuantDesc(0, 1.0, None, 0, 8)), FAKE, FAKE, FAKE, 16, None,
              FAKE, 16, None) == rq.RQ_ESHAPE
+
+
+def test_clip_search_and_row_clip_validation():
+    L = rq.lib()
+    f = L.rq_search_weight_clip
+    qd = lambda **kw: ctypes.byref(rq._QuantDesc(kw.get("asym", 0), 1.0, kw.get("idx"), kw.get("n_out", 0),
+                                                 kw.get("bits", 4), kw.get("rc")))
+    assert f(FAKE, 0, 4096, 4096, qd(), 100, FAKE, None) == rq.RQ_OK            # N == 0
+    assert f(FAKE, 8, 4096, 4096, qd(asym=1), 100, FAKE, None) == rq.RQ_EINVAL  # asymmetric weights
+    assert f(FAKE, 8, 4096, 4096, qd(), 0, FAKE, None) == rq.RQ_EINVAL          # steps
+    assert f(FAKE, 8, 4096, 4096, qd(bits=6), 100, FAKE, None) == rq.RQ_EINVAL
+    assert f(FAKE, 8, 4100, 4104, qd(), 100, FAKE, None) == rq.RQ_ESHAPE        # K % 32
+    assert f(FAKE, 8, 4096, 4096, qd(n_out=32), 100, FAKE, None) == rq.RQ_EINVAL  # outliers without a list
+    assert f(FAKE, 8, 4096, 4096, qd(), 100, None, None) == rq.RQ_EALIGN
+    # per-row clip ratios: symmetric codes without a rotation only
+    rc = rq._QuantDesc(0, 1.0, None, 0, 4, FAKE)
+    assert _rotate_quant(4, 4096, 4096, _rot("hadamard"), rc) == rq.RQ_ESHAPE
+    assert _rotate_quant(4, 4096, 4096, _rot("none"), rq._QuantDesc(1, 1.0, None, 0, 4, FAKE)) == rq.RQ_ESHAPE
+    assert _rotate_quant(4, 4096, 4096, _rot("none"), rq._QuantDesc(0, 1.0, None, 0, 4, FAKE + 2)) == rq.RQ_EALIGN
+    d = L.rq_quant_decode_linear
+    assert d(FAKE, 8, 4096, 4096, ctypes.byref(rc), FAKE, FAKE, FAKE, 16, None, FAKE, 16, None) == rq.RQ_ESHAPE

@@ -819,3 +819,80 @@ def test_quik8_full_size_sampled():
     assert np.array_equal(host(xq["zero"])[ts], xr["zero"]) and np.array_equal(host(xq["scale"])[ts], xr["scale"])
     assert np.array_equal(host(wq["q"])[ns], wr["packed"]) and np.array_equal(host(wq["rowsum"])[ns], wr["rowsum"])
     check_y(host(y)[np.ix_(ts, ns)], o.linear(xr, wr)["y"])
+
+
+# ----------------------------------------------------------------------------- QUIK clip search
+
+def _check_clip_choice(clip_gpu, ref, what="clip"):
+    """The GPU's ratio is the oracle's, or ties with it: the oracle's error at
+    the GPU's ratio is within 1e-12 (relative) of the minimum.  (The GPU sums
+    the same fp64 terms in another order.)"""
+    clip_gpu = np.asarray(clip_gpu)
+    diff = clip_gpu != ref["clip"]
+    for n in np.flatnonzero(diff):
+        j = int(np.flatnonzero(ref["ratios"] == clip_gpu[n])[0])
+        best = ref["err"][n].min()
+        assert ref["err"][n, j] <= best * (1 + 1e-12) + 1e-300, f"{what}: row {n} picked {clip_gpu[n]}"
+    return int(diff.sum())
+
+
+CLIP_CASES = [
+    # name, workload, N, K, n_out, bits, steps
+    ("4bit-outliers", "quik_prefill", 300, 1024, 32, 4, 100),
+    ("8bit-outliers", "quik8_down", 70, 2048, 64, 8, 100),
+    ("4bit-odd-steps", "llama7b", 41, 4096, 0, 4, 7),
+    ("4bit-one-step", "llama7b", 5, 512, 0, 4, 1),
+    ("8bit-width-32768", "quik8_down", 3, 32768, 0, 8, 100),
+]
+
+
+@pytest.mark.parametrize("case", CLIP_CASES, ids=[c[0] for c in CLIP_CASES])
+def test_clip_search_matches_oracle(case):
+    name, wl, N, K, n_out, bits, steps = case
+    note(f"[clip search] {name} N={N} K={K} n_out={n_out} bits={bits} steps={steps}")
+    inp = workloads.make_inputs(wl, T=4, K=K, N=N)
+    w = inp["w"].copy()
+    w[1] = 0                                          # zero row: ratio 1
+    qm = 127 if bits == 8 else 7
+    w[2, :] = (np.arange(K) % (2 * qm + 1) - qm) * 2.0 ** -10   # on the c = 1 grid: ratio 1
+    idx = inp["outlier_ch"][:n_out].astype(np.int32) if n_out else None
+    ref = o.search_weight_clip(w, outlier_idx=idx, bits=bits, steps=steps)
+    clip = rq.rq_search_weight_clip(dev(w), outlier_idx=None if idx is None else dev(idx), bits=bits, steps=steps)
+    torch.cuda.synchronize()
+    _check_clip_choice(host(clip), ref)
+    assert host(clip)[1] == 1.0 and host(clip)[2] == 1.0
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_prepare_weights_with_searched_clip(bits):
+    """Weight prep with the searched per-row ratios equals the oracle's
+    prepare_weights at those ratios (bit-exact at 8 bits; at 4 bits within
+    the quantizer tolerance, whose fp32 scale rounding differs)."""
+    wl = "quik8_down" if bits == 8 else "quik_prefill"
+    note(f"[prepare_weights searched clip] bits={bits}")
+    inp = workloads.make_inputs(wl, T=4, K=2048, N=150)
+    w, idx = inp["w"], inp["outlier_ch"][:64].astype(np.int32)
+    clip = rq.rq_search_weight_clip(dev(w), outlier_idx=dev(idx), bits=bits)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=dev(idx), bits=bits, row_clip=clip)
+    torch.cuda.synchronize()
+    ref = o.prepare_weights(w, "none", clip=host(clip), outlier_idx=idx, bits=bits)
+    assert np.any(host(clip) < 1.0)   # gaussian rows: clipping pays (at 8 bits, not on every row)
+    if bits == 8:
+        assert np.array_equal(host(wq["q"]), ref["packed"]) and np.array_equal(host(wq["scale"]), ref["scale"])
+        assert np.array_equal(host(wq["rowsum"]), ref["rowsum"])
+    else:
+        check_sym_quant(host(wq["q"]), host(wq["scale"]), ref, what="w")
+    assert np.array_equal(host(wq["w_out"]), ref["w_out"])
+
+
+def test_clip_search_full_size_sampled():
+    """QUIK's 4-bit weight side at full size: W [28672, 8192] with 256 outlier
+    columns (the quik_prefill workload), sampled rows against the oracle."""
+    inp = workloads.make_inputs("quik_prefill")
+    w, idx = inp["w"], inp["outlier_ch"].astype(np.int32)
+    note(f"[clip search full size] w {w.shape}")
+    clip = rq.rq_search_weight_clip(dev(w), outlier_idx=dev(idx))
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, w.shape[0] - 1, np.random.default_rng(3).choice(w.shape[0], 30, replace=False)])
+    ref = o.search_weight_clip(w[rows], outlier_idx=idx)
+    _check_clip_choice(host(clip)[rows], ref)
