@@ -33,6 +33,16 @@ __device__ __forceinline__ float cs_rne_div(float x, float s, float inv) {
   return __builtin_rintf(b + __builtin_amdgcn_fmed3f(d * 0x1p64f, -0.25f, 0.25f));
 }
 
+// The fp32 neighbours lo <= 1/s <= hi; where the two magic-number products
+// x*lo and x*hi round to the same integer, it is rne(x / s) (they bracket
+// it); elsewhere cs_rne_div decides.
+__device__ __forceinline__ void cs_bracket(float s, float inv, float &lo, float &hi) {
+  const float e = __builtin_fmaf(-s, inv, 1.0f);
+  lo = hi = inv;
+  if (e > 0.0f) hi = __uint_as_float(__float_as_uint(inv) + 1u);
+  if (e < 0.0f) lo = __uint_as_float(__float_as_uint(inv) - 1u);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -94,13 +104,14 @@ __global__ __launch_bounds__(kCsThreads) void clip_search(CsArgs a) {
     bool have = false;
     for (int k0 = a.steps; k0 >= 1; k0 -= kCsBatch) {
       double e[kCsBatch];
-      float cb[kCsBatch], sb[kCsBatch], ib[kCsBatch];
+      float cb[kCsBatch], sb[kCsBatch], ib[kCsBatch], lb[kCsBatch], hb[kCsBatch];
 #pragma unroll
       for (int b = 0; b < kCsBatch; ++b) {
         const int k = max(k0 - b, 1);
         cb[b] = (float)((double)k / (double)a.steps);
         sb[b] = (float)((double)cb[b] * (double)amax / (double)QMAX);
         ib[b] = sb[b] > 0.0f ? 1.0f / sb[b] : 0.0f;
+        cs_bracket(sb[b], ib[b], lb[b], hb[b]);
         e[b] = 0.0;
       }
 #pragma unroll 2
@@ -111,9 +122,10 @@ __global__ __launch_bounds__(kCsThreads) void clip_search(CsArgs a) {
           const float xv = h ? f.y : f.x;
 #pragma unroll
           for (int b = 0; b < kCsBatch; ++b) {
-            const float q = sb[b] > 0.0f
-                                ? __builtin_amdgcn_fmed3f(cs_rne_div(xv, sb[b], ib[b]), -(float)QMAX, (float)QMAX)
-                                : 0.0f;
+            const float ma = __builtin_fmaf(xv, lb[b], 12582912.0f), mb = __builtin_fmaf(xv, hb[b], 12582912.0f);
+            float r = ma - 12582912.0f;
+            if (ma != mb) r = cs_rne_div(xv, sb[b], ib[b]);
+            const float q = sb[b] > 0.0f ? __builtin_amdgcn_fmed3f(r, -(float)QMAX, (float)QMAX) : 0.0f;
             const double d = (double)xv - (double)sb[b] * (double)q;
             e[b] = __builtin_fma(d, d, e[b]);
           }

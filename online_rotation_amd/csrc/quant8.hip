@@ -13,7 +13,9 @@
 // loads and keeps them for both passes: masked fp16 min / max (or |x| max)
 // and the block reduction, then codes written byte by byte into an LDS copy
 // of the packed row at their compacted positions, outlier values to x_out,
-// and the row stored with 16-byte writes.
+// and the row stored with 16-byte writes.  Codes come from two magic-number
+// products (recip_bracket below); the exact boundary test runs only where
+// they disagree.
 #include "rq_device.h"
 #include "rq_kernels.h"
 
@@ -36,6 +38,20 @@ __device__ __forceinline__ float rne_div(float x, float s, float inv) {
   const float d = __builtin_fmaf(-b, s, x);
   return __builtin_rintf(b + __builtin_amdgcn_fmed3f(d * 0x1p64f, -0.25f, 0.25f));
 }
+
+// The fp32 neighbours lo <= 1/s <= hi (equal when 1/s is exact).  The
+// magic-number products x*lo and x*hi, each rounded once to an integer,
+// bracket rne(x / s); where they agree that integer is rne(x / s) exactly,
+// and only where they differ (x / s within about 2^-23 of a half-integer)
+// does rne_div decide.
+__device__ __forceinline__ void recip_bracket(float s, float inv, float &lo, float &hi) {
+  const float e = __builtin_fmaf(-s, inv, 1.0f);  // sign of 1/s - inv, exact
+  lo = hi = inv;
+  if (e > 0.0f) hi = __uint_as_float(__float_as_uint(inv) + 1u);
+  if (e < 0.0f) lo = __uint_as_float(__float_as_uint(inv) - 1u);
+}
+
+constexpr float kQ8Magic = 12582912.0f;  // 1.5 * 2^23: fma(x, r, kQ8Magic) - kQ8Magic = rne(x * r)
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
   v = is_max ? wave_max(v) : wave_min(v);
@@ -156,6 +172,15 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
     }
     // pass 2: codes into the LDS row at their compacted positions; outlier
     // values to x_out
+    float rlo = 0.0f, rhi = 0.0f;
+    if (s > 0.0f) recip_bracket(s, inv, rlo, rhi);
+    // rne(x / s) + zero point, clamped; s == 0 (a zero range) gives 0
+    auto code_of = [&](float f) {
+      const float a = __builtin_fmaf(f, rlo, kQ8Magic), b = __builtin_fmaf(f, rhi, kQ8Magic);
+      float r = a - kQ8Magic;
+      if (a != b) r = rne_div(f, s, inv);
+      return (int)__builtin_amdgcn_fmed3f(s > 0.0f ? r + zf : 0.0f, lo_c, hi_c);
+    };
     int csum = 0;
 #pragma unroll
     for (int i = 0; i < kQ8MaxChunks; ++i) {
@@ -168,8 +193,7 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float2 f2 = __half22float2(*reinterpret_cast<const __half2 *>(&w[e >> 1]));
-          const float f = (e & 1) ? f2.y : f2.x;
-          const int ci = (int)__builtin_amdgcn_fmed3f(s > 0.0f ? rne_div(f, s, inv) + zf : 0.0f, lo_c, hi_c);
+          const int ci = code_of((e & 1) ? f2.y : f2.x);
           csum += ci;
           if (kpos + e < a.kint) row[kpos + e] = (uint8_t)ci;
         }
@@ -182,8 +206,7 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
             if (opos < a.n_out) reinterpret_cast<uint16_t *>(a.x_out)[r * a.n_out + opos] = (uint16_t)bits;
             ++opos;
           } else {
-            const float f = __half2float(__ushort_as_half((unsigned short)bits));
-            const int ci = (int)__builtin_amdgcn_fmed3f(s > 0.0f ? rne_div(f, s, inv) + zf : 0.0f, lo_c, hi_c);
+            const int ci = code_of(__half2float(__ushort_as_half((unsigned short)bits)));
             csum += ci;
             if (kpos < a.kint) row[kpos] = (uint8_t)ci;
             ++kpos;
