@@ -896,3 +896,43 @@ def test_clip_search_full_size_sampled():
     rows = np.unique(np.r_[0, w.shape[0] - 1, np.random.default_rng(3).choice(w.shape[0], 30, replace=False)])
     ref = o.search_weight_clip(w[rows], outlier_idx=idx)
     _check_clip_choice(host(clip)[rows], ref)
+
+
+def test_8bit_quantizer_and_clip_search_strided_rows():
+    """Row strides above K (ldx = K + 64) through the 8-bit quantizer, the clip
+    search and the weight prep with searched ratios."""
+    note("[8-bit / clip search] strided rows")
+    inp = workloads.make_inputs("quik8_down", T=9, K=2048, N=11)
+    x, w, idx = inp["x"], inp["w"], inp["outlier_ch"][:64].astype(np.int32)
+    bx = np.zeros((9, 2048 + 64), np.float16)
+    bx[:, :2048] = x
+    bw = np.zeros((11, 2048 + 64), np.float16)
+    bw[:, :2048] = w
+    xt, wt = dev(bx)[:, :2048], dev(bw)[:, :2048]
+    assert xt.stride(0) == 2112 and wt.stride(0) == 2112
+    xq = rq.rq_rotate_quant(xt, rq.Rotation("none"), asym=True, outlier_idx=dev(idx), bits=8)
+    clip = rq.rq_search_weight_clip(wt, outlier_idx=dev(idx), bits=8)
+    wq = rq.rq_prepare_weights(wt, rq.Rotation("none"), outlier_idx=dev(idx), bits=8, row_clip=clip)
+    torch.cuda.synchronize()
+    xr = o.rotate_quant(x, "none", asym=True, outlier_idx=idx, bits=8)
+    assert np.array_equal(host(xq["q"]), xr["packed"]) and np.array_equal(host(xq["x_out"]), xr["x_out"])
+    _check_clip_choice(host(clip), o.search_weight_clip(w, outlier_idx=idx, bits=8))
+    wr = o.prepare_weights(w, "none", clip=host(clip), outlier_idx=idx, bits=8)
+    assert np.array_equal(host(wq["q"]), wr["packed"]) and np.array_equal(host(wq["scale"]), wr["scale"])
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 33])
+def test_w8a8_linear_decode_sizes(T):
+    """Decode-sized batches through the 8-bit linear layer (the 256-row tile
+    kernel with clamped rows), the full down-projection width."""
+    note(f"[w8a8_linear] decode T={T}")
+    inp = workloads.make_inputs("quik8_down", T=T, K=28672, N=130)
+    x, w, idx = inp["x"], inp["w"], inp["outlier_ch"].astype(np.int32)
+    xr = o.rotate_quant(x, "none", asym=True, outlier_idx=idx, bits=8)
+    wr = o.prepare_weights(w, "none", outlier_idx=idx, bits=8)
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=dev(idx), bits=8)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=dev(idx), bits=8)
+    y = rq.rq_w8a8_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"], wq["rowsum"],
+                          xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    check_y(host(y), o.linear(xr, wr)["y"])
