@@ -143,6 +143,42 @@ def test_gsr_is_block_local():
         o.gsr_rotation(100, 64)
 
 
+def _butterfly_fwht(x):
+    """Radix-2 fast Walsh-Hadamard transform in fp64, rows of x, no matrix:
+    log2(n) stages of (a, b) -> (a + b, a - b) on pairs h apart, then 1/sqrt(n)."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        v = y.reshape(y.shape[0], n // (2 * h), 2, h)
+        a = v[:, :, 0, :].copy()
+        b = v[:, :, 1, :].copy()
+        v[:, :, 0, :] = a + b
+        v[:, :, 1, :] = a - b
+        h *= 2
+    return y / math.sqrt(n)
+
+
+def test_butterfly_fwht_cross_checks_the_dense_rotations():
+    """The oracle rotates by a dense matrix product; an independent fast
+    transform on the same rows must agree to fp64 rounding: the full 4096-point
+    transform, and the 64-point block transform reordered by sequency
+    (s -> bitrev(gray(s))) for the GSR form."""
+    rng = np.random.default_rng(11)
+    K = 4096
+    x = rng.standard_normal((6, K))
+    x[:, rng.choice(K, 16, replace=False)] *= 40.0
+    ref = x @ o.rotation("hadamard", K)
+    np.testing.assert_allclose(_butterfly_fwht(x), ref, rtol=0, atol=1e-11 * np.abs(x).max())
+
+    g = 64
+    perm = np.array([_bitrev(s ^ (s >> 1), 6) for s in range(g)])
+    blocks = _butterfly_fwht(x.reshape(-1, g)).reshape(x.shape[0], K // g, g)
+    fast = blocks[:, :, perm].reshape(x.shape)
+    np.testing.assert_allclose(fast, x @ o.rotation("gsr", K, block=g), rtol=0,
+                               atol=1e-12 * np.abs(x).max())
+
+
 # ---------------------------------------------------------------- Kronecker affine
 
 def test_kron_matches_elementwise_definition_and_matrix_form():
