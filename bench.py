@@ -28,6 +28,10 @@ offline weight side instead: rq_search_weight_clip (the per-channel clip
 ratio by linear search over 100 ratios) and rq_prepare_weights with those
 ratios; the roofline is the search kernel's fp64 error arithmetic.
 
+`--sweep` adds the quantizer alone at 16K and 64K tokens (the batch's rows
+repeated) to the line, under rotate_quant.sweep; it is off by default so
+that a kernel trace of the default run holds one launch shape per kernel.
+
 `--workload kv` measures the KV-cache quantizer instead: one step quantizes
 one attention layer's keys (R3, a 128-point Walsh-Hadamard per head) and
 values, group-wise asymmetric INT4 with groups of 128 channels; the line
@@ -65,6 +69,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled per step (0: >640 MB)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the quantizer alone at 16K and 64K tokens (rotate_quant.sweep)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--weight-prep", action="store_true",
                     help="time QUIK's offline weight side instead: clip linear search + per-channel quantization")
@@ -97,14 +103,48 @@ def quant_kernel(wl):
     return "split_quant" if wl.rot == "none" else "rowlds_quant"
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def oracle_leg(fn, seconds, per_run, unit, sample):
+    """Times fn (one oracle run over the sample) twice: with every BLAS thread,
+    then limited to one thread; each leg repeats fn for about `seconds`.
+    `value` is the all-threads rate (per_run units per run, divided by 1e9 or
+    1e12 for GB/s or TOPS); `cores` is the BLAS thread count of that leg."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    scale = 1e12 if unit == "TOPS" else 1e9
+
+    def leg():
+        runs = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return runs, el
+
+    cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    runs, el = leg()
+    with threadpool_limits(limits=1):
+        runs1, el1 = leg()
+    return {"value": per_run * runs / el / scale, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "value_1core": per_run * runs1 / el1 / scale, "nproc": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model(),
+            "sample": f"{sample}; {runs} runs in {el:.1f} s on {cores} threads, {runs1} runs in {el1:.1f} s on 1"}
+
+
 def cpu_baseline(inp, wl, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     from oracle import rq_oracle as o
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     kind = wl.rot
     kw = {"block": wl.block} if kind == "gsr" else {}
     if kind == "kron":
@@ -113,19 +153,14 @@ def cpu_baseline(inp, wl, seconds):
     wq = o.prepare_weights(inp["w"], kind, outlier_idx=idx, bits=wl.bits, **kw)   # offline side, untimed
     ts = min(256, inp["x"].shape[0])
     xs = inp["x"][:ts]
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def run():
         xq = o.rotate_quant(xs, kind, clip=wl.clip_x, asym=wl.asym, outlier_idx=idx, bits=wl.bits, **kw)
         o.linear(xq, wq)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    ops = 2.0 * ts * wl.N * wl.K * runs
-    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"{ts} of {inp['x'].shape[0]} tokens of the {wl.name} workload (full K={wl.K}, N={wl.N}), "
-                      f"rotate+quantize+INT GEMM+dequant, {runs} runs in {el:.1f} s; weight prep untimed"}
+
+    return oracle_leg(run, seconds, 2.0 * ts * wl.N * wl.K, "TOPS",
+                      f"{ts} of {inp['x'].shape[0]} tokens of the {wl.name} workload (full K={wl.K}, N={wl.N}), "
+                      f"rotate+quantize+INT GEMM+dequant; weight prep untimed")
 
 
 KV_METRIC = "KV-cache quantizer GB/s (R3 on keys + group-wise asymmetric INT4 of keys and values), % HBM roofline"
@@ -140,26 +175,16 @@ def kv_bytes(T, K, g):
 def cpu_baseline_kv(inp, wl, seconds):
     """The oracle on a bounded sample of the kv workload's tokens."""
     from oracle import rq_oracle as o
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     ts = min(256, inp["x"].shape[0])
     xs, vs = inp["x"][:ts], inp["v"][:ts]
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def run():
         o.kv_rotate_quant(xs, group=wl.block, rotate=True)
         o.kv_rotate_quant(vs, group=wl.block, rotate=False)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    nbytes = 2 * kv_bytes(ts, wl.K, wl.block) * runs
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{ts} of {inp['x'].shape[0]} tokens of the kv workload (keys with R3, values without, "
-                      f"4096 channels, g={wl.block}), {runs} runs in {el:.1f} s"}
+
+    return oracle_leg(run, seconds, 2 * kv_bytes(ts, wl.K, wl.block), "GB/s",
+                      f"{ts} of {inp['x'].shape[0]} tokens of the kv workload (keys with R3, values without, "
+                      f"{wl.K} channels, g={wl.block})")
 
 
 def main_kv(args, torch, rq, prof, workloads):
@@ -372,19 +397,67 @@ def main_weight_prep(args, torch, rq, prof, workloads):
     }
     if not args.no_cpu_baseline:
         rows = 64
-        t0 = time.perf_counter()
-        runs = 0
-        while True:
-            o.search_weight_clip(inp["w"][:rows], outlier_idx=inp["outlier_ch"][:n_out] if n_out else None,
-                                 bits=bits, steps=steps)
-            runs += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        el = time.perf_counter() - t0
-        rec["cpu_baseline"] = {"value": round(rows * K * 2 * runs / el / 1e9, 4), "unit": "GB/s", "cores": os.cpu_count(),
-                               "kind": "oracle", "sample": f"{rows} of {N} weight rows, clip search only, "
-                                                           f"{runs} runs in {el:.1f} s"}
+        oidx = inp["outlier_ch"][:n_out] if n_out else None
+        rec["cpu_baseline"] = oracle_leg(
+            lambda: o.search_weight_clip(inp["w"][:rows], outlier_idx=oidx, bits=bits, steps=steps),
+            args.cpu_seconds, rows * K * 2, "GB/s", f"{rows} of {N} weight rows, clip search only")
     print(json.dumps(rec), flush=True)
+
+
+def quant_sweep(torch, rq, x0, rot, wl, idx, bits, Kqb, n_out, reps, stream):
+    """The workload's quantizer alone at larger token counts (16K and 64K
+    tokens: rows of the batch repeated, so the distribution is the same):
+    per-launch time from a graph of back-to-back launches over buffer sets
+    totalling more than 640 MB, median of `reps` replays."""
+    dev = x0.device
+    T0, K = x0.shape
+    mixed = wl.asym
+    out = []
+    for T in (16384, 65536):
+        if T <= T0 or T % T0:
+            continue
+        per = T * K * 2 + T * Kqb + T * 8 + T * n_out * 2
+        S = max(2, -(-(640 << 20) // per))
+        xs = [x0.repeat(T // T0, 1) for _ in range(S)]
+        qs = [{"q": torch.empty((T, Kqb), dtype=torch.uint8, device=dev),
+               "scale": torch.empty((T,), dtype=torch.float32, device=dev),
+               "zero": torch.empty((T,), dtype=torch.int32, device=dev) if mixed else None,
+               "x_out": torch.empty((T, n_out), dtype=torch.float16, device=dev) if mixed else None}
+              for _ in range(S)]
+
+        def call(i):
+            rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, asym=mixed, outlier_idx=idx, out=qs[i], bits=bits)
+
+        for i in range(S):
+            call(i)
+        torch.cuda.synchronize()
+        n = max(S, 8)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for j in range(n):
+                    call(j % S)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                ev0.record(stream)
+                g.replay()
+                ev1.record(stream)
+            ev1.synchronize()
+            times.append(ev0.elapsed_time(ev1) / 1e3 / n)
+        sec = float(np.median(times))
+        nbytes = T * K * 2 + T * Kqb + T * 4 + (T * 4 + T * n_out * 2 if mixed else 0)
+        out.append({"T": T, "avg_launch_us": round(sec * 1e6, 2), "achieved_GBps": round(nbytes / sec / 1e9, 1),
+                    "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "buffer_sets": S})
+        del g, xs, qs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -586,6 +659,11 @@ def main():
         "rotate_quant": quant,
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.sweep and T >= 2048:
+        del xs, wqs, xq, ys, g_step, g_rot, g_gemm
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rec["rotate_quant"]["sweep"] = quant_sweep(torch, rq, x0, rot, wl, idx, bits, Kqb, n_out, args.reps, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -395,6 +395,45 @@ def test_rotate_quant_several_tokens_per_wavefront(T, kind, block, clip):
     check_sym_quant(host(xq["q"])[ts], host(xq["scale"])[ts], xr)
 
 
+@pytest.mark.parametrize("T", [16384, 65536])
+@pytest.mark.parametrize("name", ["llama7b", "gsr", "flat", "quik_prefill", "quik8_down"])
+def test_rotate_quant_large_token_counts_sampled(name, T):
+    """The quantizer at the benchmark's 16K and 64K token sweep in its launch
+    configuration (up to 32 tokens per wavefront for the 4096-point transform,
+    many rows per workgroup for the others): the workload's rows repeated, each
+    copy scaled by its own factor so that a row written to the wrong place
+    fails; sampled rows against the oracle."""
+    note(f"[rotate_quant sweep] {name} T={T}")
+    wl = workloads.get(name)
+    inp = workloads.make_inputs(name, with_weights=False)
+    x0 = inp["x"]
+    T0 = x0.shape[0]
+    x = np.concatenate([x0 * np.float16(1.0 + r / 64.0) for r in range(T // T0)])
+    assert np.isfinite(x).all()
+    rng = np.random.default_rng(T + T0)
+    ts = np.unique(np.concatenate([[0, 1, 31, 32, 33, T0 - 1, T0, 2047, 2048, T - 33, T - 2, T - 1],
+                                   rng.choice(T, 36, replace=False)]))
+    kind, block = wl.rot, wl.block
+    idx = inp["outlier_ch"].astype(np.int32) if wl.asym else None
+    ref = o.rotate_quant(x[ts], kind, clip=wl.clip_x, asym=wl.asym, outlier_idx=idx, bits=wl.bits,
+                         **_rot_args(kind, block, inp))
+    out = rq.rq_rotate_quant(dev(x), _gpu_rot(kind, block, inp), clip=wl.clip_x, asym=wl.asym,
+                             outlier_idx=None if idx is None else dev(idx), bits=wl.bits)
+    torch.cuda.synchronize()
+    del x
+    sel = torch.from_numpy(ts).cuda()
+    q, s = host(out["q"][sel]), host(out["scale"][sel])
+    if wl.bits == 8:
+        assert np.array_equal(q, ref["packed"]) and np.array_equal(s, ref["scale"])
+        assert np.array_equal(host(out["zero"][sel]), ref["zero"])
+    elif wl.asym:
+        check_asym_quant(q, s, host(out["zero"][sel]), ref)
+    else:
+        check_sym_quant(q, s, ref)
+    if idx is not None:
+        assert np.array_equal(host(out["x_out"][sel]), ref["x_out"])
+
+
 @pytest.mark.parametrize("wl", ["quik_prefill", "quik_decode"])
 def test_full_size_quik_sampled(wl):
     note(f"[full] {wl}")
