@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
   auto load = [&](uint4 *r, int64_t t, int32_t gc) {
     const __half *src = a.x + t * a.ldx + (int64_t)gc * G + 8 * sub;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) r[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
+    for (int c = 0; c < NC; ++c) r[c] = load_nt(src + 32 * c);
   };
 
   // Cross-lane butterflies store sigma * value with sigma = (-1)^popcount(sub),
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
     if (valid) {
       uint32_t *dst = reinterpret_cast<uint32_t *>(a.q + t * (a.gpr * (int64_t)(G / 2)) + (int64_t)gc * (G / 2)) + sub;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) dst[4 * c] = wd[c];
+      for (int c = 0; c < NC; ++c) store_nt(dst + 4 * c, wd[c]);
       if (sub == 0) {
         const int64_t gi = t * a.gpr + gc;
         a.scale[gi] = rq.s;

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
     uint4 v[kQ8MaxChunks];
 #pragma unroll
     for (int i = 0; i < kQ8MaxChunks; ++i)
-      v[i] = *reinterpret_cast<const uint4 *>(src + 8 * min(tid + kQ8Threads * i, a.nch - 1));
+      v[i] = load_nt(src + 8 * min(tid + kQ8Threads * i, a.nch - 1));
     // pass 1: masked min / max of the kept columns (outliers count as 0,
     // which the range [min(x, 0), max(x, 0)] already contains), or |x| max
     h2 mn2 = {0, 0}, mx2 = {0, 0};
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
     __syncthreads();
     uint8_t *dst = a.q + r * (int64_t)a.kint;
     for (int o = 16 * tid; o < a.kint; o += 16 * kQ8Threads)
-      *reinterpret_cast<uint4 *>(dst + o) = *reinterpret_cast<const uint4 *>(row + o);
+      store_nt(dst + o, *reinterpret_cast<const uint4 *>(row + o));
     __syncthreads();
   }
 }

@@ -636,7 +636,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
   __syncthreads();
 
   // A row's 16-byte chunks; inactive words reload the thread's last active
-  // word (their keep masks are zero), so the loads hold no branch.
+  // word (their keep masks are zero), so the loads hold no branch.  Cached
+  // loads: the outlier gather below re-reads the row from L2 (with
+  // nontemporal loads it went to HBM and the kernel ran 30% slower).
   auto load_row = [&](uint4 (&u)[WPT][4], int64_t t) {
     const __half *row = x + t * ldx;
 #pragma unroll
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
     __syncthreads();
     uint8_t *qrow = q + t * (int64_t)(Kn / 2);
     for (int i = tid; i < nwords; i += kSplitThreads) {
-      reinterpret_cast<uint32_t *>(qrow)[i] = packed[i];
+      store_nt(reinterpret_cast<uint32_t *>(qrow) + i, packed[i]);
       packed[i] = 0u;
     }
     if (tid == 0) {

@@ -16,6 +16,18 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
+// Streaming accesses for data touched once (the quantizers' input rows and
+// output codes): nontemporal 16-byte loads and 4- / 16-byte stores.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+  const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(void *p, uint4 v) {
+  __builtin_nontemporal_store((v4u32){v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 // Orders this wave's earlier LDS writes before its later LDS reads (the wave
 // works alone on its LDS slice, so no workgroup barrier is involved).
 __device__ __forceinline__ void wave_lds_sync() {
