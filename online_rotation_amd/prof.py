@@ -15,6 +15,15 @@
       The record carries the SHA-256 of the kernel's sources, so that a
       reader can tell when the kernel has changed since the counters were
       taken.
+
+  python -m online_rotation_amd.prof sq DIR [DIR ...] --kernel NAME [--match SUBSTR]
+         [--mfma-ops N] [--workload W] [--command CMD ...] [--out FILE]
+      SQ counters of kernel NAME from one or more `rocprofv3 --pmc SQ_...`
+      runs (medians per dispatch), with derived figures: matrix-core
+      instructions times N ops each, the matrix pipe's busy share of the
+      SIMD-cycles while the CUs were busy (SQ_VALU_MFMA_BUSY_CYCLES over
+      4 x SQ_BUSY_CU_CYCLES), VALU instructions per wavefront and LDS
+      bank-conflict cycles per LDS instruction.
 """
 from __future__ import annotations
 
@@ -105,7 +114,17 @@ def main(argv=None):
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
     t.add_argument("--out")
+    q = sub.add_parser("sq")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    q.add_argument("--match", help="substring naming the kernel's instance (default: NAME<)")
+    q.add_argument("--mfma-ops", type=float, default=0.0, help="ops per matrix-core instruction")
+    q.add_argument("--workload", default="")
+    q.add_argument("--command", action="append", default=[])
+    q.add_argument("--out")
     a = ap.parse_args(argv)
+    if a.cmd == "sq":
+        return sq_summary(a)
     if a.cmd == "stats":
         print(f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'total_us':>11}")
         for name, calls, avg, tot in kernel_stats(a.dir):
@@ -142,6 +161,34 @@ def main(argv=None):
         f"traffic_bytes_per_launch: {fb + wb:.0f}",
         f"source_sha256: {source_hash(a.kernel)}",
     ]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+def sq_summary(a):
+    match = a.match or a.kernel + "<"
+    vals = {}
+    for d in a.dirs:
+        names = sorted({r["Counter_Name"] for r in _rows(d, "*counter_collection.csv")})
+        for c in names:
+            if c.startswith("SQ_"):
+                vals[c] = _pick(counter_means(d, c), match, c)
+    lines = [f"# SQ counters of {a.kernel} ({a.workload}), medians per dispatch, rocprofv3 --pmc"]
+    lines += [f"command: {c}" for c in a.command]
+    lines += [f"kernel: {a.kernel}", f"instance: {match}", f"workload: {a.workload}"]
+    lines += [f"{c}: {v:.0f}" for c, v in sorted(vals.items())]
+    if a.mfma_ops and "SQ_INSTS_MFMA" in vals:
+        lines.append(f"mfma_ops_per_dispatch: {vals['SQ_INSTS_MFMA'] * a.mfma_ops:.0f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and vals.get("SQ_BUSY_CU_CYCLES"):
+        lines.append(f"mfma_busy_share: {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * vals['SQ_BUSY_CU_CYCLES']):.3f}")
+    if "SQ_INSTS_VALU" in vals and vals.get("SQ_WAVES"):
+        lines.append(f"valu_insts_per_wave: {vals['SQ_INSTS_VALU'] / vals['SQ_WAVES']:.1f}")
+    if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_INSTS_LDS"):
+        lines.append(f"lds_conflict_cycles_per_lds_inst: {vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.2f}")
+    lines.append(f"source_sha256: {source_hash(a.kernel)}")
     text = "\n".join(lines) + "\n"
     if a.out:
         with open(a.out, "w") as f:
