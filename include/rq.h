@@ -125,7 +125,8 @@ typedef struct {
  *            weight side uses it for the asymmetric zero-point correction
  *   x_out    out fp16 [T, n_out] outlier columns (NULL iff n_out == 0)
  * T == 0 is a no-op.  (K - n_out) must be a positive multiple of 64 (QUIK's
- * 8192 - 256 = 7936 qualifies). */
+ * 8192 - 256 = 7936 qualifies).  Rows holding Inf or NaN get unspecified
+ * codes, scale and zero point (never an out-of-range write). */
 rq_status rq_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx,
                           const rq_rot_desc *rot, const rq_quant_desc *qd,
                           uint8_t *q, float *scale, int32_t *zero, int32_t *code_sum,
