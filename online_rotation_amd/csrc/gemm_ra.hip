@@ -52,6 +52,25 @@ __device__ __forceinline__ int ra_off(int row, int slot) {
   return row * kRaRow + ((slot ^ ((row >> 1) & 7)) << 4);
 }
 
+// Tile order within an XCD's contiguous range of positions (the same XCD
+// remap as map_tile): groups of G row tiles walked against consecutive column
+// tiles.  With 16 or more row tiles (the QUIK shapes, K up to 28672) a group
+// of 8 holds 8 row tiles of A, more than an XCD's 4 MB L2, and each round of
+// resident workgroups re-fetched them; groups of 4 fetch 20% less there in
+// the same time.  Smaller problems keep groups of 8.
+__device__ __forceinline__ void ra_map_tile(int bid, int nt_m, int nt_n, int &tm, int &tn) {
+  const int nt = nt_m * nt_n;
+  int pos = bid;
+  if ((nt & 7) == 0) pos = (bid & 7) * (nt >> 3) + (bid >> 3);
+  const int G = nt_m >= 16 ? 4 : 8;
+  const int group = pos / (G * nt_n);
+  const int first = group * G;
+  const int gsz = min(G, nt_m - first);
+  const int in = pos - group * G * nt_n;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
@@ -71,7 +90,7 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   int tm, tn;
-  map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
+  ra_map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kRaBM, n0 = (int64_t)tn * kRaBN, Kb = p.Kb;
   const int nsteps = (int)(Kb >> 6), last = nsteps - 1;
 
