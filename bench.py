@@ -315,7 +315,7 @@ def main_kv(args, torch, rq, prof, workloads):
     print(json.dumps(rec), flush=True)
 
 
-FP64_VECTOR_PEAK_TFLOPS = 78.6  # MI355X fp64 vector
+FP64_VECTOR_PEAK_TFLOPS = 78.6  # MI355X fp64 vector: 256 CUs x 128 flops/clock (64 FMA) x 2.4 GHz
 
 
 def main_weight_prep(args, torch, rq, prof, workloads):
@@ -385,12 +385,13 @@ def main_weight_prep(args, torch, rq, prof, workloads):
         "config": {"workload": f"{wl.name} weights: W fp16 [{N},{K}], {n_out} fp16 outlier columns, "
                                f"INT{bits} per channel, {steps} clip ratios", "N": N, "K": K, "n_out": n_out,
                    "bits": bits, "ratios": steps},
-        "roofline": {"bound": "fp64", "achieved": round(flops / search_s / 1e12, 2),
+        "roofline": {"bound": "alu", "achieved": round(flops / search_s / 1e12, 2),
                      "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / search_s / 1e12 / FP64_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "clip_search", "flops_per_launch": flops, "avg_launch_us": round(search_s * 1e6, 1),
-                     "note": "4 fp64 flops per value and ratio (the error term); the exact fp32 codes beside them "
-                             "are not counted"},
+                     "note": "fp64 vector ALU arithmetic: 4 fp64 flops per value and ratio (the error term), the "
+                             "exact fp32 codes beside them not counted; peak = 256 CUs x 128 fp64 flops per clock "
+                             "x 2.4 GHz"},
         "quantize": {"kernel": "split_quant8" if bits == 8 else "split_quant", "avg_launch_us": round(quant_s * 1e6, 1),
                      "achieved_GBps": round((w_bytes + N * (kint if bits == 8 else kint // 2)) / quant_s / 1e9, 1)},
         "gpu": torch.cuda.get_device_name(0),

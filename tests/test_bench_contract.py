@@ -60,3 +60,27 @@ def test_kv_line():
     assert rc == 0, r.stderr[-2000:]
     _check_common(d, 3, 1)
     assert d["unit"] == "GB/s" and d["roofline"]["bound"] == "hbm" and d["roofline"]["peak"] == 8000.0
+
+
+@pytest.mark.gpu
+def test_sweep_entries():
+    rc, d, r = _run(["--workload", "gsr", "--sweep", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+                    timeout=600)
+    assert rc == 0, r.stderr[-2000:]
+    _check_common(d, 2, 1)
+    sw = d["rotate_quant"]["sweep"]
+    assert [e["T"] for e in sw] == [16384, 65536]
+    for e in sw:
+        assert e["avg_launch_us"] > 0 and 0 < e["frac"] < 1
+        # bytes of the gsr quantizer per token (8192 in, 2048 codes, 4 scale) over the launch time
+        assert e["achieved_GBps"] == pytest.approx(e["T"] * 10244 / e["avg_launch_us"] / 1e3, rel=2e-3)
+
+
+@pytest.mark.gpu
+def test_weight_prep_line():
+    rc, d, r = _run(["--workload", "quik_prefill", "--weight-prep", "--steps", "1", "--warmup", "1",
+                     "--no-cpu-baseline"], timeout=600)
+    assert rc == 0, r.stderr[-2000:]
+    _check_common(d, 1, 1)
+    assert d["unit"] == "GB/s" and d["roofline"]["kernel"] == "clip_search"
+    assert d["quantize"]["kernel"] == "split_quant" and d["quantize"]["avg_launch_us"] > 0
