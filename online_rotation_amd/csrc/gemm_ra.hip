@@ -87,6 +87,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   constexpr int kGroups = BITS == 8 ? 2 : 4;  // MFMA groups per k-step
   __shared__ __align__(16) uint8_t Bs[kRaNB * kRaBuf];
+  // The tile's dequantization vectors (sx, zx per row; sw, rowsum per
+  // column), staged in LDS at the start so that the epilogue does not wait on
+  // global loads after the k loop (modes 1 and 2).
+  __shared__ float s_sx[kRaBM], s_sw[kRaBN];
+  __shared__ int32_t s_zx[kRaBM], s_rs[kRaBN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   int tm, tn;
@@ -177,11 +182,36 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aw[i], bf[f][j], acc[i][j], 0, 0, 0);
   };
 
+  // The dequantization vectors go out first, unconditionally (clamped
+  // indices; a missing zx or rowsum reads a stand-in and is zeroed), so that
+  // waiting for B(0) below also covers them.
+  constexpr int kZoffS = (BITS == 8 && XU) ? 128 : 0;
+  const bool need_zx = MODE == 2 && p.zx;
+  const bool need_rs = need_zx || kZoffS;
+  float vsx = 0.0f, vsw = 0.0f;
+  int32_t vzx = 0, vrs = 0;
+  if (MODE != 0) {
+    const int64_t sr = min(m0 + tid, p.T - 1), sc = min(n0 + (tid & (kRaBN - 1)), p.N - 1);
+    const int32_t *zxp = need_zx ? p.zx : reinterpret_cast<const int32_t *>(p.sx);
+    const int32_t *rsp = need_rs ? p.rowsum : reinterpret_cast<const int32_t *>(p.sw);
+    vsx = p.sx[sr];
+    vzx = zxp[sr];
+    vsw = p.sw[sc];
+    vrs = rsp[sc];
+  }
   // prologue: steps 0 .. kRaD-1 in flight, B(0) into buffer 0, its first fragments
 #pragma unroll
   for (int s = 0; s < kRaD; ++s) gload(s, min(s, last));
   bstore(0, 0, 0);
   bstore(0, 0, 1);
+  if (MODE != 0) {
+    s_sx[tid] = vsx;
+    s_zx[tid] = need_zx ? vzx : 0;
+    if (tid < kRaBN) {
+      s_sw[tid] = vsw;
+      s_rs[tid] = need_rs ? vrs : 0;
+    }
+  }
   __syncthreads();
   bread(0, 0, 0);
 
@@ -285,18 +315,17 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   int32_t rsn[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t gn = min(col0 + 32 * j + l32, p.N - 1);
-    swn[j] = p.sw[gn];
-    rsn[j] = ((MODE == 2 && p.zx) || kZoff) ? p.rowsum[gn] : 0;
+    swn[j] = s_sw[32 * j + l32];
+    rsn[j] = s_rs[32 * j + l32];
   }
   v16f f[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t gm = min(row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3), p.T - 1);
-      const float sxm = p.sx[gm];
-      const int32_t zxm = ((MODE == 2 && p.zx) ? p.zx[gm] : 0) - kZoff;
+      const int lr = wave * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float sxm = s_sx[lr];
+      const int32_t zxm = s_zx[lr] - kZoff;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int32_t v = acc[i][j][r] >> kShift;
