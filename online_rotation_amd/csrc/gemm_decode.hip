@@ -381,7 +381,7 @@ __device__ __forceinline__ void stage_fused(const GemmArgs &p, const FuseArgs &f
 template <bool XU, int MODE, int G>
 __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   extern __shared__ __align__(16) uint8_t xs[];
-  __shared__ float sxl[16];  // G = 0: the rows' scales and zero points
+  __shared__ float sxl[16];  // the rows' scales and zero points (G = 0: made here; else staged)
   __shared__ int zxl[16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -421,6 +421,12 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     // the compiler wait for every load at its join); a lane past the end
     // reloads the last chunk (one shared line per instruction).
     const uint32_t nt = na + no;
+    // the rows' scales and zero points, loaded unconditionally (clamped row;
+    // without zx a stand-in read, zeroed) and parked in LDS with the codes
+    const uint32_t tc = min((uint32_t)tid, T - 1);
+    const int32_t *zxp = p.zx ? p.zx : reinterpret_cast<const int32_t *>(p.sx);
+    const float vsx = MODE != 0 ? p.sx[tc] : 0.0f;
+    const int32_t vzx = MODE == 2 ? zxp[tc] : 0;
     v4u s0[8], s1[8];
     auto sload = [&](v4u (&v)[8], int h) {
 #pragma unroll
@@ -455,6 +461,10 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       sstore(s0, 0);
       if (G == 2) sstore(s1, 1);
     }
+    if (tid < T) {
+      sxl[tid] = vsx;
+      zxl[tid] = p.zx ? vzx : 0;
+    }
   }
   __syncthreads();
   if (n0 >= p.N) return;  // whole wavefront past the last channel (after its share of the staging)
@@ -462,6 +472,12 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const uint32_t arow = min((uint32_t)l16, T - 1);
   const uint8_t *xa = xs + arow * pa + 16 * kg;
   const uint8_t *xoa = nk ? xs + xo_base + arow * po + 16 * kg : xa;  // never read unmasked when nk == 0
+  // the channel's scale and code sum go out before the weight stream, so the
+  // epilogue does not wait on them
+  const bool has_zx = G == 0 ? XU : p.zx != nullptr;
+  const int64_t gnc = min(n0 + l16, p.N - 1);
+  const float swn = MODE != 0 ? p.sw[gnc] : 0.0f;
+  const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
   v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   v4f fo = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int kb0 = 0; kb0 < S; kb0 += kD16) {
@@ -503,18 +519,14 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     }
     return;
   }
-  const int64_t gnc = min(gn, p.N - 1);
-  const float swn = p.sw[gnc];
-  const bool has_zx = G == 0 ? XU : p.zx != nullptr;
-  const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
   __half *out = reinterpret_cast<__half *>(p.out);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t gm = 4 * kg + r;
     const int64_t gmc = min(gm, p.T - 1);
     int32_t v = (acc0[r] + acc1[r]) >> kShift;
-    if (MODE == 2 && has_zx) v -= (G == 0 ? zxl[gmc] : p.zx[gmc]) * rsn;
-    const float y = (float)v * (G == 0 ? sxl[gmc] : p.sx[gmc]) * swn + fo[r];
+    if (MODE == 2 && has_zx) v -= zxl[gmc] * rsn;
+    const float y = (float)v * sxl[gmc] * swn + fo[r];
     if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(y);
   }
 }
