@@ -286,7 +286,12 @@ def int_gemm(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def to_fp16(y: np.ndarray) -> np.ndarray:
-    """Round fp64 once to fp16, round half to even (numpy's direct conversion)."""
+    """Round fp64 once to fp16, round half to even (numpy's direct conversion).
+
+    [QUIK] part 1: the dequantized INT4 product and the FP16 outlier product
+    are summed into an FP16 output; reading c14: the sum is formed exactly and
+    rounded once.  Values at or above 65520 in magnitude become infinities.
+    """
     return np.asarray(y, np.float64).astype(np.float16)
 
 

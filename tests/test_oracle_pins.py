@@ -372,6 +372,85 @@ def test_dequant_equals_product_of_dequantized_operands():
     np.testing.assert_array_equal(o.dequant_sym(o.int_gemm(qx, qw), sx, sw), dense.astype(np.float16))
 
 
+def _term(t):
+    """'2^-11', '-2^-40', '65504', 'inf' -> float, each exactly representable."""
+    if t in ("inf", "-inf"):
+        return float(t)
+    sign = -1.0 if t.startswith("-") else 1.0
+    t = t.lstrip("-")
+    if "^" in t:
+        b, e = t.split("^")
+        assert b == "2"
+        return sign * math.ldexp(1.0, int(e))
+    return sign * float(t)
+
+
+def _exact_sum(terms):
+    """Sum of powers of two and small integers, exactly (as a Fraction)."""
+    from fractions import Fraction
+    return sum((Fraction(_term(t)) for t in terms), Fraction(0))
+
+
+def test_fp16_rounding_hand_worked(golden_dir):
+    """Single round-half-to-even fp64 -> fp16 of the output (reading c14), on
+    values whose rounding through fp32 would differ: the oracle must round
+    the exact value once."""
+    from fractions import Fraction
+    rows = _rows(os.path.join(golden_dir, "fp16_rounding.txt"))
+    plain = [r for r in rows if not r[0].startswith("epilogue")]
+    assert len(plain) >= 10
+    for name, value, want in plain:
+        v = _exact_sum(value.split())
+        assert Fraction(float(v)) == v, name            # the value itself is an fp64
+        w = want.split()
+        expect = float(w[0]) if w[0] in ("inf", "0") else float(_exact_sum(w))
+        got = o.to_fp16(np.array([float(v)]))[0]
+        assert got.dtype == np.float16
+        assert float(got) == expect, f"{name}: got {float(got)!r}, want {expect!r}"
+    # the first line is the fp32-detour trap: rounding through fp32 lands on
+    # the tie and gives 1, the single rounding gives 1 + 2^-10
+    v = float(_exact_sum(plain[0][1].split()))
+    assert float(np.float16(np.float32(v))) == 1.0 and float(o.to_fp16(np.array([v]))[0]) == 1 + 2.0 ** -10
+
+
+def test_fp16_rounding_through_the_epilogues(golden_dir):
+    """dequant_sym and dequant_mixed form y exactly and round it once: the
+    hand-worked lines give outputs that an fp32 product or sum would miss."""
+    rows = {r[0]: r for r in _rows(os.path.join(golden_dir, "fp16_rounding.txt")) if r[0].startswith("epilogue")}
+    assert set(rows) == {"epilogue_sym", "epilogue_mixed", "epilogue_outliers_only"}
+
+    def parse(spec):
+        out, key = {}, None
+        for tok in spec.split():
+            if "=" in tok:
+                key, tok = tok.split("=")
+                out[key] = []
+            out[key].append(tok)
+        return out
+
+    for name, r in rows.items():
+        f = parse(r[1])
+        want = float(_exact_sum(r[2].split()))
+        acc = np.array([[int(_exact_sum(f["acc"]))]], np.int32)
+        sx = np.array([float(_exact_sum(f["sx"]))], np.float32)
+        sw = np.array([float(_exact_sum(f["sw"]))], np.float32)
+        assert float(sx[0]) == float(_exact_sum(f["sx"])) and float(sw[0]) == float(_exact_sum(f["sw"]))
+        if name == "epilogue_sym":
+            y = o.dequant_sym(acc, sx, sw)
+        else:
+            zx = np.array([int(_exact_sum(f["z"]))], np.int32)
+            rs = np.array([int(_exact_sum(f["rowsum"]))], np.int32)
+            if name == "epilogue_outliers_only":   # one outlier column per term
+                xo_v = [float(_exact_sum([t])) for t in f["xo"]]
+                wo_v = [float(_exact_sum([t])) for t in f["wo"]]
+            else:
+                xo_v, wo_v = [float(_exact_sum(f["xo"]))], [float(_exact_sum(f["wo"]))]
+            xo, wo = np.array([xo_v], np.float16), np.array([wo_v], np.float16)
+            assert xo.astype(np.float64).tolist() == [xo_v] and wo.astype(np.float64).tolist() == [wo_v]
+            y = o.dequant_mixed(acc, sx, zx, sw, rs, xo, wo)
+        assert y.dtype == np.float16 and float(y[0, 0]) == want, f"{name}: got {float(y[0, 0])!r}, want {want!r}"
+
+
 # ---------------------------------------------------------------- QUIK split
 
 def test_quik_split_identity_and_zero_point_correction():
