@@ -36,26 +36,30 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link librq.so; returns the library path."""
+def _compile(hipcc: str, src: str, objdir: str, verbose: bool) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source (in parallel) and link librq.so; returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     hipcc = _hipcc()
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"]
-        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", os.path.join(ROOT, "include"), "-c",
-               os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
-        if verbose and err.strip():
-            print(err, file=sys.stderr)
-        objs.append(obj)
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(hipcc, src, objdir, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

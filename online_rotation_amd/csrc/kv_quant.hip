@@ -10,10 +10,14 @@
 // lane.  The Walsh-Hadamard of natural order factors over the index bits:
 // two of its bits select the lane in the quad (DPP quad permutations, no
 // LDS), the others are register butterflies within the lane.  The
-// transform runs unnormalized in fp32 and is scaled by 1/sqrt(g) once; the
-// quad's min / max then give the group's asymmetric scale and zero point
-// with the arithmetic of the per-token quantizer (split_common.h), and each
-// lane packs its V codes into V/8 dwords.
+// transform runs unnormalized in fp64, where it is exact: every fp16 value
+// is an integer multiple of 2^-24 below 2^16, so a signed sum of at most 256
+// of them is an integer multiple of 2^-24 below 2^48.  The sums are scaled
+// by 1/sqrt(g) and rounded to fp32 once, so each value is within 2^-23
+// (relative) of the exact rotation; the quad's min / max then give the
+// group's asymmetric scale and zero point with the arithmetic of the
+// per-token quantizer (split_common.h), and each lane packs its V codes into
+// V/8 dwords.
 #include "rq_device.h"
 #include "rq_kernels.h"
 #include "split_common.h"
@@ -27,6 +31,14 @@ __device__ __forceinline__ float quad_xor1(float v) {
 }
 __device__ __forceinline__ float quad_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+// the same for an fp64 value, one dword at a time
+template <int CTRL>
+__device__ __forceinline__ double quad_perm64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 }  // namespace
 
@@ -47,7 +59,7 @@ struct KvArgs {
   int32_t step_cols;
   int32_t gpr;           // groups per row
   uint32_t gpr_magic;    // floor((2^32 - 1) / gpr) + 1: n / gpr = umulhi(n, magic) for n * gpr < 2^32
-  float norm;            // fp32(1 / sqrt(group))
+  double norm;           // fp64(1 / sqrt(group))
 };
 
 template <int V, bool ROT>
@@ -84,8 +96,8 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
 
   // Cross-lane butterflies store sigma * value with sigma = (-1)^popcount(sub),
   // each one fma with the partner; fin = sigma / sqrt(group) restores the value.
-  const float c1 = (sub & 1) ? -1.0f : 1.0f, c2 = (sub & 2) ? -1.0f : 1.0f;
-  const float fin = ROT ? c1 * c2 * a.norm : 1.0f;
+  const double c1 = (sub & 1) ? -1.0 : 1.0, c2 = (sub & 2) ? -1.0 : 1.0;
+  const double fin = c1 * c2 * a.norm;
 
   int64_t t;
   int32_t gc;
@@ -121,34 +133,33 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
       }
     }
     if (ROT) {
-      // y_j = sum_i x_i (-1)^popcount(i & j): one butterfly stage per index bit
+      // y_j = sum_i x_i (-1)^popcount(i & j): one butterfly stage per index
+      // bit, in fp64 (exact), then one rounding to fp32
+      double d[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) d[i] = (double)v[i];
 #pragma unroll
       for (int h = 1; h < V; h <<= 1)
 #pragma unroll
         for (int i = 0; i < V; ++i)
           if (!(i & h)) {
-            const float p = v[i], r = v[i + h];
-            v[i] = p + r;
-            v[i + h] = p - r;
+            const double p = d[i], r = d[i + h];
+            d[i] = p + r;
+            d[i + h] = p - r;
           }
 #pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = __builtin_fmaf(quad_xor1(v[i]), c1, v[i]);
+      for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0xB1>(d[i]), c1, d[i]);  // quad_perm [1,0,3,2]
 #pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = __builtin_fmaf(quad_xor2(v[i]), c2, v[i]);
+      for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0x4E>(d[i]), c2, d[i]);  // quad_perm [2,3,0,1]
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = (float)(d[i] * fin);
     }
-    // the group's min and max over the quad (0 included, as the quantizer's
-    // range); the stored values times fin are the group's values, so lanes
-    // with fin < 0 swap their minimum and maximum
+    // the group's min and max over the quad (0 included, as the quantizer's range)
     float mn = 0.0f, mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       mn = fminf(mn, v[i]);
       mx = fmaxf(mx, v[i]);
-    }
-    if (ROT) {
-      const float lo = (fin > 0.0f ? mn : mx) * fin, hi = (fin > 0.0f ? mx : mn) * fin;
-      mn = lo;
-      mx = hi;
     }
     mn = fminf(mn, quad_xor1(mn));
     mx = fmaxf(mx, quad_xor1(mx));
@@ -169,9 +180,16 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
         wd[c] = (o << 4) | e;
       }
     };
-    if (__builtin_amdgcn_ballot_w64(rq.exact) == 0) {
-      const float coef = fin * rq.inv;
-      pack([&](float f) { return __builtin_fmaf(f, coef, rq.base); });
+    if (__builtin_amdgcn_ballot_w64(rq.exact || (!ROT && rq.wide)) == 0) {
+      pack([&](float f) { return __builtin_fmaf(f, rq.inv, rq.base); });
+    } else if (!ROT && __builtin_amdgcn_ballot_w64(rq.wide) != 0) {
+      // Some fp16 group spans a wide range (its hi - lo has more than 16
+      // significant bits: a large value beside a tiny one of the other
+      // sign), so a value may lie closer to a rounding boundary than one fma
+      // resolves: every group of the wavefront takes the exact quotient.
+      pack([&](float f) {
+        return rq.s > 0.0f ? rne_quotient(f, rq.s, rq.inv) + rq.base : rq.base;
+      });
     } else {
       // Some group's scale is exact (s equals the real (hi - lo)/15), so its
       // ties x/s = k + 1/2 are real and go to even.  With the two fp32
@@ -186,9 +204,9 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
         if (e > 0.0f) hi_inv = __uint_as_float(__float_as_uint(rq.inv) + 1u);
         if (e < 0.0f) lo_inv = __uint_as_float(__float_as_uint(rq.inv) - 1u);
       }
-      const float ca = fin * lo_inv, cb = fin * hi_inv, zf = (float)rq.zp;
+      const float zf = (float)rq.zp;
       pack([&](float f) {
-        return __builtin_fmaf(__builtin_fmaf(f, ca, kMagic0) + __builtin_fmaf(f, cb, kMagic0), 0.5f, zf);
+        return __builtin_fmaf(__builtin_fmaf(f, lo_inv, kMagic0) + __builtin_fmaf(f, hi_inv, kMagic0), 0.5f, zf);
       });
     }
     if (valid) {
@@ -229,7 +247,7 @@ hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, 
   a.gpr = (int32_t)(K / group);
   a.total = T * a.gpr;
   a.gpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)a.gpr) + 1u;
-  a.norm = 1.0f / sqrtf((float)group);
+  a.norm = 1.0 / sqrt((double)group);
   const int64_t sets = (a.total + 15) / 16;
   const int64_t waves = std::min<int64_t>(sets, kKvWaves);
   const int64_t blocks = (waves + 3) / 4;

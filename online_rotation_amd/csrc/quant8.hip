@@ -154,10 +154,12 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
       const float mn = block_reduce(fminf((float)mn2[0], (float)mn2[1]), red[0], false);
       const float mx = block_reduce(fmaxf((float)mx2[0], (float)mx2[1]), red[1], true);
       const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
-      // the scale is the exact quotient rounded once to fp32: formed in fp64
-      // (hi - lo is exact) and converted, as a single rounding would be
-      // except where the fp64 quotient itself falls on an fp32 midpoint
-      s = (float)((double)(hi - lo) / 255.0);
+      // the scale is the exact quotient rounded once to fp32: hi - lo formed
+      // exactly in fp64 (fp16 bounds span at most 40 bits; in fp32 the
+      // difference rounds when max / |min| exceeds about 2^12), the quotient
+      // rounded to fp64 and converted, as a single rounding would be except
+      // where the fp64 quotient itself falls on an fp32 midpoint
+      s = (float)(((double)hi - (double)lo) / 255.0);
       inv = s > 0.0f ? 1.0f / s : 0.0f;
       if (s > 0.0f) zf = __builtin_amdgcn_fmed3f(rne_div(-lo, s, inv), 0.0f, 255.0f);
       lo_c = 0.0f;

@@ -124,25 +124,12 @@ __device__ __forceinline__ uint32_t pack8(const int *c) {
   return w;
 }
 
-// Symmetric per-row scale: fp32(clip * absmax / 7) with the scale's
-// reciprocal used for the codes.
+// Symmetric per-row scale: fp32(clip * absmax / 7), with the product exact in
+// fp64 (24 x 24 bits) and the quotient rounded to fp64 and then to fp32, as
+// the exact scale is rounded; also the scale's reciprocal used for the codes.
 __device__ __forceinline__ void sym_scale(float amax, float clip, float &s, float &inv) {
-  s = (clip * amax) / 7.0f;
+  s = (float)((double)clip * (double)amax / 7.0);
   inv = s > 0.0f ? 1.0f / s : 0.0f;
-}
-
-// Asymmetric per-row parameters from the row's min and max.
-__device__ __forceinline__ void asym_params(float mn, float mx, float &s, float &inv, int &zero) {
-  const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
-  s = (hi - lo) / 15.0f;
-  if (s > 0.0f) {
-    inv = 1.0f / s;
-    float z = __builtin_rintf(-lo / s);
-    zero = (int)__builtin_amdgcn_fmed3f(z, 0.0f, 15.0f);
-  } else {
-    inv = 0.0f;
-    zero = 0;
-  }
 }
 
 }  // namespace rq

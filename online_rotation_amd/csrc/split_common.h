@@ -9,13 +9,21 @@
 // reductions test no value.
 //
 // Rounding matches rne(x / s) with s = fp32(S), S the exact real scale
-// (clip*amax/7 or (hi - lo)/15).  The inputs are fp16, so x / S lies either
-// exactly on a rounding boundary k + 1/2 or at least ~2^-15 (relative) away
-// from every boundary; the reciprocal of s (2^-24 off) only matters for the
-// exact ties, and there x / s falls on the side that the rounding of S to s
-// decides.  directed_inv moves the reciprocal by at most one ulp so that
-// x * inv lands on that same side.  When S == s the ties are real and go to
-// even; such rows take rne_quotient, which tests the boundary exactly.
+// (clip*amax/7 or (hi - lo)/15), and s is formed as the oracle forms it: the
+// numerator clip*amax or hi - lo exactly in fp64, the quotient rounded to
+// fp64 and then to fp32.  Write the numerator as an integer of m significant
+// bits times a power of two.  With fp16 inputs, x / S then lies either
+// exactly on a rounding boundary k + 1/2 or at least 2^-(m+1) (and 2^-17)
+// from every boundary, while x * inv, with inv within an ulp of 1/s, differs
+// from x / S by less than 2^-18.  So for m <= 16 ("narrow" rows, which
+// include every row with a zero bound or clip 1) one fma per value is exact
+// except at the exact ties, and there x / s falls on the side that the
+// rounding of S to s decides; directed_inv moves the reciprocal by at most
+// one ulp so that x * inv lands on that same side.  When S == s the ties are
+// real and go to even, and when m > 16 ("wide" rows: a large max beside a
+// tiny negative min, or clip ratios below 1) a value may lie closer to a
+// boundary than the fma resolves; both take rne_quotient, which tests the
+// boundary exactly.
 #pragma once
 #include "rq_device.h"
 
@@ -27,11 +35,11 @@ constexpr float kMagic0 = 12582912.0f;
 constexpr float kMagic8 = 12582920.0f;  // kMagic0 + 8
 
 // Reciprocal of s nudged to the side of 1/s on which exact ties must land.
-// num / den = S; `exact` is set when s == S.
-__device__ __forceinline__ float directed_inv(float s, float inv, float num, float den, bool &exact) {
-  const float r = __builtin_fmaf(-den, s, num);   // S - s, sign exact
-  const float e = __builtin_fmaf(-s, inv, 1.0f);  // 1/s - inv, sign exact
-  exact = r == 0.0f;
+// num / den = S (num exact in fp64, den = 7 or 15); `exact` is set when s == S.
+__device__ __forceinline__ float directed_inv(float s, float inv, double num, double den, bool &exact) {
+  const double r = __builtin_fma(-den, (double)s, num);  // den*(S - s), exact: den*s has <= 28 bits
+  const float e = __builtin_fmaf(-s, inv, 1.0f);         // 1/s - inv, sign exact
+  exact = r == 0.0;
   uint32_t bits = __float_as_uint(inv);
   if (r > 0.0f && e > 0.0f) ++bits;       // s < S: ties round away from zero, need inv >= 1/s
   else if (r < 0.0f && e < 0.0f) --bits;  // s > S: ties round toward zero, need inv <= 1/s
@@ -96,22 +104,34 @@ __device__ __forceinline__ float wave_uniform(float v) {
 struct RowQuant {
   float s, inv, base, lo_c, hi_c;
   int zp;
-  bool exact;
+  bool exact;  // s == S: exact ties are real ties
+  bool wide;   // the numerator of S has more than 16 significant bits
 };
 
+// More than 16 significant bits in a finite double: a set bit among the 37
+// lowest of its 52 stored fraction bits.
+__device__ __forceinline__ bool wide_significand(double v) {
+  return (__double_as_longlong(v) & ((1ll << 37) - 1)) != 0;
+}
+
 // From the row's min and max (asymmetric: lo = min(mn, 0), hi = max(mx, 0);
-// symmetric: mx = max |x|, scale clip * mx / 7).
+// symmetric: mx = max |x|, scale clip * mx / 7).  The numerator is exact in
+// fp64 (fp16 bounds span at most 40 bits; clip * mx has at most 35).
 __device__ __forceinline__ RowQuant row_quant(bool asym, float clip, float mn, float mx) {
   RowQuant r;
   r.zp = 0;
   r.exact = false;
+  r.wide = false;
   if (asym) {
     const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
-    r.s = (hi - lo) / 15.0f;
+    const double range = (double)hi - (double)lo;
+    r.s = (float)(range / 15.0);
     r.inv = r.s > 0.0f ? 1.0f / r.s : 0.0f;
     if (r.s > 0.0f) {
-      r.inv = directed_inv(r.s, r.inv, hi - lo, 15.0f, r.exact);
-      const float zf = r.exact ? rne_quotient(-lo, r.s, r.inv) : __builtin_fmaf(-lo, r.inv, kMagic0) - kMagic0;
+      r.inv = directed_inv(r.s, r.inv, range, 15.0, r.exact);
+      r.wide = wide_significand(range);
+      const float zf = (r.exact || r.wide) ? rne_quotient(-lo, r.s, r.inv)
+                                           : __builtin_fmaf(-lo, r.inv, kMagic0) - kMagic0;
       r.zp = (int)__builtin_amdgcn_fmed3f(zf, 0.0f, 15.0f);
     }
     r.base = kMagic0 + (float)r.zp;  // code = clamp(rne(x/s) + zero, 0, 15)
@@ -119,7 +139,11 @@ __device__ __forceinline__ RowQuant row_quant(bool asym, float clip, float mn, f
     r.hi_c = kMagic0 + 15.0f;
   } else {
     sym_scale(mx, clip, r.s, r.inv);
-    if (r.s > 0.0f) r.inv = directed_inv(r.s, r.inv, clip * mx, 7.0f, r.exact);
+    if (r.s > 0.0f) {
+      const double num = (double)clip * (double)mx;
+      r.inv = directed_inv(r.s, r.inv, num, 7.0, r.exact);
+      r.wide = wide_significand(num);
+    }
     r.base = kMagic8;  // low nibble = code + 8
     r.lo_c = kMagic8 - 7.0f;
     r.hi_c = kMagic8 + 7.0f;
@@ -155,10 +179,10 @@ __device__ __forceinline__ int quant_word(const uint32_t *d, uint32_t m, int pos
       w[i] = asym ? wd : (wd ^ 0x88888888u);  // symmetric: offset-8 nibble -> two's complement
     }
   };
-  // Rows with exact ties (rq.exact, uniform) take the exact quotient, the
-  // rest one fma.  The exact path is rare: its loop stays rolled so that it
-  // does not set the kernel's register budget.
-  if (rq.exact) {
+  // Rows with exact ties or a wide numerator (rq.exact, rq.wide, uniform)
+  // take the exact quotient, the rest one fma.  The exact path is rare: its
+  // loop stays rolled so that it does not set the kernel's register budget.
+  if (rq.exact || rq.wide) {
     uint32_t dl[16], q[16];  // a private copy: the rolled loop indexes it
 #pragma unroll
     for (int k = 0; k < 16; ++k) dl[k] = d[k];

@@ -1,6 +1,10 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol
 include/rq.h declares, and its host-side validation rejects bad arguments
-with the documented status codes before anything is launched."""
+with the documented status codes before anything is launched.
+
+Every test runs in both sessions: once unmarked (the CPU session) and once
+marked `gpu` (the GPU session, against the library the GPU tests load).  A
+missing librq.so is built first, never skipped."""
 import ctypes
 import os
 import re
@@ -12,8 +16,16 @@ import online_rotation_amd as rq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rq.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(rq.LIB_PATH),
-                                reason="librq.so not built (run python -m online_rotation_amd.build)")
+
+
+@pytest.fixture(scope="module", autouse=True,
+                params=[pytest.param("host"), pytest.param("gpu-session", marks=pytest.mark.gpu)])
+def _library(request):
+    if not os.path.exists(rq.LIB_PATH):
+        from online_rotation_amd import build
+        build.build()
+    assert os.path.exists(rq.LIB_PATH), "librq.so is missing"
+    return request.param
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 

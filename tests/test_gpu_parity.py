@@ -233,8 +233,10 @@ def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
 
 # ----------------------------------------------------------------------------- fused decode
 
-# The fused decode form against the two calls it replaces, which here run the
-# same 16-channel decode kernel on staged codes: equal bit for bit.  Shapes:
+# The fused decode form against the oracle (codes within the quantizer
+# tolerance, y within the output tolerance widened by the tolerated flips) and
+# against the two calls it replaces, which here run the same 16-channel decode
+# kernel on staged codes: equal bit for bit.  Shapes:
 # the QUIK decode rows, T = 1 and the T = 16 maximum (at K = 8192 its LDS
 # exceeds 64 KB), asymmetric and symmetric, with and without outliers, a
 # clustered outlier run, small K, ragged N and N > 16384 (more than 4
@@ -268,7 +270,24 @@ def test_quant_decode_linear_equals_two_calls(T, N, K, n_out, asym, pattern):
     y1 = rq.rq_quant_decode_linear(xd, wq["q"], wq["scale"], wq["rowsum"] if asym else None,
                                    wq["w_out"], asym=asym, outlier_idx=idxd)
     torch.cuda.synchronize()
+    _check_fused_against_oracle(x, w, idx, asym, xq, wq, y1)
     assert torch.equal(y1, y2)
+
+
+def _check_fused_against_oracle(x, w, idx, asym, xq, wq, y1):
+    """y of the fused form against o.rotate_quant + o.prepare_weights +
+    o.linear; the codes the fused kernel made are those of the standalone
+    quantizer (checked bit for bit against it through y above), so their
+    tolerated flips widen the output tolerance."""
+    ref = o.rotate_quant(x, "none", asym=asym, outlier_idx=idx)
+    wr = o.prepare_weights(w, "none", outlier_idx=idx)
+    fw = check_sym_quant(host(wq["q"]), host(wq["scale"]), wr, what="w")
+    if asym:
+        fx = check_asym_quant(host(xq["q"]), host(xq["scale"]), host(xq["zero"]), ref)
+    else:
+        fx = check_sym_quant(host(xq["q"]), host(xq["scale"]), ref)
+    extra = flip_allowance(ref["scale"], wr["scale"], fx, fw)
+    check_y(host(y1), o.linear(ref, wr)["y"], extra=extra, what="fused y")
 
 
 def test_quant_decode_linear_exact_ties():
@@ -287,6 +306,7 @@ def test_quant_decode_linear_exact_ties():
             y2 = rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"])
         y1 = rq.rq_quant_decode_linear(xd, wq["q"], wq["scale"], wq["rowsum"] if asym else None, asym=asym)
         torch.cuda.synchronize()
+        _check_fused_against_oracle(rows, w, None, asym, xq, wq, y1)
         assert torch.equal(y1, y2)
 
 
@@ -525,6 +545,87 @@ def test_edge_asymmetric_rows():
     torch.cuda.synchronize()
     check_asym_quant(host(out["q"]), host(out["scale"]), host(out["zero"]), ref)
     assert host(out["zero"])[0] == 0 and host(out["zero"])[1] == 15 and host(out["scale"])[2] == 0
+
+
+def _wide_rows(T, K, qmax, asym, clip=1.0, seed=5):
+    """fp16 rows whose scale numerator needs many bits: a large maximum
+    (20..60) beside a tiny negative minimum (-5e-3..-1e-4), so that hi - lo
+    (or clip * max) is not exact in fp32.  Columns 0 and 1 hold the bounds
+    (hi and lo, or hi and -hi when symmetric); a quarter of each row holds the
+    fp16 values of the row's range whose x / s lies closest to a rounding
+    boundary (s the oracle's fp32 scale); row 0 holds a reported case: hi =
+    39.78, lo = -0.002882, x = 31.28125 (x / s = 200.50001 at 8 bits)."""
+    rng = np.random.default_rng(seed)
+    all16 = np.arange(65536, dtype=np.uint16).view(np.float16)
+    fin = np.unique(all16[np.isfinite(all16)].astype(np.float64))
+    rows = []
+    for t in range(T):
+        if t == 0:
+            hi, lo = float(np.float16(39.78)), float(np.float16(-0.002882))
+        else:
+            hi, lo = float(np.float16(rng.uniform(20, 60))), -float(np.float16(rng.uniform(1e-4, 5e-3)))
+        num = (hi - lo) if asym else float(np.float32(clip)) * hi
+        s = float(np.float32(num / qmax))
+        cand = fin[(fin > lo) & (fin < hi)] if asym else fin[(fin > -hi) & (fin < hi)]
+        pre = cand / s
+        near = cand[np.argsort(np.abs(pre - np.floor(pre) - 0.5), kind="stable")[:K // 4]]
+        body = rng.choice(cand, K - near.size - 3)
+        # the bounds and the reported value in columns 0-2, the rest shuffled
+        rows.append(np.concatenate([[hi, lo if asym else -hi, 31.28125 if t == 0 else body[0]],
+                                    rng.permutation(np.concatenate([near, body]))]))
+    x = np.array(rows).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64).max(axis=1), [r.max() for r in rows])
+    return x
+
+
+@pytest.mark.parametrize("bits,asym,clip,n_out", [(8, True, 1.0, 0), (8, True, 1.0, 64), (4, True, 1.0, 0),
+                                                  (4, True, 1.0, 128), (4, False, 0.9, 0), (4, False, 1.0, 0),
+                                                  (8, False, 0.9, 0)])
+def test_wide_range_rows_are_exact(bits, asym, clip, n_out):
+    """Rows whose scale numerator is not exact in fp32 (ranges spanning more
+    than 24 bits, clip ratios below 1), packed with values next to rounding
+    boundaries: scales, zero points and codes equal the oracle's exactly."""
+    T, K = 9, 2048
+    qm = ((1 << bits) - 1) if asym else ((1 << (bits - 1)) - 1)
+    note(f"[rotate_quant] wide-range rows bits={bits} asym={asym} clip={clip} n_out={n_out}")
+    x = _wide_rows(T, K, qm, asym, clip)
+    idx = np.sort(np.random.default_rng(1).choice(np.arange(3, K), n_out, replace=False)).astype(np.int32) \
+        if n_out else None
+    ref = o.rotate_quant(x, "none", clip=clip, asym=asym, outlier_idx=idx, bits=bits)
+    # the trap: with the numerator rounded to fp32 first, some scales differ
+    x32 = x.astype(np.float32)
+    num32 = (x32.max(axis=1) - np.minimum(x32.min(axis=1), 0)) if asym else np.float32(clip) * np.abs(x32).max(axis=1)
+    assert np.any((num32 / np.float32(qm)).astype(np.float32) != ref["scale"]) or n_out or (not asym and clip == 1)
+    out = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), clip=clip, asym=asym,
+                             outlier_idx=None if idx is None else dev(idx), code_sum=True, bits=bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["scale"]), ref["scale"]), "scales differ"
+    if asym:
+        assert np.array_equal(host(out["zero"]), ref["zero"]), "zero points differ"
+    assert np.array_equal(host(out["q"]), ref["packed"]), "codes differ"
+    assert np.array_equal(host(out["code_sum"]), ref["q"].astype(np.int64).sum(axis=1))
+    if bits == 4 and asym:  # the fused decode form quantizes the same rows itself
+        w = (np.random.default_rng(2).standard_normal((80, K)) * 0.02).astype(np.float16)
+        wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=None if idx is None else dev(idx))
+        y1 = rq.rq_quant_decode_linear(dev(x), wq["q"], wq["scale"], wq["rowsum"], wq["w_out"], asym=True,
+                                       outlier_idx=None if idx is None else dev(idx))
+        torch.cuda.synchronize()
+        wr = o.prepare_weights(w, "none", outlier_idx=idx)
+        assert np.array_equal(host(wq["q"]), wr["packed"])
+        check_y(host(y1), o.linear(ref, wr)["y"])
+
+
+def test_kv_wide_range_groups_are_exact():
+    """Unrotated KV groups with a wide range (see _wide_rows): identical to
+    the oracle; rotated, within the common tolerance."""
+    g, K = 128, 1024
+    x = np.concatenate([_wide_rows(8, g, 15, True, seed=s) for s in range(K // g)], axis=1)
+    note(f"[kv_rotate_quant] wide-range groups {x.shape}")
+    for rot in (False, True):
+        ref = o.kv_rotate_quant(x, group=g, rotate=rot)
+        out = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=rot)
+        torch.cuda.synchronize()
+        check_kv_quant(*(host(t) for t in out), ref, x, g, rot)
 
 
 def _exact_tie_rows(seed=11, K=1024):

@@ -1,6 +1,8 @@
-"""CPU checks of the comparison helpers themselves: the KV quantizer's fp32
-window admits a plain fp32 evaluation of the same steps and rejects a code
-that is wrong away from a rounding boundary."""
+"""CPU checks of the comparison helpers themselves: the KV quantizer's check
+admits an evaluation with the rotation rounded once to fp32 (what the GPU
+computes) and rejects a code that is wrong away from a rounding boundary, a
+scale off by more than 1e-6, and more near-boundary flips than 1e-4 of the
+codes."""
 import numpy as np
 import pytest
 
@@ -9,42 +11,44 @@ from oracle import rq_oracle as o
 from parity_utils import check_kv_quant
 
 
-def _fp32_butterflies(x16, g):
-    """Walsh-Hadamard of each group by in-place butterflies in float32, then
-    one multiply by float32(1/sqrt(g)): the evaluation order the window is
-    derived for (any other tree of log2(g) additions has the same bound)."""
-    v = x16.astype(np.float32).reshape(-1, g).copy()
-    h = 1
-    while h < g:
-        v = v.reshape(-1, g // (2 * h), 2, h)
-        a, b = v[:, :, 0, :].copy(), v[:, :, 1, :].copy()
-        v[:, :, 0, :], v[:, :, 1, :] = a + b, a - b
-        v = v.reshape(-1, g)
-        h *= 2
-    return v * np.float32(1.0 / np.sqrt(g))
+def _sylvester_signs(g):
+    h = np.array([[1.0]])
+    while h.shape[0] < g:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def _rotated_fp32(x16, g):
+    """Each group's Walsh-Hadamard image, summed exactly (integer multiples of
+    2^-24 below 2^48 in fp64), scaled by fp64(1/sqrt(g)) and rounded to fp32."""
+    x = x16.astype(np.float64).reshape(-1, g)
+    return ((x @ _sylvester_signs(g)) * (1.0 / np.sqrt(g))).astype(np.float32)
 
 
 def _fp32_quant(v):
-    lo = np.minimum(v.min(axis=1), np.float32(0))
-    hi = np.maximum(v.max(axis=1), np.float32(0))
-    s = ((hi - lo) / np.float32(15)).astype(np.float32)
-    safe = np.where(s > 0, s, np.float32(1))
-    z = np.where(s > 0, np.clip(np.rint(-lo / safe), 0, 15), 0).astype(np.int64)
-    q = np.clip(np.rint(v / safe[:, None]) + z[:, None], 0, 15).astype(np.uint8)
+    lo = np.minimum(v.min(axis=1), np.float32(0)).astype(np.float64)
+    hi = np.maximum(v.max(axis=1), np.float32(0)).astype(np.float64)
+    s = ((hi - lo) / 15).astype(np.float32)
+    s64 = s.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    z = np.where(s64 > 0, np.clip(np.rint(-lo / safe), 0, 15), 0).astype(np.int64)
+    inv = (np.float32(1) / np.where(s > 0, s, np.float32(1))).astype(np.float32)
+    prod = v * inv[:, None]                                   # fp32 products, as the fma form rounds them
+    q = np.where(s64[:, None] > 0, np.clip(np.rint(prod.astype(np.float64)) + z[:, None], 0, 15), 0).astype(np.uint8)
     return q, s, z
 
 
 @pytest.mark.parametrize("g", [64, 128, 256])
-def test_kv_window_admits_fp32_evaluation(g):
+def test_kv_check_admits_the_rotation_rounded_once(g):
     x = workloads.make_inputs("kv", T=64, K=4096, with_weights=False)["x"]
     T, K = x.shape
-    q, s, z = _fp32_quant(_fp32_butterflies(x, g))
+    q, s, z = _fp32_quant(_rotated_fp32(x, g))
     ref = o.kv_rotate_quant(x, group=g, rotate=True)
     flips = check_kv_quant(o.pack_int4(q.reshape(T, K)), s.reshape(T, -1), z.reshape(T, -1), ref, x, g, True)
-    assert flips.sum() <= 1e-3 * x.size
+    assert flips.sum() <= 1e-4 * x.size
 
 
-def test_kv_window_rejects_a_wrong_code():
+def test_kv_check_rejects_wrong_codes_scales_and_too_many_flips():
     g = 128
     x = workloads.make_inputs("kv", T=16, K=1024, with_weights=False)["x"]
     ref = o.kv_rotate_quant(x, group=g, rotate=True)
@@ -60,3 +64,22 @@ def test_kv_window_rejects_a_wrong_code():
         check_kv_quant(q, s, z, bad, x, g, True)
     with pytest.raises(AssertionError):
         check_kv_quant(q, s, z, bad | {"packed": o.pack_int4(bad["q"])}, x, g, False)
+    # a scale 2e-6 off
+    s2 = s.copy()
+    s2[3, 2] = np.float32(s2[3, 2] * (1 + 2e-6))
+    with pytest.raises(AssertionError):
+        check_kv_quant(q, s2, z, ref, x, g, True)
+    # near-boundary flips on more than 1e-4 of the codes: every code of a
+    # window wide enough to hold a few pre-round values, planted as if they
+    # were all within 1e-5 of their boundary
+    near = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in ref.items()}
+    inner = (ref["q"] > 0) & (ref["q"] < 15)
+    pos = np.argwhere(inner)[:8]
+    for tt, jj in pos:
+        near["pre"][tt, jj] = np.floor(near["pre"][tt, jj]) + 0.5 + 1e-6
+    q3 = ref["q"].copy()
+    for tt, jj in pos:
+        q3[tt, jj] += 1
+    assert len(pos) > 1e-4 * x.size
+    with pytest.raises(AssertionError):
+        check_kv_quant(o.pack_int4(q3), s, z, near, x, g, True)
