@@ -151,6 +151,23 @@ rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw,
                              uint8_t *qw, float *sw, int32_t *w_rowsum, void *w_out,
                              void *workspace, int64_t workspace_bytes, void *stream);
 
+/* rq_prepare_weights_noalloc -- rq_prepare_weights for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and the same results bit for bit.  The KRON
+ * factors' inverse transposes go to a scratch array of 32768 bytes in the
+ * library's own device memory, one per GPU, which each GPU keeps until the
+ * process ends (its address is looked up on the first call on that device).
+ * The call allocates and frees nothing.  Every call on one GPU shares that
+ * GPU's scratch array, so calls that may overlap on one GPU (on different
+ * streams, or from different threads) race on it: order them.  A transform
+ * needing more than 32768 bytes of scratch returns RQ_ESHAPE (none does:
+ * KRON factors are at most 64 x 64). */
+rq_status rq_prepare_weights_noalloc(const void *w, int64_t N, int64_t K, int64_t ldw,
+                                     const rq_rot_desc *rot, const rq_quant_desc *qd,
+                                     uint8_t *qw, float *sw, int32_t *w_rowsum, void *w_out,
+                                     void *stream);
+
 /* rq_search_weight_clip -- QUIK's weight clipping by linear search (QUIK
  * blog, "QUIK量化" part 2), per output channel.  For each row n of w, the
  * candidate ratios c = fp32(k / steps), k = steps, ..., 1, are scored by

@@ -24,13 +24,13 @@ ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
            "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
-           "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
+           "rq_prepare_weights_noalloc", "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
            "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
-           "rq_status_string", "rq_last_error", "rq_abi_version")
+           "rq_prepare_weights_noalloc", "rq_status_string", "rq_last_error", "rq_abi_version")
 
 
 class RqError(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.rq_prepare_weights_workspace_bytes.restype = i64
         L.rq_prepare_weights.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
                                          ctypes.POINTER(_QuantDesc), vp, vp, vp, vp, vp, i64, vp]
+        L.rq_prepare_weights_noalloc.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
+                                                 ctypes.POINTER(_QuantDesc), vp, vp, vp, vp, vp]
         L.rq_w4a4_linear.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i64, vp]
         L.rq_mixed_outlier_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp,
                                               i32, vp, i64, vp]
@@ -79,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.rq_w8a8_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, vp, i64, vp]
         L.rq_w8a8_gemm_i32.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp, i64, vp]
         L.rq_search_weight_clip.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), i32, vp, vp]
-        for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_w4a4_linear", "rq_mixed_outlier_linear",
+        for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_prepare_weights_noalloc", "rq_w4a4_linear",
+                   "rq_mixed_outlier_linear",
                    "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_w8a8_linear",
                    "rq_w8a8_gemm_i32", "rq_search_weight_clip"):
             getattr(L, fn).restype = ctypes.c_int
@@ -233,6 +236,28 @@ def rq_prepare_weights(w, rot: Rotation, clip: float = 1.0, outlier_idx=None, bi
     _check(st, "rq_prepare_weights")
     o["_workspace"] = ws   # keep alive until the stream has consumed it
     return o
+
+
+def rq_prepare_weights_noalloc(w, rot: Rotation, qw, sw, rowsum, w_out=None, clip: float = 1.0,
+                               outlier_idx=None, bits: int = 4, row_clip=None) -> None:
+    """rq_prepare_weights into caller-given outputs, with no workspace: the
+    library's per-GPU scratch array holds the KRON factors' inverses."""
+    import torch
+    _gpu(w, qw, sw, rowsum, w_out, outlier_idx, rot.p1, rot.p2, rot.chan_scale, row_clip)
+    N, K = w.shape
+    _want(w, "w", torch.float16, dense=False)
+    _want(outlier_idx, "outlier_idx", torch.int32)
+    _want(row_clip, "row_clip", torch.float32, (N,))
+    rot.check(K)
+    qd, n_out = _qdesc(False, clip, outlier_idx, bits, row_clip)
+    _want(qw, "qw", torch.uint8, (N, (K - n_out) if bits == 8 else (K - n_out) // 2))
+    _want(sw, "sw", torch.float32, (N,))
+    _want(rowsum, "rowsum", torch.int32, (N,))
+    _want(w_out, "w_out", torch.float16, (N, n_out))
+    rd = rot.desc()
+    st = lib().rq_prepare_weights_noalloc(_ptr(w), N, K, w.stride(0), ctypes.byref(rd), ctypes.byref(qd),
+                                          _ptr(qw), _ptr(sw), _ptr(rowsum), _ptr(w_out), _stream(w.device))
+    _check(st, "rq_prepare_weights_noalloc")
 
 
 def rq_search_weight_clip(w, outlier_idx=None, bits: int = 4, steps: int = 100, out=None):

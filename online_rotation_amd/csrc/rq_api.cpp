@@ -7,9 +7,22 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "rq_kernels.h"
 
 namespace {
+
+// Scratch memory of rq_prepare_weights_noalloc: the KRON factors' inverse
+// transposes (at most two 64 x 64 fp32 images, the second at a 256-byte
+// offset), in device memory that exists for the life of the process, one copy
+// per GPU.  Host code never uses the array's name as an address: each device's
+// copy is looked up once with hipGetSymbolAddress and the result is kept.
+constexpr int64_t kScratchBytes = 32768;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device id, under g_scratch_mu
 
 thread_local char g_err[512] = "";
 
@@ -156,6 +169,34 @@ int64_t rq_prepare_weights_workspace_bytes(const rq_rot_desc *rot) {
   if (!rot || rot->kind != RQ_ROT_KRON) return 0;
   const int64_t a = (int64_t)rot->n1 * rot->n1 * 4, b = (int64_t)rot->n2 * rot->n2 * 4;
   return ((a + 255) / 256) * 256 + b;
+}
+
+rq_status rq_prepare_weights_noalloc(const void *w, int64_t N, int64_t K, int64_t ldw, const rq_rot_desc *rot,
+                                     const rq_quant_desc *qd, uint8_t *qw, float *sw, int32_t *w_rowsum,
+                                     void *w_out, void *stream) {
+  if (!rot) return fail(RQ_EINVAL, "rot and qd descriptors are required");
+  const int64_t need = rq_prepare_weights_workspace_bytes(rot);
+  if (need > kScratchBytes)
+    return fail(RQ_ESHAPE, "the transform needs %lld bytes of scratch, above the %lld this entry point holds",
+                (long long)need, (long long)kScratchBytes);
+  void *ptr = nullptr;
+  if (need > 0 && N > 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(RQ_EINVAL, "device id %d is not below %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return hip_status(e, "hipGetSymbolAddress(scratch)");
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return rq_prepare_weights(w, N, K, ldw, rot, qd, qw, sw, w_rowsum, w_out, ptr, need > 0 ? kScratchBytes : 0,
+                            stream);
 }
 
 rq_status rq_prepare_weights(const void *w, int64_t N, int64_t K, int64_t ldw, const rq_rot_desc *rot,

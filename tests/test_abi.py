@@ -230,3 +230,20 @@ def test_clip_search_and_row_clip_validation():
     assert _rotate_quant(4, 4096, 4096, _rot("none"), rq._QuantDesc(0, 1.0, None, 0, 4, FAKE + 2)) == rq.RQ_EALIGN
     d = L.rq_quant_decode_linear
     assert d(FAKE, 8, 4096, 4096, ctypes.byref(rc), FAKE, FAKE, FAKE, 16, None, FAKE, 16, None) == rq.RQ_ESHAPE
+
+
+def test_prepare_weights_noalloc_validates_first():
+    L = rq.lib()
+    qd = _qd()
+    # no descriptor
+    assert L.rq_prepare_weights_noalloc(FAKE, 4, 4096, 4096, None, ctypes.byref(qd), FAKE, FAKE, FAKE, None,
+                                        None) == rq.RQ_EINVAL
+    # a shape check of the common path (KRON factors wider than 64) fails before the scratch lookup
+    rot = _rot("kron", n1=128, n2=32, p1=FAKE, p2=FAKE)
+    assert L.rq_prepare_weights_noalloc(FAKE, 4, 4096, 4096, ctypes.byref(rot), ctypes.byref(qd), FAKE, FAKE,
+                                        FAKE, None, None) == rq.RQ_ESHAPE
+    # asymmetric weights are rejected as by rq_prepare_weights
+    rot = _rot("none")
+    qa = _qd(asym=1)
+    assert L.rq_prepare_weights_noalloc(FAKE, 4, 4096, 4096, ctypes.byref(rot), ctypes.byref(qa), FAKE, FAKE,
+                                        FAKE, None, None) == rq.RQ_EINVAL
