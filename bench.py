@@ -21,7 +21,8 @@ two calls a few times, for `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` runs.
 
 `--workload quik8_down` runs the same step at 8 bits (QUIK-8B's form for
 the LLaMA-2-70B down projection: T=4096, K=28672, N=8192, 896 fp16 outlier
-columns; rq_w8a8_linear on INT8 matrix cores).
+columns; rq_w8a8_linear on INT8 matrix cores); `--workload quik8_decode` is
+that layer at decode (T=8), reported in GB/s against HBM.
 
 `--weight-prep` (with quik_prefill, quik_decode or quik8_down) times QUIK's
 offline weight side instead: rq_search_weight_clip (the per-channel clip
@@ -65,7 +66,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b",
                     choices=["tiny", "llama7b", "gsr", "flat", "quik_prefill", "quik_decode", "quik8_down",
-                             "kv"])
+                             "quik8_decode", "kv"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled per step (0: >640 MB)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,7 +83,7 @@ def parse():
 def gemm_kernel(T, Kb, n_out=0, bits=4):
     """The GEMM kernel the library dispatches to (launch_gemm's rules)."""
     if bits == 8:
-        return "gemm_ra"
+        return "gemm_decode8" if T <= 32 else "gemm_ra"
     if Kb % 64 == 0 and T <= 16 and T * (Kb // 16 + n_out // 8) <= 4096:
         return "gemm_decode16"
     if Kb % 64 == 0 and T <= 32:

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
 SOURCES = ["rq_api.cpp", "rotate_quant.hip", "kron.hip", "gemm_w4a4.hip", "gemm_ra.hip",
-           "gemm_decode.hip", "kv_quant.hip", "quant8.hip",
+           "gemm_decode.hip", "gemm_decode8.hip", "kv_quant.hip", "quant8.hip",
            "clip_search.hip"]
 ARCH = "gfx950"
 
@@ -26,7 +26,8 @@ HIPCC_FLAGS = [
 # MFMA accumulators in VGPRs (no AGPR copies) where a kernel fits in 256
 # VGPRs; gemm_ra and kron64_mfma keep their accumulators in AGPRs instead.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM, "gemm_decode.hip": VGPR_FORM}
+EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM, "gemm_decode.hip": VGPR_FORM,
+               "gemm_decode8.hip": VGPR_FORM}
 
 
 def _hipcc() -> str:

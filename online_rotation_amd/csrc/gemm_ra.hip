@@ -433,6 +433,7 @@ hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStrea
 }
 
 hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
+  if (p.T <= 32 && gemm_decode8_fits(p, mode)) return launch_gemm_decode8(p, x_unsigned, mode, st);
   const int nt_m = (int)((p.T + kRaBM - 1) / kRaBM), nt_n = (int)((p.N + kRaBN - 1) / kRaBN);
   const dim3 grid((unsigned)(nt_m * nt_n)), block(256);
   if (mode == 0) {

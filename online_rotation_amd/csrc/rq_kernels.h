@@ -64,8 +64,11 @@ hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, 
                               uint8_t *q, float *scale, int32_t *zero, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
-// one-byte codes (Kb = K bytes per row); x_unsigned: codes in [0, 255], p.rowsum required
+// one-byte codes (Kb = K bytes per row); x_unsigned: codes in [0, 255], p.rowsum required;
+// T <= 32 goes to gemm_decode8 when its activation stage fits LDS
 hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
+bool gemm_decode8_fits(const GemmArgs &p, int mode);
+hipError_t launch_gemm_decode8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 // quant8.hip: unrotated per-row INT8 with the outlier split
 size_t split8_smem_bytes(int64_t K);
 hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,

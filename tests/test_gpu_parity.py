@@ -910,6 +910,62 @@ def test_w8a8_gemm_i32_bit_exact(shape, unsigned):
     assert np.array_equal(host(acc), ref)
 
 
+# The decode-size 8-bit kernel (T <= 32): K split 4 ways (N < 16384), 2 ways
+# (16384 <= N < 32768, or T > 16 with 4 parts over 64 staged rows) and not at
+# all (N >= 32768); one or two blocks of 16 tokens; K parts of unequal length
+# and steps past the end of a part (K = 27776 = 434 steps, K = 64 = 1 step).
+D8_SHAPES = [(1, 27776, 100), (8, 27776, 8192), (16, 1024, 33), (17, 4096, 130), (32, 640, 16400),
+             (3, 64, 40000), (5, 4160, 2048), (32, 27776, 257)]
+
+
+@pytest.mark.parametrize("shape", D8_SHAPES, ids=[f"{t}x{k}x{n}" for t, k, n in D8_SHAPES])
+@pytest.mark.parametrize("unsigned", [True, False], ids=["u8", "s8"])
+def test_w8a8_decode_gemm_i32_bit_exact(shape, unsigned):
+    T, K, N = shape
+    note(f"[w8a8_gemm_i32 decode] T={T} K={K} N={N} unsigned={unsigned}")
+    rng = np.random.default_rng(T * 11 + K + N)
+    qx = rng.integers(0, 256, (T, K)) if unsigned else rng.integers(-127, 128, (T, K))
+    qw = rng.integers(-127, 128, (N, K))
+    qx[0, :] = 255 if unsigned else -127
+    qw[-1, :] = -127
+    ref = o.int_gemm(qx, qw)
+    rowsum = qw.sum(axis=1).astype(np.int32)
+    acc = rq.rq_w8a8_gemm_i32(dev(qx.astype(np.int16).astype(np.uint8)), dev(qw.astype(np.int16).astype(np.uint8)),
+                              x_unsigned=unsigned, w_rowsum=dev(rowsum) if unsigned else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), ref)
+
+
+@pytest.mark.parametrize("T,N,n_out", [(8, 8192, 896), (1, 300, 64), (16, 130, 0), (24, 2100, 896),
+                                       (32, 64, 64)])
+def test_w8a8_linear_decode_kernel(T, N, n_out):
+    """The 8-bit linear layer at decode sizes (the decode kernel: codes from
+    LDS phases, the outlier product split over the K parts and summed) against
+    the oracle, at the down projection's width."""
+    K = 28672
+    note(f"[w8a8_linear decode] T={T} K={K} N={N} n_out={n_out}")
+    inp = workloads.make_inputs("quik8_down", T=T, K=K, N=N)
+    x, w = inp["x"], inp["w"]
+    idx = inp["outlier_ch"][:n_out].astype(np.int32) if n_out else None
+    didx = dev(idx) if n_out else None
+    xr = o.rotate_quant(x, "none", asym=True, outlier_idx=idx, bits=8)
+    wr = o.prepare_weights(w, "none", outlier_idx=idx, bits=8)
+    xq = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), asym=True, outlier_idx=didx, bits=8)
+    wq = rq.rq_prepare_weights(dev(w), rq.Rotation("none"), outlier_idx=didx, bits=8)
+    y = rq.rq_w8a8_linear(xq["q"], xq["scale"], xq["zero"], wq["q"], wq["scale"], wq["rowsum"],
+                          xq["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(xq["q"]), xr["packed"]) and np.array_equal(host(wq["q"]), wr["packed"])
+    check_y(host(y), o.linear(xr, wr)["y"])
+    # symmetric activations (signed codes, no zero point)
+    xs = o.rotate_quant(x, "none", outlier_idx=idx, bits=8)
+    xqs = rq.rq_rotate_quant(dev(x), rq.Rotation("none"), outlier_idx=didx, bits=8)
+    ys = rq.rq_w8a8_linear(xqs["q"], xqs["scale"], None, wq["q"], wq["scale"], wq["rowsum"],
+                           xqs["x_out"], wq["w_out"])
+    torch.cuda.synchronize()
+    check_y(host(ys), o.linear(xs, wr)["y"])
+
+
 @pytest.mark.parametrize("n_out", [64, 0])
 def test_w8a8_linear_end_to_end(n_out):
     note(f"[w8a8_linear] T=70 K=2048 N=96 n_out={n_out}")
@@ -1063,8 +1119,9 @@ def test_8bit_quantizer_and_clip_search_strided_rows():
 
 @pytest.mark.parametrize("T", [1, 8, 16, 33])
 def test_w8a8_linear_decode_sizes(T):
-    """Decode-sized batches through the 8-bit linear layer (the 256-row tile
-    kernel with clamped rows), the full down-projection width."""
+    """Decode-sized batches through the 8-bit linear layer, the full
+    down-projection width: the decode kernel up to 32 rows, the 256-row tile
+    kernel with clamped rows above."""
     note(f"[w8a8_linear] decode T={T}")
     inp = workloads.make_inputs("quik8_down", T=T, K=28672, N=130)
     x, w, idx = inp["x"], inp["w"], inp["outlier_ch"].astype(np.int32)

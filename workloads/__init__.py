@@ -29,6 +29,7 @@ token, the failure case FlatQuant's article describes in its section 2.2):
            X [4096, 28672] N(0,1) with 896 outlier columns x40 kept in fp16
            (256 per 8192 input features, scaled to 28672), W [8192, 28672];
            per-token asymmetric INT8 activations, per-channel INT8 weights.
+  quik8_decode  the same layer at decode: the first 8 rows of that X.
 
 Draw order per workload (numpy Generator, PCG64): outlier channel indices
 (choice without replacement, sorted), X (standard normal, scaled, cast to fp16
@@ -93,6 +94,8 @@ WORKLOADS = {
                    n_outlier_ch=16, outlier_mult=30.0),
     "quik8_down": Workload("quik8_down", 6, 4096, 28672, 8192, "none", asym=True,
                            n_outlier_ch=896, outlier_mult=40.0, n_out=896, bits=8),
+    "quik8_decode": Workload("quik8_decode", 6, 4096, 28672, 8192, "none", asym=True,
+                             n_outlier_ch=896, outlier_mult=40.0, n_out=896, bits=8, decode_rows=8),
 }
 
 
