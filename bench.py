@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--weight-prep", action="store_true",
                     help="time QUIK's offline weight side instead: clip linear search + per-channel quantization")
+    ap.add_argument("--fused-decode", action="store_true",
+                    help="also time decode batches (T = 1 .. 16 of the workload's rows) as the quantizer + linear "
+                         "calls and as the one fused call (rotate_quant_decode)")
     ap.add_argument("--counters", action="store_true",
                     help="launch the calibration kernels and each call a few times, print one line")
     return ap.parse_args()
@@ -462,6 +465,83 @@ def quant_sweep(torch, rq, x0, rot, wl, idx, bits, Kqb, n_out, reps, stream):
     return out
 
 
+def fused_decode_sweep(torch, rq, x0, w_q, rot, wl, idx, reps, stream):
+    """Decode batches of the workload (its first T rows, T = 1, 2, 4, 8, 16)
+    through the two calls (rq_rotate_quant, then rq_w4a4_linear or
+    rq_mixed_outlier_linear) and through the one fused call
+    (rq_rotate_quant_decode_linear); per-step time of graphs of back-to-back
+    steps over weight copies totalling more than 640 MB, median of `reps`."""
+    dev = x0.device
+    mixed = wl.asym
+    N = w_q["q"].shape[0]
+    wbytes = sum(v.numel() * v.element_size() for k, v in w_q.items() if v is not None and k != "_workspace")
+    S = max(2, -(-(640 << 20) // wbytes))
+    ws = [{k: (v.clone() if v is not None and k != "_workspace" else v) for k, v in w_q.items()} for _ in range(S)]
+    out = []
+    for T in (1, 2, 4, 8, 16):
+        xs = [x0[:T].clone() for _ in range(S)]
+        ys = [torch.empty((T, N), dtype=torch.float16, device=dev) for _ in range(S)]
+        K = x0.shape[1]
+        n_out = wl.n_out if mixed else 0
+        xq = [{"q": torch.empty((T, (K - n_out) // 2), dtype=torch.uint8, device=dev),
+               "scale": torch.empty((T,), dtype=torch.float32, device=dev),
+               "zero": torch.empty((T,), dtype=torch.int32, device=dev) if mixed else None,
+               "x_out": torch.empty((T, n_out), dtype=torch.float16, device=dev) if mixed else None}
+              for _ in range(S)]
+
+        def two(i):
+            rq.rq_rotate_quant(xs[i], rot, clip=wl.clip_x, asym=mixed, outlier_idx=idx, out=xq[i])
+            if mixed:
+                rq.rq_mixed_outlier_linear(xq[i]["q"], xq[i]["scale"], xq[i]["zero"], ws[i]["q"], ws[i]["scale"],
+                                           ws[i]["rowsum"], xq[i]["x_out"], ws[i]["w_out"], out=ys[i])
+            else:
+                rq.rq_w4a4_linear(xq[i]["q"], xq[i]["scale"], ws[i]["q"], ws[i]["scale"], out=ys[i])
+
+        def fused(i):
+            rq.rq_rotate_quant_decode_linear(xs[i], rot, ws[i]["q"], ws[i]["scale"],
+                                             ws[i]["rowsum"] if mixed else None, ws[i]["w_out"], asym=mixed,
+                                             clip=wl.clip_x, outlier_idx=idx, out=ys[i])
+
+        row = {"T": T}
+        for name, fn in (("two_calls_us", two), ("fused_us", fused)):
+            for i in range(S):
+                fn(i)
+            torch.cuda.synchronize()
+            n = max(S, 32)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for j in range(n):
+                        fn(j % S)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            times = []
+            for _ in range(reps):
+                with torch.cuda.stream(stream):
+                    ev0.record(stream)
+                    g.replay()
+                    ev1.record(stream)
+                ev1.synchronize()
+                times.append(ev0.elapsed_time(ev1) / 1e3 / n)
+            row[name] = round(float(np.median(times)) * 1e6, 2)
+            del g
+        two(0)
+        torch.cuda.synchronize()
+        y_two = ys[0].clone()
+        fused(0)
+        torch.cuda.synchronize()
+        row["equal"] = bool(torch.equal(y_two, ys[0]))
+        row["fused_wins"] = row["fused_us"] < row["two_calls_us"]
+        out.append(row)
+        del xs, ys, xq
+    del ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -661,6 +741,8 @@ def main():
         "rotate_quant": quant,
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.fused_decode and bits == 4 and (wl.rot == "none" or (wl.rot in ("hadamard", "gsr") and K == 4096)):
+        rec["fused_decode"] = fused_decode_sweep(torch, rq, x0, wq0, rot, wl, idx, args.reps, stream)
     if args.sweep and T >= 2048:
         del xs, wqs, xq, ys, g_step, g_rot, g_gemm
         torch.cuda.synchronize()

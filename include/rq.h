@@ -236,6 +236,30 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
                                  const int32_t *w_rowsum, int64_t N, const void *w_out,
                                  void *y, int64_t ldy, void *stream);
 
+/* rq_rotate_quant_decode_linear -- rq_rotate_quant followed by the linear
+ * layer in one launch for decode batches, with the online transform: each
+ * workgroup transforms and quantizes the T activation rows into on-chip
+ * memory and streams its weight rows against them (the online transform
+ * fused with quantization, FlatQuant article section 2.3; the fused online
+ * Hadamard's cost, SpinQuant OpenReview, the authors' answers on inference
+ * overhead).
+ *   rot NONE      exactly rq_quant_decode_linear (same arguments and limits).
+ *   rot HADAMARD  (K == 4096) or GSR (K == 4096, block 8, 16, 32 or 64):
+ *                 qd symmetric 4-bit, no outliers, no row clips, clip_ratio
+ *                 in (0, 1]; the codes and scales are those of
+ *                 rq_rotate_quant(x, rot, qd) and y that of rq_w4a4_linear on
+ *                 them, bit for bit.  w_rowsum and w_out are ignored.
+ *   x fp16 [T, ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned; qw, sw as
+ *   written by rq_prepare_weights with the same rot; y out fp16 [T, ldy].
+ * 1 <= T <= 16 (T == 0 is a no-op); other shapes or transforms: RQ_ESHAPE.
+ * Every workgroup repeats the transform of all T rows, so the fused form
+ * pays off only for the smallest T (measured per T in the design notes). */
+rq_status rq_rotate_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ldx,
+                                        const rq_rot_desc *rot, const rq_quant_desc *qd,
+                                        const uint8_t *qw, const float *sw, const int32_t *w_rowsum,
+                                        int64_t N, const void *w_out, void *y, int64_t ldy,
+                                        void *stream);
+
 /* rq_kv_rotate_quant -- the KV-cache quantizer: R3, a normalized
  * Walsh-Hadamard transform over each head's `group` channels (SpinQuant
  * OpenReview: the authors' answer on the number of rotation matrices, R3

@@ -24,13 +24,15 @@ ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
            "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
-           "rq_prepare_weights_noalloc", "rq_status_string", "rq_last_error", "rq_abi_version", "EXPORTS"]
+           "rq_prepare_weights_noalloc", "rq_rotate_quant_decode_linear", "rq_status_string", "rq_last_error",
+           "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
            "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
-           "rq_prepare_weights_noalloc", "rq_status_string", "rq_last_error", "rq_abi_version")
+           "rq_prepare_weights_noalloc", "rq_rotate_quant_decode_linear", "rq_status_string", "rq_last_error",
+           "rq_abi_version")
 
 
 class RqError(RuntimeError):
@@ -78,11 +80,13 @@ def lib() -> ctypes.CDLL:
         L.rq_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), vp, vp,
                                              vp, i64, vp, vp, i64, vp]
         L.rq_kv_rotate_quant.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.rq_rotate_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
+                                                    ctypes.POINTER(_QuantDesc), vp, vp, vp, i64, vp, vp, i64, vp]
         L.rq_w8a8_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, vp, i64, vp]
         L.rq_w8a8_gemm_i32.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp, i64, vp]
         L.rq_search_weight_clip.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), i32, vp, vp]
         for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_prepare_weights_noalloc", "rq_w4a4_linear",
-                   "rq_mixed_outlier_linear",
+                   "rq_mixed_outlier_linear", "rq_rotate_quant_decode_linear",
                    "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_w8a8_linear",
                    "rq_w8a8_gemm_i32", "rq_search_weight_clip"):
             getattr(L, fn).restype = ctypes.c_int
@@ -342,6 +346,32 @@ def rq_quant_decode_linear(x, qw, sw, w_rowsum=None, w_out=None, asym: bool = Fa
                                       _ptr(w_rowsum), N, _ptr(w_out), _ptr(y), y.stride(0),
                                       _stream(x.device))
     _check(st, "rq_quant_decode_linear")
+    return y
+
+
+def rq_rotate_quant_decode_linear(x, rot: Rotation, qw, sw, w_rowsum=None, w_out=None, asym: bool = False,
+                                  clip: float = 1.0, outlier_idx=None, out=None):
+    """rq_rotate_quant (with its online transform) + the linear layer in one
+    launch for T <= 16 rows: x fp16 [T, K] -> y fp16 [T, N]."""
+    import torch
+    _gpu(x, qw, sw, w_rowsum, w_out, outlier_idx, out, rot.p1, rot.p2, rot.chan_scale)
+    T, K = x.shape
+    N = qw.shape[0]
+    _want(x, "x", torch.float16, dense=False)
+    _want(outlier_idx, "outlier_idx", torch.int32)
+    rot.check(K)
+    qd, n_out = _qdesc(asym, clip, outlier_idx)
+    _want(qw, "qw", torch.uint8, (N, (K - n_out) // 2))
+    _want(sw, "sw", torch.float32, (N,))
+    _want(w_rowsum, "w_rowsum", torch.int32, (N,))
+    _want(w_out, "w_out", torch.float16, (N, n_out))
+    y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=x.device)
+    _want(y, "out", torch.float16, (T, N), dense=False)
+    rd = rot.desc()
+    st = lib().rq_rotate_quant_decode_linear(_ptr(x), T, K, x.stride(0), ctypes.byref(rd), ctypes.byref(qd),
+                                             _ptr(qw), _ptr(sw), _ptr(w_rowsum), N, _ptr(w_out), _ptr(y),
+                                             y.stride(0), _stream(x.device))
+    _check(st, "rq_rotate_quant_decode_linear")
     return y
 
 

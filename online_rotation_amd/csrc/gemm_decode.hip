@@ -17,6 +17,7 @@
 //     ring's prologue.
 #include <algorithm>
 
+#include "fwht_common.h"
 #include "gemm_common.h"
 #include "rq_kernels.h"
 #include "split_common.h"
@@ -378,7 +379,44 @@ __device__ __forceinline__ void stage_fused(const GemmArgs &p, const FuseArgs &f
   }
 }
 
-template <bool XU, int MODE, int G>
+// The rotated fused staging step (G = 0, RG > 0: 1 Walsh-Hadamard, 2 with a
+// clip ratio below 1, 3 GSR, 4 GSR clipped), K = 4096: wavefront w takes rows
+// w, w + nwaves, ..., each through fwht_token (the standalone quantizer's
+// transform and arithmetic, so the codes are its codes), and writes the 2 KB
+// of packed codes into its LDS code row and the scale beside it.  The weight
+// ring's first loads go out as soon as the first row's loads are issued.
+template <int RG, typename Prologue>
+__device__ __forceinline__ void stage_rotated(const FuseArgs &f, uint8_t *xs, uint32_t pa, uint32_t T, float *sxl,
+                                              Prologue prologue) {
+  constexpr bool GSR = RG >= 3, CLAMP = RG == 2 || RG == 4;
+  __shared__ uint4 ltab[GSR ? 8 : 16][64];
+  __shared__ v4w stage[8][32 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t nthr = blockDim.x, nwaves = nthr >> 6;
+  auto load = [&](v4w (&raw)[8], uint32_t t) {
+    const v4w *row = reinterpret_cast<const v4w *>(f.x + (int64_t)t * f.ldx);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) raw[c] = row[64 * c + lane];
+  };
+  v4w raw[8];
+  load(raw, min(wave, T - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  prologue();
+  __builtin_amdgcn_sched_barrier(0);
+  fwht_load_tables<GSR>(ltab, f.gsr_log2, tid, (int)nthr);
+  __syncthreads();
+  for (uint32_t t = wave; t < T; t += nwaves) {
+    if (t != wave) load(raw, t);
+    const FwhtOut o = fwht_token<GSR, false, CLAMP>(raw, stage[wave], ltab, f.norm, f.clip);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      *reinterpret_cast<v4w *>(xs + t * pa + 32 * (r32 + 32 * nb) + 16 * g) = o.code[nb];
+    if (lane == 0) sxl[t] = o.s;
+  }
+}
+
+template <bool XU, int MODE, int G, int RG = 0>
 __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   extern __shared__ __align__(16) uint8_t xs[];
   __shared__ float sxl[16];  // the rows' scales and zero points (G = 0: made here; else staged)
@@ -387,10 +425,15 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, l16 = lane & 15;
   const uint32_t nthr = blockDim.x;
-  const int64_t n0 = ((int64_t)blockIdx.x * (nthr >> 6) + wave) * 16, Kb = p.Kb;
+  // f.ks wavefronts share each block of 16 channels, each streaming one part
+  // of its k-steps (INT4 steps, then outlier steps, each split f.ks ways)
+  const int ks = f.ks, cb = (int)(nthr >> 6) / ks;
+  const int part = wave / cb, cbk = wave - part * cb;
+  const int64_t n0 = ((int64_t)blockIdx.x * cb + cbk) * 16, Kb = p.Kb;
   const int nsteps = (int)(Kb >> 6), last = nsteps - 1;
   const int nk = MODE == 2 ? p.n_out / 32 : 0;  // outlier steps
-  const int S = nsteps + nk;
+  const int qs = (nsteps + ks - 1) / ks, qk = (nk + ks - 1) / ks;  // steps per part
+  const int j0 = part * qs, o0 = part * qk, L = qs + qk;
   const uint32_t T = (uint32_t)p.T;
   // G = 0 rows have room for all K codes, so that a list with repeated
   // indices (fewer distinct outliers) cannot run a row into the next one
@@ -401,15 +444,21 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const int64_t nrow = min(n0 + l16, p.N - 1);
   const uint8_t *bp = p.qw + nrow * Kb + 16 * kg;
   const uint8_t *wp = nk ? reinterpret_cast<const uint8_t *>(p.wo + nrow * p.n_out) + 16 * kg : bp;
-  auto src = [&](int j) {
-    return j < nsteps ? bp + 64 * (int64_t)j : wp + 64 * (int64_t)min(j - nsteps, nk - 1);
+  // the part's local step i, clamped into the stream
+  auto src = [&](int i) {
+    return i < qs ? bp + 64 * (int64_t)min(j0 + i, last) : wp + 64 * (int64_t)max(min(o0 + i - qs, nk - 1), 0);
   };
 
   uint4 rb[kD16];
-  if constexpr (G == 0) {
+  if constexpr (G == 0 && RG != 0) {
+    stage_rotated<RG>(f, xs, pa, T, sxl, [&] {
+#pragma unroll
+      for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
+    });
+  } else if constexpr (G == 0) {
     stage_fused<XU>(p, f, xs, pa, po, xo_base, T, nk, sxl, zxl, [&] {
 #pragma unroll
-      for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
+      for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     });
   } else {
     // Staging: 16-byte chunks c < na are activation codes (row c / ka), the
@@ -441,7 +490,7 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     // for the latter below leaves it in flight
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, S - 1)));
+    for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     __builtin_amdgcn_sched_barrier(0);
     {
       const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
@@ -467,7 +516,9 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     }
   }
   __syncthreads();
-  if (n0 >= p.N) return;  // whole wavefront past the last channel (after its share of the staging)
+  // a wavefront past the last channel leaves (after its share of the
+  // staging) unless it must meet the others again to add the parts
+  if (ks == 1 && n0 >= p.N) return;
 
   const uint32_t arow = min((uint32_t)l16, T - 1);
   const uint8_t *xa = xs + arow * pa + 16 * kg;
@@ -480,30 +531,56 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
   v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   v4f fo = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kb0 = 0; kb0 < S; kb0 += kD16) {
+  for (int i0 = 0; i0 < L; i0 += kD16) {
 #pragma unroll
     for (int u = 0; u < kD16; ++u) {
-      const int j = kb0 + u;
+      const int i = i0 + u;
       const uint4 wq = rb[u];
-      const uint32_t l4 = j < nsteps ? 0xFFFFFFFFu : 0u;
-      const uint4 wa = *reinterpret_cast<const uint4 *>(xa + 64 * min(j, last));
+      const uint32_t l4 = (i < qs && j0 + i < nsteps) ? 0xFFFFFFFFu : 0u;
+      const uint4 wa = *reinterpret_cast<const uint4 *>(xa + 64 * min(j0 + i, last));
       const v4i a0 = XU ? widen_unsigned(wa.x & l4, wa.y & l4) : widen_signed(wa.x & l4, wa.y & l4);
       const v4i a1 = XU ? widen_unsigned(wa.z & l4, wa.w & l4) : widen_signed(wa.z & l4, wa.w & l4);
       const v4i b0 = widen_signed(wq.x, wq.y), b1 = widen_signed(wq.z, wq.w);
       v8h ao, bo;
       if (MODE == 2) {
-        const uint32_t lo = (j >= nsteps && j < S) ? 0xFFFFFFFFu : 0u;
-        const uint4 xv = *reinterpret_cast<const uint4 *>(xoa + 64 * max(min(j - nsteps, nk - 1), 0));
+        const int jo = o0 + i - qs;
+        const uint32_t lo = (i >= qs && i < L && jo < nk) ? 0xFFFFFFFFu : 0u;
+        const uint4 xv = *reinterpret_cast<const uint4 *>(xoa + 64 * max(min(jo, nk - 1), 0));
         const uint4 am = {xv.x & lo, xv.y & lo, xv.z & lo, xv.w & lo};
         const uint4 bm = {wq.x & lo, wq.y & lo, wq.z & lo, wq.w & lo};
         __builtin_memcpy(&ao, &am, 16);
         __builtin_memcpy(&bo, &bm, 16);
       }
       __builtin_amdgcn_sched_barrier(0);
-      rb[u] = *reinterpret_cast<const uint4 *>(src(min(j + kD16, S - 1)));
+      rb[u] = *reinterpret_cast<const uint4 *>(src(min(i + kD16, L - 1)));
       acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc1, 0, 0, 0);
       if (MODE == 2) fo = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, fo, 0, 0, 0);
+    }
+  }
+  if (ks > 1) {
+    // the parts' sums meet in LDS (the staged rows are free once every
+    // wavefront is past its loop); part 0 adds them in part order
+    __syncthreads();
+    uint32_t *red = reinterpret_cast<uint32_t *>(xs);
+    if (part > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        red[(wave * 12 + r) * 64 + lane] = (uint32_t)acc0[r];
+        red[(wave * 12 + 4 + r) * 64 + lane] = (uint32_t)acc1[r];
+        red[(wave * 12 + 8 + r) * 64 + lane] = __float_as_uint(fo[r]);
+      }
+    }
+    __syncthreads();
+    if (part > 0 || n0 >= p.N) return;
+    for (int q = 1; q < ks; ++q) {
+      const int w2 = q * cb + cbk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc0[r] += (int)red[(w2 * 12 + r) * 64 + lane];
+        acc1[r] += (int)red[(w2 * 12 + 4 + r) * 64 + lane];
+        fo[r] += __uint_as_float(red[(w2 * 12 + 8 + r) * 64 + lane]);
+      }
     }
   }
 
@@ -531,6 +608,24 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   }
 }
 
+// Waves per workgroup (w) and K parts (ks) for N channels of `steps` k-steps
+// (INT4 and outlier steps).  One wavefront streams each block of 16 channels
+// whole, w sized so that the workgroups spread evenly over the 256 CUs
+// (N = 28672 takes 256 of 7; 448 of 4 left 64 CUs with half the work of the
+// rest and measured 11% slower).  With fewer than 1024 blocks and long rows
+// the blocks' k-steps are split over ks = 2 .. 8 wavefronts of 8-wavefront
+// workgroups, towards 2048 weight streams, as long as each part keeps at
+// least 32 steps: split into 8-step parts, the 4096-wide rows of N = 11008
+// measured 35% slower (every stream a single round trip, 22 MB requested at
+// once) and N = 4096 no faster.
+static void d16_grid(int64_t N, int64_t steps, int &w, int &ks) {
+  const int64_t rb = (N + 15) / 16;
+  ks = 1;
+  while (rb < 1024 && ks < 8 && rb * ks < 2048 && steps / (2 * ks) >= 32) ks *= 2;
+  w = ks > 1 ? 8 : (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
+}
+constexpr size_t kD16Reduce = 8 * 12 * 64 * 4;  // LDS for adding the parts
+
 bool gemm_decode_fits(const GemmArgs &p) { return p.T <= 32 && p.Kb % 64 == 0 && p.Kb >= 64; }
 
 hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st) {
@@ -541,10 +636,12 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
     // workgroups of 7 (448 of 4 left 64 CUs with half the work of the rest
     // and measured 11% slower); at least 4, at most 8
     const int64_t rb = (p.N + 15) / 16;
-    const int w = (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
-    const dim3 grid((unsigned)((rb + w - 1) / w)), block(64 * w);
+    int w, ks;
+    d16_grid(p.N, p.Kb / 64 + n_out / 32, w, ks);
+    const int cb = w / ks;
+    const dim3 grid((unsigned)((rb + cb - 1) / cb)), block(64 * w);
     const bool g2 = d16_chunks(p.T, p.Kb, n_out) > 8 * 64 * w;
-    const size_t lds = d16_lds(p.T, p.Kb, n_out);
+    const size_t lds = std::max(d16_lds(p.T, p.Kb, n_out), ks > 1 ? kD16Reduce : 0);
     void (*k)(GemmArgs, FuseArgs);
     if (g2)
       k = mode == 0   ? (x_unsigned ? gemm_decode16<true, 0, 2> : gemm_decode16<false, 0, 2>)
@@ -559,7 +656,9 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    k<<<grid, block, lds, st>>>(p, FuseArgs{});
+    FuseArgs f{};
+    f.ks = ks;
+    k<<<grid, block, lds, st>>>(p, f);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((p.N + 127) / 128)), block(256);
@@ -581,16 +680,44 @@ static size_t fused_lds(int64_t T, int64_t K, int64_t n_out) {
   return (size_t)T * d16_pitch(K / 2) + (n_out ? (size_t)T * d16_pitch(2 * n_out) + 2 * (size_t)n_out : 0);
 }
 
+bool decode_fused_rot_fits(const GemmArgs &p, const FuseArgs &f) {
+  return p.T >= 1 && p.T <= 16 && f.K == 4096 && p.Kb == 2048 && p.n_out == 0 && f.gsr_log2 >= 0 &&
+         f.gsr_log2 <= 6 && f.gsr_log2 != 1 && f.gsr_log2 != 2;
+}
+
+hipError_t launch_decode_fused_rot(const GemmArgs &p, const FuseArgs &f0, hipStream_t st) {
+  const int64_t rb = (p.N + 15) / 16;
+  int w, ks;
+  d16_grid(p.N, p.Kb / 64, w, ks);
+  FuseArgs f = f0;
+  f.ks = ks;
+  const int cb = w / ks;
+  const dim3 grid((unsigned)((rb + cb - 1) / cb)), block(64 * w);
+  const size_t lds = std::max((size_t)p.T * d16_pitch(2048), ks > 1 ? kD16Reduce : 0);
+  const bool gsr = f.gsr_log2 != 0, clamp = f.clip < 1.0f;
+  void (*k)(GemmArgs, FuseArgs) = gsr ? (clamp ? gemm_decode16<false, 1, 0, 4> : gemm_decode16<false, 1, 0, 3>)
+                                      : (clamp ? gemm_decode16<false, 1, 0, 2> : gemm_decode16<false, 1, 0, 1>);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  k<<<grid, block, lds, st>>>(p, f);
+  return hipGetLastError();
+}
+
 bool decode_fused_fits(const GemmArgs &p, const FuseArgs &f) {
   return p.T >= 1 && p.T <= 16 && f.K % 32 == 0 && f.K <= 8192 && p.Kb % 64 == 0 && p.Kb >= 64 &&
          2 * p.Kb + p.n_out == f.K && fused_lds(p.T, f.K, p.n_out) <= 96 * 1024;
 }
 
-hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f, bool asym, int mode, hipStream_t st) {
+hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f0, bool asym, int mode, hipStream_t st) {
   const int64_t rb = (p.N + 15) / 16;
-  const int w = (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
-  const dim3 grid((unsigned)((rb + w - 1) / w)), block(64 * w);
-  const size_t lds = fused_lds(p.T, f.K, mode == 2 ? p.n_out : 0);
+  int w, ks;
+  d16_grid(p.N, p.Kb / 64 + (mode == 2 ? p.n_out / 32 : 0), w, ks);
+  FuseArgs f = f0;
+  f.ks = ks;
+  const int cb = w / ks;
+  const dim3 grid((unsigned)((rb + cb - 1) / cb)), block(64 * w);
+  const size_t lds = std::max(fused_lds(p.T, f.K, mode == 2 ? p.n_out : 0), ks > 1 ? kD16Reduce : 0);
   void (*k)(GemmArgs, FuseArgs) = mode == 1 ? gemm_decode16<false, 1, 0>
                                   : asym    ? gemm_decode16<true, 2, 0>
                                             : gemm_decode16<false, 2, 0>;

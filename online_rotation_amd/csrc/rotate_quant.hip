@@ -14,6 +14,7 @@
 //                    scaling and clipping (FlatQuant article, section 2.3).
 //   kron_inverse_t   fp64 Gauss-Jordan inverse-transpose of a Kronecker
 //                    factor, for the weight side of the affine transform.
+#include "fwht_common.h"
 #include "rq_device.h"
 #include "rq_kernels.h"
 #include "split_common.h"
@@ -164,155 +165,8 @@ __global__ __launch_bounds__(256) void fwht4096_quant(const __half *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// fwht4096_mfma: the same transforms on FP16 matrix cores.
-//
-// A 4096-wide row viewed as M[a][b] = x[64a + b] (64 x 64).  Since
-// H_4096 = H_64 kron H_64, x . H_4096 / 64 = H_64 . M . H_64 / 64, two 64^3
-// products; a GSR row with blocks of B <= 64 is the single product M . G,
-// G = blockdiag(Wal_B).  Both run on v_mfma_f32_32x32x16_f16:
-//   - the fp16 input is exact as an MFMA operand and +-2^k are exact fp16
-//     values, so the first product only rounds in its fp32 accumulation;
-//   - the second Hadamard product takes its fp32 input as hi + lo fp16
-//     (hi rounded to nearest, lo the remainder), 2^-22 relative.  So that lo
-//     never falls into fp16 subnormals, the first product is scaled by a
-//     per-row power of two chosen from the exponent of max|x| (exact), which
-//     puts the largest intermediate just below 2^15; the quantizer divides
-//     it out again (exact).
-// Constant operands come from compile-time sign tables (16 bytes per lane),
-// staged in LDS once per workgroup.  Up to 2048 tokens, one wavefront per
-// token; beyond, each wavefront takes an even number of tokens and loads the
-// next one while it computes the current one.
-// Output layout (both cases): accumulator [mb][nb] register r of lane
-// (r32, g) holds element 64*(r32 + 32*nb) + 32*mb + 8*(r/4) + 4*g + r%4,
-// so four consecutive elements share a lane and a lane pair (l, l+32)
-// swaps halves (v_permlane32_swap) into 16 contiguous packed bytes.
+// fwht4096_mfma: the same transforms on FP16 matrix cores (fwht_common.h).
 // ---------------------------------------------------------------------------
-constexpr int cpopc(uint32_t v) {
-  int c = 0;
-  while (v) {
-    c += (int)(v & 1u);
-    v >>= 1;
-  }
-  return c;
-}
-constexpr uint32_t cbitrev(uint32_t v, int bits) {
-  uint32_t r = 0;
-  for (int i = 0; i < bits; ++i) r |= ((v >> i) & 1u) << (bits - 1 - i);
-  return r;
-}
-
-struct OpTab {
-  uint32_t w[8][64][4];  // [operand][lane][dword]: 8 fp16 values per lane
-};
-
-// Step 1 of the Hadamard product, B = H_64: operand (cb, kc) of lane
-// (r32, g) is column b' = r32 + 32*cb, slot s is row b = 16*kc + 8*g + s.
-// Only the sign bits are stored; the kernel ORs in a per-row magnitude.
-constexpr OpTab make_had1() {
-  OpTab t{};
-  for (int cb = 0; cb < 2; ++cb)
-    for (int kc = 0; kc < 4; ++kc)
-      for (int l = 0; l < 64; ++l)
-        for (int s = 0; s < 8; ++s) {
-          const uint32_t col = (l & 31) + 32 * cb, b = 16 * kc + 8 * (l >> 5) + s;
-          const uint32_t sign = (uint32_t)(cpopc(b & col) & 1);
-          t.w[cb * 4 + kc][l][s / 2] |= (sign << 15) << (16 * (s & 1));
-        }
-  return t;
-}
-// Step 2, B = H_64 (+-1): operand (nb, rb, c) of lane (r32, g) is column
-// a' = r32 + 32*nb; slot s is row a = 32*rb + 16*c + 8*(s/4) + 4*g + s%4,
-// the row the step-1 accumulator register 8*c + s of that lane holds.
-constexpr OpTab make_had2() {
-  OpTab t{};
-  for (int nb = 0; nb < 2; ++nb)
-    for (int rb = 0; rb < 2; ++rb)
-      for (int c = 0; c < 2; ++c)
-        for (int l = 0; l < 64; ++l)
-          for (int s = 0; s < 8; ++s) {
-            const uint32_t col = (l & 31) + 32 * nb;
-            const uint32_t a = 32 * rb + 16 * c + 8 * (s >> 2) + 4 * (l >> 5) + (s & 3);
-            const uint32_t v = 0x3C00u | ((uint32_t)(cpopc(a & col) & 1) << 15);
-            t.w[(nb * 2 + rb) * 2 + c][l][s / 2] |= v << (16 * (s & 1));
-          }
-  return t;
-}
-// GSR, A = G^T with G = blockdiag(Wal_B): operand (mb, kc) of lane (r32, g)
-// is output j = r32 + 32*mb, slot s is input b = 16*kc + 8*g + s;
-// G[b][j] = H_B[sigma(b%B)][j%B] inside a block (sigma = bitrev o gray:
-// row sigma(s) of H_B is the one with s sign changes), 0 across blocks.
-constexpr OpTab make_gsr(int blog2) {
-  OpTab t{};
-  const uint32_t B = 1u << blog2, bm = B - 1;
-  for (int mb = 0; mb < 2; ++mb)
-    for (int kc = 0; kc < 4; ++kc)
-      for (int l = 0; l < 64; ++l)
-        for (int s = 0; s < 8; ++s) {
-          const uint32_t j = (l & 31) + 32 * mb, b = 16 * kc + 8 * (l >> 5) + s;
-          uint32_t v = 0;
-          if ((b >> blog2) == (j >> blog2)) {
-            const uint32_t bl = b & bm, sig = cbitrev(bl ^ (bl >> 1), blog2);
-            v = 0x3C00u | ((uint32_t)(cpopc(sig & (j & bm)) & 1) << 15);
-          }
-          t.w[mb * 4 + kc][l][s / 2] |= v << (16 * (s & 1));
-        }
-  return t;
-}
-
-__device__ const OpTab kHad1 = make_had1();
-__device__ const OpTab kHad2 = make_had2();
-__device__ const OpTab kGsr8 = make_gsr(3);
-__device__ const OpTab kGsr16 = make_gsr(4);
-__device__ const OpTab kGsr32 = make_gsr(5);
-__device__ const OpTab kGsr64 = make_gsr(6);
-
-__device__ __forceinline__ uint4 tab_load(const OpTab &t, int op, int lane) {
-  return *reinterpret_cast<const uint4 *>(&t.w[op][lane][0]);
-}
-
-__device__ __forceinline__ v8h as_h8(uint4 u) {
-  v8h h;
-  __builtin_memcpy(&h, &u, 16);
-  return h;
-}
-
-__device__ __forceinline__ v16f mfma16(uint4 a, uint4 b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
-}
-
-// Split eight fp32 values into fp16 hi (nearest) and lo (remainder) operands.
-// hi is one v_cvt_pk_f16_f32 per pair (round to nearest even); the remainder
-// f - hi is exact in fp32 and comes from one mixed-precision fma per value
-// (v_fma_mix_f32: the fp16 operand widened inside the fma), then one pair
-// conversion.  `neg1` is -1.0 held in a register the compiler cannot see
-// through: with a literal -1 the fma folds to a subtraction that needs a
-// separate fp16 -> fp32 conversion of hi.
-__device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo, float neg1) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const h2 ab = __builtin_convertvector((f2){f[2 * j], f[2 * j + 1]}, h2);
-    const float ra = __builtin_fmaf((float)ab.x, neg1, f[2 * j]);
-    const float rb = __builtin_fmaf((float)ab.y, neg1, f[2 * j + 1]);
-    const h2 lr = __builtin_convertvector((f2){ra, rb}, h2);
-    __builtin_memcpy(&h[j], &ab, 4);
-    __builtin_memcpy(&l[j], &lr, 4);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// max over the wave of values below 2^24 (exact as floats)
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return (uint32_t)wave_max((float)v); }
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// kMagic8 (split_common.h) = 1.5 * 2^23 + 8: fma(v, inv, kMagic8) = kMagic8 +
-// rne(v*inv) for |v*inv| < 2^22, so the low nibble of the result's bit
-// pattern is the code + 8.
-
 // CLAMP: clip ratio below 1.  At clip 1, |x'| <= amax gives |x' / s| <= 7
 // (1 + 2^-22) and the rounded code never leaves [-7, 7], so the clamp is
 // dropped; non-finite inputs then leave byte-clean NaN patterns (nibble 0).
@@ -330,21 +184,7 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
   // Constant operands, staged in LDS once per workgroup: read through
   // lgkmcnt, waiting for them never waits for a token prefetch in flight.
   __shared__ uint4 ltab[GSR ? 8 : 16][64];
-  {
-    const OpTab &t1 = GSR ? (blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8) : kHad1;
-    constexpr int nop = GSR ? 8 : 16;
-    uint4 v[nop / 4];
-#pragma unroll
-    for (int j = 0; j < nop / 4; ++j) {
-      const int e = j * 256 + threadIdx.x, op = e >> 6, l = e & 63;
-      v[j] = op < 8 ? tab_load(t1, op, l) : tab_load(kHad2, op - 8, l);
-    }
-#pragma unroll
-    for (int j = 0; j < nop / 4; ++j) {
-      const int e = j * 256 + threadIdx.x;
-      ltab[e >> 6][e & 63] = v[j];
-    }
-  }
+  fwht_load_tables<GSR>(ltab, blog2, threadIdx.x, 256);
   __syncthreads();
   if (t0 >= T) return;
 
@@ -359,166 +199,24 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
   // layout, each load instruction touched 32 rows 128 bytes apart.  In the
   // stage, column j of row a sits at j ^ ((a >> 1) & 7), so that both the
   // row-wise writes and the 16-lane column reads hit distinct banks.
-  typedef uint32_t v4w __attribute__((ext_vector_type(4)));  // a register vector, not a struct
   __shared__ v4w stage[4][32 * 8];
   auto load = [&](v4w (&raw)[8], int64_t t) {
     const v4w *row = reinterpret_cast<const v4w *>(x + t * ldx);
 #pragma unroll
     for (int c = 0; c < 8; ++c) raw[c] = __builtin_nontemporal_load(&row[64 * c + lane]);
   };
-  auto swz = [](int a, int j) { return a * 8 + (j ^ ((a >> 1) & 7)); };
 
   // transform, scale, quantize and store token t
   auto body = [&](const v4w (&raw)[8], int64_t t) {
-    v4w *st = stage[wave];
-    uint4 mop[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) st[swz(8 * c + (lane >> 3), lane & 7)] = raw[4 * rb + c];
-      wave_lds_sync();
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const v4w v = st[swz(r32, 2 * kc + g)];
-        mop[rb][kc] = make_uint4(v.x, v.y, v.z, v.w);
-      }
-      wave_lds_sync();  // the stage is free again once these reads are done
-    }
-    v16f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    float nrm = norm;
-
-    if (GSR) {
-      // C[j][a] = sum_b G[b][j] M[a][b]: A = G^T (table), B = M (column a = lane).
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint4 a = ltab[mb * 4 + kc][lane];
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, mop[nb][kc], acc[mb][nb]);
-        }
-    } else {
-      // per-row scale 2^sx: step-1 operand magnitude 2^(te-15), te = min(38 - e, 30)
-      // with e the fp16 exponent field of max|x|, so |P * 2^sx| < 2^15.
-      uint32_t mx = 0;
-      {
-        u16x2 m2 = {0, 0};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const uint32_t d[4] = {mop[rb][kc].x, mop[rb][kc].y, mop[rb][kc].z, mop[rb][kc].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              u16x2 v;
-              const uint32_t dm = d[i] & 0x7FFF7FFFu;
-              __builtin_memcpy(&v, &dm, 4);
-              m2 = __builtin_elementwise_max(m2, v);
-            }
-          }
-        mx = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
-      }
-      float neg1 = -1.0f;
-      asm volatile("" : "+v"(neg1));
-      const int e = (int)((mx >> 10) & 0x1Fu);
-      const int te = min(38 - e, 30);
-      const uint32_t mag = (uint32_t)te << 10, magd = mag | (mag << 16);
-      nrm = __builtin_ldexpf(1.0f, 9 - te);  // undoes 2^(te - 9)
-      // step 1: P = M . H_64 * 2^(te-15), lanes <-> column b', registers <-> row a
-      v16f p[2][2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[rb][cb][r] = 0.0f;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          uint4 hb = ltab[cb * 4 + kc][lane];
-          hb.x |= magd;
-          hb.y |= magd;
-          hb.z |= magd;
-          hb.w |= magd;
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) p[rb][cb] = mfma16(mop[rb][kc], hb, p[rb][cb]);
-        }
-      }
-      // step 2: Y^T[b'][a'] = sum_a P[a][b'] H_64[a][a'] with A = P^T taken
-      // straight from the step-1 accumulators.
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            float f[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) f[s] = p[rb][mb][8 * c + s];
-            uint4 hi, lo;
-            split8(f, hi, lo, neg1);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const uint4 hb = ltab[8 + (nb * 2 + rb) * 2 + c][lane];
-              acc[mb][nb] = mfma16(hi, hb, acc[mb][nb]);
-              acc[mb][nb] = mfma16(lo, hb, acc[mb][nb]);
-            }
-          }
-        }
-      }
-    }
-
-    // per-row symmetric scale from the normalized absmax
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][j][r]));
-    amax = wave_max(amax) * nrm;
-    float s, inv;
-    sym_scale(amax, clip, s, inv);
-    const float invn = inv * nrm;
-    const float lo_c = kMagic8 - 7.0f, hi_c = kMagic8 + 7.0f;
-    float csum = 0.0f;
+    const FwhtOut o = fwht_token<GSR, CSUM, CLAMP>(raw, stage[wave], ltab, norm, clip);
     uint8_t *qrow = q + t * 2048;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      uint32_t d[4];
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        uint32_t h[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          uint32_t bits[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float f = __builtin_fmaf(acc[mb][nb][4 * j4 + i], invn, kMagic8);
-            if (CLAMP) f = __builtin_amdgcn_fmed3f(f, lo_c, hi_c);
-            if (CSUM) csum += f - kMagic8;
-            __builtin_memcpy(&bits[i], &f, 4);
-          }
-          // low byte of bits[i] is code+8 in [1, 15]; pack pairs, then bytes
-          const uint32_t p01 = (bits[1] << 4) | bits[0];
-          const uint32_t p23 = (bits[3] << 4) | bits[2];
-          h[mb] = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);
-        }
-        auto sw = __builtin_amdgcn_permlane32_swap(h[0], h[1], false, false);
-        d[j4] = ((uint32_t)sw[0] | ((uint32_t)sw[1] << 16)) ^ 0x88888888u;  // offset -> two's complement
-      }
-      __builtin_nontemporal_store((v4w){d[0], d[1], d[2], d[3]}, reinterpret_cast<v4w *>(qrow + 32 * (r32 + 32 * nb) + 16 * g));
+    for (int nb = 0; nb < 2; ++nb)
+      __builtin_nontemporal_store(o.code[nb], reinterpret_cast<v4w *>(qrow + 32 * (r32 + 32 * nb) + 16 * g));
+    if (lane == 0) {
+      if (CSUM) code_sum[t] = o.csum;
+      scale[t] = o.s;
     }
-    if (CSUM) {
-      const int cs = wave_sum((int)csum);
-      if (lane == 0) code_sum[t] = cs;
-    }
-    if (lane == 0) scale[t] = s;
   };
 
   // Tokens t0 + i*nw for i < tpw, tpw being 1 or even.  With P even the next

@@ -312,9 +312,41 @@ rq_status rq_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ld
   const int mode = (asym || n_out > 0) ? 2 : 1;
   rq::GemmArgs p{nullptr, qw, T, N, (K - n_out) / 2, nullptr, sw, nullptr, asym ? w_rowsum : nullptr,
                  nullptr, (const __half *)w_out, n_out, y, ldy};
-  rq::FuseArgs f{(const __half *)x, ldx, (int)K, qd->clip_ratio, qd->outlier_idx};
+  rq::FuseArgs f{(const __half *)x, ldx, (int)K, qd->clip_ratio, qd->outlier_idx, 0, 1.0f};
   if (!rq::decode_fused_fits(p, f)) return fail(RQ_ESHAPE, "T=%lld, K=%lld do not fit the fused decode form", (long long)T, (long long)K);
   return hip_status(rq::launch_decode_fused(p, f, asym, mode, (hipStream_t)stream), "fused decode launch");
+}
+
+rq_status rq_rotate_quant_decode_linear(const void *x, int64_t T, int64_t K, int64_t ldx, const rq_rot_desc *rot,
+                                        const rq_quant_desc *qd, const uint8_t *qw, const float *sw,
+                                        const int32_t *w_rowsum, int64_t N, const void *w_out, void *y,
+                                        int64_t ldy, void *stream) {
+  if (!rot || !qd) return fail(RQ_EINVAL, "rot and qd descriptors are required");
+  if (rot->kind == RQ_ROT_NONE)
+    return rq_quant_decode_linear(x, T, K, ldx, qd, qw, sw, w_rowsum, N, w_out, y, ldy, stream);
+  if (rot->kind != RQ_ROT_HADAMARD && rot->kind != RQ_ROT_GSR)
+    return fail(rot->kind == RQ_ROT_KRON ? RQ_ESHAPE : RQ_EINVAL, "the fused decode form takes NONE, HADAMARD or GSR");
+  if (T < 0 || K <= 0 || N < 1) return fail(RQ_EINVAL, "need T >= 0, K > 0, N >= 1");
+  if (K != 4096) return fail(RQ_ESHAPE, "the rotated fused decode form takes K == 4096 (K=%lld)", (long long)K);
+  if (rot->kind == RQ_ROT_GSR && !(pow2(rot->block) && rot->block >= 8 && rot->block <= 64))
+    return fail(RQ_ESHAPE, "the rotated fused decode form takes GSR blocks of 8 to 64 (block=%d)", rot->block);
+  if (qd->asymmetric || qd->n_out || qd->row_clip || (qd->bits != 0 && qd->bits != 4))
+    return fail(RQ_ESHAPE, "the rotated fused decode form takes symmetric 4-bit codes without outliers or row clips");
+  if (!(qd->clip_ratio > 0.0f && qd->clip_ratio <= 1.0f)) return fail(RQ_EINVAL, "clip_ratio must be in (0, 1]");
+  if (T > 16) return fail(RQ_ESHAPE, "the fused decode form takes T <= 16 (T=%lld)", (long long)T);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(RQ_EALIGN, "x is required, 16-byte aligned");
+  if (ldx < K || ldx % 8) return fail(RQ_EALIGN, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!qw || !aligned(qw, 16)) return fail(RQ_EALIGN, "qw is required, 16-byte aligned");
+  if (!sw || !aligned(sw, 4)) return fail(RQ_EINVAL, "sw is required (4-byte aligned)");
+  if (!y || !aligned(y, 2)) return fail(RQ_EALIGN, "y is required, 2-byte aligned");
+  if (ldy < N) return fail(RQ_EALIGN, "leading dimension %lld must be >= N=%lld", (long long)ldy, (long long)N);
+  const int blog2 = rot->kind == RQ_ROT_GSR ? ilog2(rot->block) : 0;
+  const float norm = blog2 ? (float)(1.0 / sqrt((double)rot->block)) : 1.0f;
+  rq::GemmArgs p{nullptr, qw, T, N, K / 2, nullptr, sw, nullptr, nullptr, nullptr, nullptr, 0, y, ldy};
+  rq::FuseArgs f{(const __half *)x, ldx, (int)K, qd->clip_ratio, nullptr, blog2, norm};
+  if (!rq::decode_fused_rot_fits(p, f)) return fail(RQ_ESHAPE, "T=%lld does not fit the rotated fused decode form", (long long)T);
+  return hip_status(rq::launch_decode_fused_rot(p, f, (hipStream_t)stream), "rotated fused decode launch");
 }
 
 rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,

@@ -32,6 +32,9 @@ struct FuseArgs {
   int K;                 // columns of x (K - n_out = 2 * GemmArgs::Kb)
   float clip;            // symmetric clip ratio (1 when asymmetric)
   const int32_t *oidx;   // [n_out] outlier columns, or null when n_out == 0
+  int gsr_log2;          // rotated form (K = 4096): 0 = Walsh-Hadamard, else GSR block log2
+  float norm;            // GSR: 1 / sqrt(block); Walsh-Hadamard: unused
+  int ks;                // set by the launcher: wavefronts sharing a channel block's k-steps
 };
 
 hipError_t launch_fwht4096(const void *x, int64_t T, int64_t ldx, bool gsr, int span_log2,
@@ -58,6 +61,10 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
 // fused decode: p.qx, p.sx, p.zx and p.xo unused; the codes are made in the kernel
 bool decode_fused_fits(const GemmArgs &p, const FuseArgs &f);
 hipError_t launch_decode_fused(const GemmArgs &p, const FuseArgs &f, bool asym, int mode, hipStream_t st);
+// rotated fused decode (K = 4096, symmetric, no outliers): the 4096-point
+// Walsh-Hadamard or GSR transform + quantizer per row in the prologue
+bool decode_fused_rot_fits(const GemmArgs &p, const FuseArgs &f);
+hipError_t launch_decode_fused_rot(const GemmArgs &p, const FuseArgs &f, hipStream_t st);
 
 // kv_quant.hip: per-group Walsh-Hadamard (optional) + group-wise asymmetric INT4
 hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int group, bool rotate,

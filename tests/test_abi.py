@@ -247,3 +247,20 @@ def test_prepare_weights_noalloc_validates_first():
     qa = _qd(asym=1)
     assert L.rq_prepare_weights_noalloc(FAKE, 4, 4096, 4096, ctypes.byref(rot), ctypes.byref(qa), FAKE, FAKE,
                                         FAKE, None, None) == rq.RQ_EINVAL
+
+
+def test_rotate_quant_decode_linear_validates_first():
+    L = rq.lib()
+    qd = _qd()
+
+    def call(rot, qd, T=4, K=4096):
+        return L.rq_rotate_quant_decode_linear(FAKE, T, K, K, ctypes.byref(rot) if rot is not None else None,
+                                               ctypes.byref(qd), FAKE, FAKE, None, 64, None, FAKE, 64, None)
+    assert call(None, qd) == rq.RQ_EINVAL
+    assert call(_rot("kron", n1=64, n2=64, p1=FAKE, p2=FAKE), qd) == rq.RQ_ESHAPE
+    assert call(_rot("hadamard"), qd, K=2048) == rq.RQ_ESHAPE       # the rotated form is K = 4096 only
+    assert call(_rot("gsr", block=4), qd) == rq.RQ_ESHAPE            # GSR blocks of 8 to 64
+    assert call(_rot("hadamard"), _qd(asym=1)) == rq.RQ_ESHAPE       # symmetric codes only
+    assert call(_rot("hadamard"), qd, T=17) == rq.RQ_ESHAPE          # at most 16 rows
+    assert call(_rot("hadamard"), _qd(clip=0.0)) == rq.RQ_EINVAL
+    assert call(_rot("hadamard"), qd, T=0) == rq.RQ_OK               # empty batch: nothing launched

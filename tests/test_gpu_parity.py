@@ -176,10 +176,13 @@ def test_prepare_weights_matches_oracle(case):
 # K % 128 != 0 the LDS-tile kernel.  Ragged N leaves idle wavefronts in the
 # last decode workgroup; N > 16384 gives it more than 4 wavefronts (5 here,
 # with the stage loaded in one group of 8 chunks per thread, then in two).
+# Long rows at small N split each channel block's k-steps over 2 (K = 8192,
+# 8320: parts of 33 and 32 steps), 4 (K = 16384) and 8 (K = 32768) wavefronts.
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
                (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
                (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
-               (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144)]
+               (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144),
+               (5, 300, 16384), (2, 40, 32768)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -288,6 +291,42 @@ def _check_fused_against_oracle(x, w, idx, asym, xq, wq, y1):
         fx = check_sym_quant(host(xq["q"]), host(xq["scale"]), ref)
     extra = flip_allowance(ref["scale"], wr["scale"], fx, fw)
     check_y(host(y1), o.linear(ref, wr)["y"], extra=extra, what="fused y")
+
+
+# The rotated fused decode form (K = 4096): the 4096-point Walsh-Hadamard and
+# GSR blocks of 64 / 16, with and without a clip ratio below 1, T from 1 to the
+# 16-row maximum, N small, ragged and large (GSR's 11008: more than 4
+# wavefronts per workgroup is not reached below 16384, so 4 here).  Against
+# the oracle (rows' codes within the quantizer tolerance, y widened by their
+# flips) and against the two calls bit for bit.
+ROT_FUSED_CASES = [
+    # T, N, workload, kind, block, clip
+    (1, 4096, "llama7b", "hadamard", 0, 1.0), (8, 257, "llama7b", "hadamard", 0, 1.0),
+    (16, 130, "llama7b", "hadamard", 0, 0.95), (3, 11008, "gsr", "gsr", 64, 0.9),
+    (16, 96, "gsr", "gsr", 16, 1.0), (5, 70, "gsr", "gsr", 8, 0.9),
+]
+
+
+@pytest.mark.parametrize("T,N,wl,kind,block,clip", ROT_FUSED_CASES)
+def test_rotate_quant_decode_linear_matches_oracle(T, N, wl, kind, block, clip):
+    note(f"[rotated fused decode] T={T} N={N} {kind} block={block} clip={clip}")
+    inp = workloads.make_inputs(wl, T=T, K=4096, N=N)
+    x, w = inp["x"], inp["w"]
+    rot = rq.Rotation(kind, block=block)
+    xd, wd = dev(x), dev(w)
+    wq = rq.rq_prepare_weights(wd, rot)
+    y1 = rq.rq_rotate_quant_decode_linear(xd, rot, wq["q"], wq["scale"], clip=clip)
+    xq = rq.rq_rotate_quant(xd, rot, clip=clip)
+    y2 = rq.rq_w4a4_linear(xq["q"], xq["scale"], wq["q"], wq["scale"])
+    torch.cuda.synchronize()
+    kw = {"block": block} if kind == "gsr" else {}
+    ref = o.rotate_quant(x, kind, clip=clip, **kw)
+    wr = o.prepare_weights(w, kind, **kw)
+    fx = check_sym_quant(host(xq["q"]), host(xq["scale"]), ref)
+    fw = check_sym_quant(host(wq["q"]), host(wq["scale"]), wr, what="w")
+    check_y(host(y1), o.linear(ref, wr)["y"], extra=flip_allowance(ref["scale"], wr["scale"], fx, fw, qmax_x=7),
+            what="fused y")
+    assert torch.equal(y1, y2)
 
 
 def test_quant_decode_linear_exact_ties():
