@@ -219,9 +219,10 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   // with MFMA group 0's fragments already in registers, B(kb+1) in load slot
   // (kb+1) % kRaD.  Each of the four MFMA groups reads the next group's
   // fragments first.  B(kb+1) is stored into buffer (kb+1) % kRaNB during
-  // groups 0 and 1, the barrier sits before group 2, and group 3 reads step
-  // kb+1's first fragments.  With three buffers, buffer (kb+1) % 3 was last
-  // read in step kb-2, before every wave passed step kb-1's barrier.
+  // groups 0 and 1 (8-bit: group 0), the barrier follows, before step kb+1's
+  // first fragments are read in the last group.  With three buffers, buffer
+  // (kb+1) % 3 was last read in step kb-2, before every wave passed step
+  // kb-1's barrier.
   auto steps = [&](int kb0, auto tail) {
 #pragma unroll
     for (int v = 0; v < kRaU; ++v) {
@@ -264,16 +265,20 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       awiden(u, 1, aw);
       if (live) mfma8(aw, 1);
       bstore(nb, us, 1);
-      __syncthreads();
       // group 2
       bread(1, ub, 3);
       __builtin_amdgcn_sched_barrier(0);
       awiden(u, 2, aw);
       if (live) mfma8(aw, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // group 3: A(kb) is fully widened after this, so its slot is refilled
+      // group 3: A(kb) is fully widened after this, so its slot is refilled.
+      // The barrier sits here, a whole MFMA group after the last LDS stores
+      // of B(kb+1): placed before group 2 it waited for those stores to
+      // land with the matrix pipe idle (measured 1-2 us more at T = 2048,
+      // K = N = 4096).
       awiden(u, 3, aw);
       __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
       gload(u, min(kb + kRaD, last));
       bread(0, nb, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -402,6 +407,47 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     }
   }
   __half *out = reinterpret_cast<__half *>(p.out);
+  if ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ldo & 7) == 0) {
+    // Rows of 16-byte aligned outputs leave through LDS: each wavefront
+    // stages 32 rows x 128 columns of fp16 (row pitch 272 bytes) in its slice
+    // of the idle B buffers, then stores 16 bytes per lane, 4 rows x 256
+    // contiguous bytes per instruction (against two 64-byte pieces per 2-byte
+    // store instruction written straight from the accumulator layout:
+    // measured 1-3 us less at T = 2048, K = N = 4096).
+    constexpr int kP = 272;
+    __syncthreads();  // every wavefront is done with the B buffers
+    uint8_t *W = Bs + wave * (32 * kP);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + 4 * g + (r & 3);
+          *reinterpret_cast<__half *>(W + rr * kP + 2 * (32 * j + l32)) = __float2half_rn(f[i][j][r]);
+        }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rr = 4 * it + (lane >> 4), cc = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4 *>(W + rr * kP + 16 * cc);
+        const int64_t gm = row0 + 32 * i + rr, gn = col0 + 8 * cc;
+        if (gm < p.T) {
+          if (gn + 8 <= p.N) {
+            *reinterpret_cast<uint4 *>(out + gm * p.ldo + gn) = v;
+          } else {  // the last, partial chunk of a row
+            const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                                   (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gn + e < p.N) reinterpret_cast<uint16_t *>(out)[gm * p.ldo + gn + e] = h[e];
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll

@@ -209,6 +209,32 @@ def test_linear_epilogue_on_oracle_codes(T, N, K):
     check_y(host(y), o.dequant_sym(o.int_gemm(qx, qw), sx, sw))
 
 
+@pytest.mark.parametrize("N,pad,off", [(4096, 0, 0), (260, 0, 0), (4096, 3, 0), (4100, 4, 8), (300, 8, 1)])
+def test_large_gemm_output_layouts(N, pad, off):
+    """The 256-row GEMM's output paths: 16-byte row stores through LDS when
+    y rows are 16-byte aligned (N a multiple of 8, or a partial last chunk),
+    element stores otherwise (a row pitch or a start not a multiple of 8
+    elements); every layout holds the same values as a dense y."""
+    T, K = 300, 1024
+    note(f"[w4a4_linear layouts] T={T} N={N} K={K} row pad={pad} start offset={off}")
+    rng = np.random.default_rng(N + pad + off)
+    qx = rng.integers(-7, 8, (T, K)); qw = rng.integers(-7, 8, (N, K))
+    sx = rng.uniform(0.01, 0.1, T).astype(np.float32); sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    args = (dev(o.pack_int4(qx)), dev(sx), dev(o.pack_int4(qw)), dev(sw))
+    y = rq.rq_w4a4_linear(*args)
+    big = torch.full((T * (N + pad) + off + 64,), float("nan"), dtype=torch.float16, device="cuda")
+    view = big[off:off + T * (N + pad)].view(T, N + pad)[:, :N]
+    rq.rq_w4a4_linear(*args, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(y, view)
+    check_y(host(y), o.dequant_sym(o.int_gemm(qx, qw), sx, sw))
+    rest = big.clone()
+    rest[off:off + T * (N + pad)].view(T, N + pad)[:, :N] = 0
+    assert torch.isnan(rest[:off]).all() and torch.isnan(rest[off + T * (N + pad):]).all()
+    if pad:
+        assert torch.isnan(big[off:off + T * (N + pad)].view(T, N + pad)[:, N:]).all()
+
+
 @pytest.mark.parametrize("T,N,n_out,asym", [(37, 130, 256, True), (129, 64, 0, True), (20, 70, 32, False),
                                             (300, 150, 256, True), (260, 70, 32, False),
                                             (8, 300, 256, True), (32, 64, 96, True), (1, 40, 32, False),
