@@ -14,8 +14,10 @@
 // A = P1^{-T}, B = P2^{-T}, division by s, on the weight side:
 //   Z   = M . B          16 blocks of 16x16, k = 64 in 16 steps of 4
 //   Y^T = Z^T . A        the A operand is Z's own accumulator registers
-// Z is produced one row block (16 rows) at a time and folded into all of
-// Y^T at once, so only four Z blocks are live next to Y^T's sixteen.
+// Z is produced one row block (16 rows) at a time and folded into Y^T at
+// once; Y^T's column blocks go in two passes of two (a pass needs only the
+// matching column blocks of Z), so two Z blocks are live next to eight of
+// Y^T, within 256 registers: two wavefronts per SIMD.
 // v_mfma_f64_16x16x4_f64 operands: lane l supplies A[l%16][k_(l/16)] and
 // B[k_(l/16)][l%16]; accumulator register r of lane l holds row 4r + l/16,
 // column l%16 (measured on gfx950).
@@ -41,7 +43,7 @@ constexpr int kImg = 64 * 64;  // entries per image: 64 registers x 64 lanes
 }  // namespace
 
 template <bool DIVIDE>
-__global__ __launch_bounds__(256) void kron64_mfma(const __half *__restrict__ x, int64_t T, int64_t ldx,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kron64_mfma(const __half *__restrict__ x, int64_t T, int64_t ldx,
                                                    const float *__restrict__ fa,
                                                    const float *__restrict__ fb,
                                                    const float *__restrict__ chan_scale, float clip,
@@ -82,92 +84,118 @@ __global__ __launch_bounds__(256) void kron64_mfma(const __half *__restrict__ x,
 
   for (int64_t t0 = (int64_t)blockIdx.x * 4 + wave; t0 < T; t0 += (int64_t)gridDim.x * 4) {
     const __half *row = x + t0 * ldx;
-    // lane (l16, kg): M[16bi + l16][16kg .. 16kg + 15] for bi = 0..3
-    // lane (l16, kg) needs M[16bk + l16][16kg .. 16kg + 15]: two 16-byte loads per row block
+    // lane (l16, kg) takes M[16bk + l16][16kg .. 16kg + 15]: two 16-byte loads
+    // per row block, the next block's in flight while one is worked (the
+    // second pass reads the token again, from L2)
     auto xload = [&](int bk, uint4 *xr) {
       const __half *src = row + 64 * (16 * bk + l16) + 16 * kg;
       xr[0] = *reinterpret_cast<const uint4 *>(src);
       xr[1] = *reinterpret_cast<const uint4 *>(src + 8);
     };
-    uint4 xc[2], xn[2];
-    xload(0, xc);
-    // Y^T block [bj][bi] accumulates over Z's row blocks bk as each is finished
-    v4d y[4][4];
+    // Two passes over Y's column blocks, bj = 2h and 2h + 1: Y^T[bj][:]
+    // needs only Z's column block bj, so a pass computes those two blocks of
+    // Z and folds them into its half of Y^T.  Half the accumulators per pass
+    // keep the kernel within 256 registers, two wavefronts per SIMD (one
+    // pass over all four held 440 and one wavefront per SIMD).
+    float yf[2][2][4][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int h = 0; h < 2; ++h) {
+      v4d y[2][4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) y[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) y[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
+      uint4 xc[2], xn[2];
+      xload(0, xc);
 #pragma unroll 1
-    for (int bk = 0; bk < 4; ++bk) {
-      xload(min(bk + 1, 3), xn);
-      // Z row block bk = M[16bk .. 16bk+15][:] . B, column blocks bj
-      v4d z[4];
+      for (int bk = 0; bk < 4; ++bk) {
+        xload(min(bk + 1, 3), xn);
+        // Z row block bk, column blocks 2h, 2h + 1 = M[16bk .. 16bk+15][:] . B,
+        // each in two partial sums (even and odd steps t): four independent
+        // accumulator chains between the dependent FP64 MFMAs, then one add
+        v4d z[2], z2[2];
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) z[bj] = v4d{0.0, 0.0, 0.0, 0.0};
+        for (int c = 0; c < 2; ++c) z[c] = z2[c] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int tc = 0; tc < 4; ++tc) {
-        const float4 sc = iS[(4 * bk + tc) * 64 + lane];
-        const float ss[4] = {sc.x, sc.y, sc.z, sc.w};
+        for (int tc = 0; tc < 4; ++tc) {
+          const float4 sc = iS[(4 * bk + tc) * 64 + lane];
+          const float ss[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 4 * tc + e;
-          const v2d b01 = iB[(2 * t) * 64 + lane], b23 = iB[(2 * t + 1) * 64 + lane];
-          const double bb[4] = {b01.x, b01.y, b23.x, b23.y};
-          const uint32_t w = (&xc[t >> 3].x)[(t & 7) >> 1];
-          const __half hv = __ushort_as_half((unsigned short)((t & 1) ? (w >> 16) : (w & 0xFFFFu)));
-          const double xv = (double)__half2float(hv);
-          const double a = DIVIDE ? xv / (double)ss[e] : xv * (double)ss[e];
-#pragma unroll
-          for (int bj = 0; bj < 4; ++bj)
-            z[bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb[bj], z[bj], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const int t = 4 * tc + e;
+            const v2d bb = iB[(2 * t + h) * 64 + lane];  // B entries of column blocks 2h, 2h + 1
+            const uint32_t w = (&xc[t >> 3].x)[(t & 7) >> 1];
+            const __half hv = __ushort_as_half((unsigned short)((t & 1) ? (w >> 16) : (w & 0xFFFFu)));
+            const double xv = (double)__half2float(hv);
+            const double av = DIVIDE ? xv / (double)ss[e] : xv * (double)ss[e];
+            if (e & 1) {
+              z2[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bb.x, z2[0], 0, 0, 0);
+              z2[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bb.y, z2[1], 0, 0, 0);
+            } else {
+              z[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bb.x, z[0], 0, 0, 0);
+              z[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bb.y, z[1], 0, 0, 0);
+            }
+          }
+          // one group of four steps at a time: hoisting the operand reads of
+          // all sixteen spilled past 256 registers
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // Y^T += Z_bk^T . A_bk
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = 16 * bk + 4 * r;
-        const v2d a01 = iA[(v >> 1) * 64 + lane], a23 = iA[((v >> 1) + 1) * 64 + lane];
-        const double aa[4] = {a01.x, a01.y, a23.x, a23.y};
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-          for (int bi = 0; bi < 4; ++bi)
-            y[bj][bi] = __builtin_amdgcn_mfma_f64_16x16x4f64(z[bj][r], aa[bi], y[bj][bi], 0, 0, 0);
-      }
-      xc[0] = xn[0];
-      xc[1] = xn[1];
-    }
-    // per-token symmetric INT4 on the fp32-rounded values
-    float yf[4][4][4];
-    float amax = 0.0f;
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+        for (int c = 0; c < 2; ++c) z[c] += z2[c];
+        // Y^T[2h + c][:] += Z_bk[:, 2h + c]^T . A_bk
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          yf[bj][bi][r] = (float)y[bj][bi][r];
-          amax = fmaxf(amax, fabsf(yf[bj][bi][r]));
+          const int v = 16 * bk + 4 * r;
+          const v2d a01 = iA[(v >> 1) * 64 + lane], a23 = iA[((v >> 1) + 1) * 64 + lane];
+          const double aa[4] = {a01.x, a01.y, a23.x, a23.y};
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi)
+              y[c][bi] = __builtin_amdgcn_mfma_f64_16x16x4f64(z[c][r], aa[bi], y[c][bi], 0, 0, 0);
         }
+        xc[0] = xn[0];
+        xc[1] = xn[1];
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yf[h][c][bi][r] = (float)y[c][bi][r];
+    }
+    // per-token symmetric INT4 on the fp32-rounded values
+    float amax = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(yf[h][c][bi][r]));
     amax = wave_max(amax);
     float s, inv;
     sym_scale(amax, clip, s, inv);
     int csum = 0;
     uint8_t *qrow = q + t0 * 2048;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        uint32_t bits = 0;
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = quant_sym(yf[bj][bi][r], inv, 7.0f);
-          csum += c;
-          bits |= (uint32_t)(c & 0xF) << (4 * r);
+        for (int bi = 0; bi < 4; ++bi) {
+          const int bj = 2 * h + c;
+          uint32_t bits = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int cd = quant_sym(yf[h][c][bi][r], inv, 7.0f);
+            csum += cd;
+            bits |= (uint32_t)(cd & 0xF) << (4 * r);
+          }
+          // Y[i][j0 .. j0+3], i = 16bi + l16, j0 = 16bj + 4kg: byte (64 i + j0) / 2
+          *reinterpret_cast<uint16_t *>(qrow + 32 * (16 * bi + l16) + 8 * bj + 2 * kg) = (uint16_t)bits;
         }
-        // Y[i][j0 .. j0+3], i = 16bi + l16, j0 = 16bj + 4kg: byte (64 i + j0) / 2
-        *reinterpret_cast<uint16_t *>(qrow + 32 * (16 * bi + l16) + 8 * bj + 2 * kg) = (uint16_t)bits;
-      }
     if (code_sum) csum = wave_sum(csum);
     if (lane == 0) {
       scale[t0] = s;
@@ -179,8 +207,9 @@ __global__ __launch_bounds__(256) void kron64_mfma(const __half *__restrict__ x,
 hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,
                          const float *chan_scale, bool divide, float clip, uint8_t *q, float *scale,
                          int32_t *code_sum, hipStream_t st) {
+  // two workgroups of 4 wavefronts per CU, one token per wavefront at a time
   const int64_t wgs = (T + 3) / 4;
-  const dim3 g((unsigned)(wgs < 256 ? wgs : 256)), b(256);
+  const dim3 g((unsigned)(wgs < 512 ? wgs : 512)), b(256);
   const __half *xh = (const __half *)x;
   if (divide)
     kron64_mfma<true><<<g, b, 0, st>>>(xh, T, ldx, fa, fb, chan_scale, clip, q, scale, code_sum);
