@@ -38,12 +38,14 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel name -> the sources it is built from (for the staleness hash)
-_DECODE = ["csrc/gemm_decode.hip", "csrc/gemm_common.h", "csrc/rq_device.h", "csrc/split_common.h"]
-_QUANT = ["csrc/rotate_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"]
+_DECODE = ["csrc/gemm_decode.hip", "csrc/gemm_common.h", "csrc/rq_device.h", "csrc/split_common.h",
+           "csrc/fwht_common.h"]
+_QUANT = ["csrc/rotate_quant.hip", "csrc/rq_device.h", "csrc/split_common.h", "csrc/fwht_common.h"]
 KERNEL_SOURCES = {
     "gemm_ra": ["csrc/gemm_ra.hip", "csrc/gemm_common.h", "csrc/rq_device.h"],
     "gemm_decode": _DECODE,
     "gemm_decode16": _DECODE,
+    "gemm_decode8": ["csrc/gemm_decode8.hip", "csrc/rq_device.h"],
     "gemm_w4a4": ["csrc/gemm_w4a4.hip", "csrc/gemm_common.h", "csrc/rq_device.h"],
     "fwht4096_mfma": _QUANT,
     "split_quant": _QUANT,
