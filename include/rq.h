@@ -273,18 +273,43 @@ rq_status rq_rotate_quant_decode_linear(const void *x, int64_t T, int64_t K, int
  *   lo, hi   = min(min v, 0), max(max v, 0)
  *   scale    = fp32((hi - lo) / 15),  zero = clamp(rne(-lo / scale), 0, 15)
  *   code     = clamp(rne(v / scale) + zero, 0, 15);  v ~ (code - zero) * scale
- * H_group is the Sylvester Hadamard matrix (natural order).  The transform
- * runs in fp32 and is rounded once per value, so with rotate != 0 a code
- * whose v / scale lies within fp32 rounding of a half-integer may differ by
- * one from an exact evaluation; with rotate == 0 the result is exact.
+ * H_group is the Sylvester Hadamard matrix (natural order).  The signed
+ * sums are exact (fp64) and each v is rounded to fp32 once, so with
+ * rotate != 0 a code whose v / scale lies within that rounding of a
+ * half-integer may differ by one from an exact evaluation; with rotate == 0
+ * the result is exact.
  *   x        fp16 [T, ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned
  *   group    64, 128 or 256; K % group == 0, K <= 2^21
- *   q        out uint8 [T, K/2] packed codes, 4-byte aligned
+ *   q        out uint8 [T, K/2] packed codes, 4-byte aligned (16-byte
+ *            aligned: the codes leave in 16-byte stores)
  *   scale    out fp32 [T, K/group];  zero out int32 [T, K/group]
  * T == 0 is a no-op. */
 rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
                              int32_t rotate, uint8_t *q, float *scale, int32_t *zero,
                              void *stream);
+
+/* One tensor of rq_kv_cache_quant: input rows, whether R3 applies, outputs
+ * (each as the same-named argument of rq_kv_rotate_quant). */
+typedef struct rq_kv_tensor {
+  const void *x;  /* fp16 [T, ldx] */
+  int64_t ldx;
+  int32_t rotate; /* != 0: the per-group Walsh-Hadamard before quantization */
+  uint8_t *q;     /* out uint8 [T, K/2] */
+  float *scale;   /* out fp32 [T, K/group] */
+  int32_t *zero;  /* out int32 [T, K/group] */
+} rq_kv_tensor;
+
+/* rq_kv_cache_quant -- the keys and the values of the same T tokens through
+ * the KV-cache quantizer in one launch (SpinQuant OpenReview, the authors'
+ * answer on the number of rotation matrices: R3 on the keys before the KV
+ * cache is quantized; FlatQuant article, section 3: keys and values
+ * group-wise asymmetric).  Each tensor's outputs are those of
+ * rq_kv_rotate_quant(t->x, T, K, t->ldx, group, t->rotate, t->q, t->scale,
+ * t->zero), bit for bit; keys and values take the same shape arguments and
+ * limits, their buffers must not overlap.  keys and values are host
+ * pointers to descriptors read during the call.  T == 0 is a no-op. */
+rq_status rq_kv_cache_quant(const rq_kv_tensor *keys, const rq_kv_tensor *values, int64_t T, int64_t K,
+                            int32_t group, void *stream);
 
 /* rq_w8a8_linear -- the 8-bit form of rq_mixed_outlier_linear (QUIK-8B's
  * down projection: QUIK blog, "QUIK量化" part 3 and the QUIK-8B experiments;

@@ -23,14 +23,14 @@ ROT_KINDS = {"none": 0, "hadamard": 1, "gsr": 2, "kron": 3}
 
 __all__ = ["RqError", "Rotation", "lib", "rq_rotate_quant", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
+           "rq_kv_cache_quant", "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
            "rq_prepare_weights_noalloc", "rq_rotate_quant_decode_linear", "rq_status_string", "rq_last_error",
            "rq_abi_version", "EXPORTS"]
 
 # Every symbol include/rq.h declares.
 EXPORTS = ("rq_rotate_quant", "rq_prepare_weights_workspace_bytes", "rq_prepare_weights",
            "rq_w4a4_linear", "rq_mixed_outlier_linear", "rq_quant_decode_linear", "rq_kv_rotate_quant",
-           "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
+           "rq_kv_cache_quant", "rq_w8a8_linear", "rq_w8a8_gemm_i32", "rq_search_weight_clip", "rq_w4a4_gemm_i32",
            "rq_prepare_weights_noalloc", "rq_rotate_quant_decode_linear", "rq_status_string", "rq_last_error",
            "rq_abi_version")
 
@@ -45,6 +45,11 @@ class _RotDesc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("block", ctypes.c_int32), ("n1", ctypes.c_int32),
                 ("n2", ctypes.c_int32), ("p1", ctypes.c_void_p), ("p2", ctypes.c_void_p),
                 ("chan_scale", ctypes.c_void_p)]
+
+
+class _KvTensor(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("rotate", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -80,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.rq_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), vp, vp,
                                              vp, i64, vp, vp, i64, vp]
         L.rq_kv_rotate_quant.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.rq_kv_cache_quant.argtypes = [ctypes.POINTER(_KvTensor), ctypes.POINTER(_KvTensor), i64, i64, i32, vp]
         L.rq_rotate_quant_decode_linear.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_RotDesc),
                                                     ctypes.POINTER(_QuantDesc), vp, vp, vp, i64, vp, vp, i64, vp]
         L.rq_w8a8_linear.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, vp, i64, vp]
@@ -87,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.rq_search_weight_clip.argtypes = [vp, i64, i64, i64, ctypes.POINTER(_QuantDesc), i32, vp, vp]
         for fn in ("rq_rotate_quant", "rq_prepare_weights", "rq_prepare_weights_noalloc", "rq_w4a4_linear",
                    "rq_mixed_outlier_linear", "rq_rotate_quant_decode_linear",
-                   "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_w8a8_linear",
+                   "rq_w4a4_gemm_i32", "rq_quant_decode_linear", "rq_kv_rotate_quant", "rq_kv_cache_quant",
+                   "rq_w8a8_linear",
                    "rq_w8a8_gemm_i32", "rq_search_weight_clip"):
             getattr(L, fn).restype = ctypes.c_int
         L.rq_status_string.argtypes = [ctypes.c_int]
@@ -383,21 +390,49 @@ def rq_kv_rotate_quant(x, group: int = 128, rotate: bool = True, out=None):
     _gpu(x, *(out or ()))
     T, K = x.shape
     _want(x, "x", torch.float16, dense=False)
+    q, sc, zp = _kv_outputs(x, group, out, "")
+    st = lib().rq_kv_rotate_quant(_ptr(x), T, K, x.stride(0), int(group), 1 if rotate else 0,
+                                  _ptr(q), _ptr(sc), _ptr(zp), _stream(x.device))
+    _check(st, "rq_kv_rotate_quant")
+    return q, sc, zp
+
+
+def _kv_outputs(x, group, out, name):
+    import torch
+    T, K = x.shape
     if out is None:
         G = K // group if group > 0 else 0
         out = (torch.empty((T, K // 2), dtype=torch.uint8, device=x.device),
                torch.empty((T, G), dtype=torch.float32, device=x.device),
                torch.empty((T, G), dtype=torch.int32, device=x.device))
     q, sc, zp = out
-    _want(q, "q", torch.uint8, (T, K // 2))
-    _want(sc, "scale", torch.float32)
-    _want(zp, "zero", torch.int32, tuple(sc.shape))
-    if K % group == 0 and tuple(sc.shape) != (T, K // group):
-        raise ValueError(f"rq: scale must have shape {(T, K // group)}")
-    st = lib().rq_kv_rotate_quant(_ptr(x), T, K, x.stride(0), int(group), 1 if rotate else 0,
-                                  _ptr(q), _ptr(sc), _ptr(zp), _stream(x.device))
-    _check(st, "rq_kv_rotate_quant")
-    return q, sc, zp
+    _want(q, name + "q", torch.uint8, (T, K // 2))
+    _want(sc, name + "scale", torch.float32)
+    _want(zp, name + "zero", torch.int32, tuple(sc.shape))
+    if group > 0 and K % group == 0 and tuple(sc.shape) != (T, K // group):
+        raise ValueError(f"rq: {name}scale must have shape {(T, K // group)}")
+    return out
+
+
+def rq_kv_cache_quant(k, v, group: int = 128, rotate_k: bool = True, rotate_v: bool = False,
+                      out_k=None, out_v=None):
+    """Keys and values of the same tokens through the KV-cache quantizer in
+    one launch: k, v fp16 [T, K] -> ((q, scale, zero) of k, (q, scale, zero)
+    of v), each as rq_kv_rotate_quant would return it."""
+    import torch
+    _gpu(k, v, *(out_k or ()), *(out_v or ()))
+    _want(k, "k", torch.float16, dense=False)
+    _want(v, "v", torch.float16, dense=False)
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"rq: keys {tuple(k.shape)} and values {tuple(v.shape)} differ in shape")
+    T, K = k.shape
+    out_k = _kv_outputs(k, group, out_k, "keys ")
+    out_v = _kv_outputs(v, group, out_v, "values ")
+    dk = _KvTensor(_ptr(k), k.stride(0), 1 if rotate_k else 0, *(_ptr(t) for t in out_k))
+    dv = _KvTensor(_ptr(v), v.stride(0), 1 if rotate_v else 0, *(_ptr(t) for t in out_v))
+    st = lib().rq_kv_cache_quant(ctypes.byref(dk), ctypes.byref(dv), T, K, int(group), _stream(k.device))
+    _check(st, "rq_kv_cache_quant")
+    return out_k, out_v
 
 
 def rq_w8a8_linear(qx, sx, zx, qw, sw, w_rowsum, x_out=None, w_out=None, out=None):

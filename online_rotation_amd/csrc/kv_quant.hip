@@ -6,8 +6,8 @@
 // channels (FlatQuant article, section 3 quantization setting: KV cache
 // group-wise asymmetric, g = 128).
 //
-// A group of g = 4V channels lives in one lane quad, V consecutive values per
-// lane.  The Walsh-Hadamard of natural order factors over the index bits:
+// A group of g = 4V channels lives in one lane quad, V values per lane.  The
+// Walsh-Hadamard of natural order factors over the index bits:
 // two of its bits select the lane in the quad (DPP quad permutations, no
 // LDS), the others are register butterflies within the lane.  The
 // transform runs unnormalized in fp64, where it is exact: every fp16 value
@@ -17,7 +17,9 @@
 // (relative) of the exact rotation; the quad's min / max then give the
 // group's asymmetric scale and zero point with the arithmetic of the
 // per-token quantizer (split_common.h), and each lane packs its V codes into
-// V/8 dwords.
+// V/8 dwords.  The keys and values of the same tokens can share one launch:
+// per set, the rotated tensor's arithmetic then overlaps the other tensor's
+// loads, and the second launch's fixed cost is saved.
 #include "rq_device.h"
 #include "rq_kernels.h"
 #include "split_common.h"
@@ -43,84 +45,67 @@ __device__ __forceinline__ double quad_perm64(double v) {
 }  // namespace
 
 // Group sets: a wavefront takes 16 consecutive groups (one per quad) at a
-// time, in a grid-stride loop that loads the next set before it works on the
-// current one.  The position (row t0, group column c0) of a set's first group
-// is carried from set to set; a quad's own group is c0 + quad, wrapped into
-// later rows by a 32-bit reciprocal division.
+// time, in a grid-stride loop.  The position (row t0, group column c0) of a
+// set's first group is carried from set to set; a quad's own group is
+// c0 + quad, wrapped into later rows by a 32-bit reciprocal division.
 struct KvArgs {
-  const __half *x;
-  int64_t ldx;
-  uint8_t *q;
-  float *scale;
-  int32_t *zero;
+  KvTensor ten[2];       // one tensor, or keys and values of the same tokens
   int64_t T, total;      // rows, groups (T * gpr)
   int64_t step;          // groups per grid step (16 per wavefront)
   int64_t step_rows;     // step = step_rows * gpr + step_cols
   int32_t step_cols;
   int32_t gpr;           // groups per row
   uint32_t gpr_magic;    // floor((2^32 - 1) / gpr) + 1: n / gpr = umulhi(n, magic) for n * gpr < 2^32
+  int32_t vec_store;     // every code buffer 16-byte aligned: codes leave as 16-byte stores
   double norm;           // fp64(1 / sqrt(group))
 };
 
-template <int V, bool ROT>
-__global__ __launch_bounds__(256) void group_quant(KvArgs a) {
-  constexpr int G = 4 * V;   // channels per group
-  constexpr int NC = V / 8;  // 16-byte chunks per lane
-  const int lane = threadIdx.x & 63, sub = lane & 3, quad = lane >> 2;
-  const uint32_t w0 = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int64_t gb = (int64_t)w0 * 16;  // first group of the current set
-  if (gb >= a.total) return;      // whole wavefront
-  int64_t t0 = (uint32_t)gb / (uint32_t)a.gpr;
-  int32_t c0 = (int32_t)(gb - t0 * a.gpr);
+namespace {
 
-  // Lane `sub` of a quad holds channels 32c + 8 sub + e (chunk c, element e)
-  // of its group: each load instruction reads 64 contiguous bytes per quad;
-  // index bits 0-2 and 5.. are in registers, bits 3-4 in the lane.
-  auto locate = [&](int64_t gset, int64_t tr, int32_t cc, int64_t &t, int32_t &gc) -> bool {
+template <int V>
+struct KvLane {
+  static constexpr int G = 4 * V;   // channels per group
+  static constexpr int NC = V / 8;  // 16-byte chunks per lane
+  int sub, quad;
+  double c1, c2, fin;
+  __device__ KvLane(const KvArgs &a) {
+    const int lane = threadIdx.x & 63;
+    sub = lane & 3;
+    quad = lane >> 2;
+    // Cross-lane butterflies store sigma * value with sigma = (-1)^popcount(sub),
+    // each one fma with the partner; fin = sigma / sqrt(group) restores the value.
+    c1 = (sub & 1) ? -1.0 : 1.0;
+    c2 = (sub & 2) ? -1.0 : 1.0;
+    fin = c1 * c2 * a.norm;
+  }
+  // Row and group column of this quad's group in the set that starts at
+  // group gset (row tr, column cc); false past the last group, where the
+  // quad rereads the last group and stores nothing.
+  __device__ bool locate(const KvArgs &a, int64_t gset, int64_t tr, int32_t cc, int64_t &t, int32_t &gc) const {
     const uint32_t n = (uint32_t)cc + quad;
     const uint32_t dq = a.gpr == 1 ? n : __umulhi(n, a.gpr_magic);
     t = tr + dq;
     gc = (int32_t)(n - dq * (uint32_t)a.gpr);
     const bool valid = gset + quad < a.total;
-    if (!valid) {  // past the last group: reread it, store nothing
+    if (!valid) {
       t = a.T - 1;
       gc = a.gpr - 1;
     }
     return valid;
-  };
-  auto load = [&](uint4 *r, int64_t t, int32_t gc) {
-    const __half *src = a.x + t * a.ldx + (int64_t)gc * G + 8 * sub;
+  }
+  // Lane `sub` of a quad holds channels 32c + 8 sub + e (chunk c, element e)
+  // of its group: each load instruction reads 64 contiguous bytes per quad;
+  // index bits 0-2 and 5.. are in registers, bits 3-4 in the lane.
+  __device__ void load(uint4 *r, const KvTensor &x, int64_t t, int32_t gc) const {
+    const __half *src = x.x + t * x.ldx + (int64_t)gc * G + 8 * sub;
 #pragma unroll
     for (int c = 0; c < NC; ++c) r[c] = load_nt(src + 32 * c);
-  };
+  }
 
-  // Cross-lane butterflies store sigma * value with sigma = (-1)^popcount(sub),
-  // each one fma with the partner; fin = sigma / sqrt(group) restores the value.
-  const double c1 = (sub & 1) ? -1.0 : 1.0, c2 = (sub & 2) ? -1.0 : 1.0;
-  const double fin = c1 * c2 * a.norm;
-
-  int64_t t;
-  int32_t gc;
-  bool valid = locate(gb, t0, c0, t, gc);
-  uint4 cur[NC];
-  load(cur, t, gc);
-  for (;;) {
-    // the next set, or (past the end) the current one again, an L2 hit:
-    // unconditional, so that waiting for the current set never waits for it
-    const int64_t gbn = gb + a.step;
-    int64_t t0n = t0 + a.step_rows;
-    int32_t c0n = c0 + a.step_cols;
-    if (c0n >= a.gpr) {
-      c0n -= a.gpr;
-      ++t0n;
-    }
-    const bool more = gbn < a.total;
-    int64_t tn;
-    int32_t gcn;
-    const bool validn = more ? locate(gbn, t0n, c0n, tn, gcn) : (tn = t, gcn = gc, false);
-    uint4 nxt[NC];
-    load(nxt, tn, gcn);
-
+  // Transform (ROT), quantize and store one set.
+  template <bool ROT>
+  __device__ void quant(const KvArgs &a, const uint4 *cur, const KvTensor &o, int64_t t, int32_t gc,
+                        bool valid) const {
     float v[V];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -176,8 +161,8 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) b[k] = __float_as_uint(__builtin_amdgcn_fmed3f(code(v[8 * c + k]), rq.lo_c, rq.hi_c));
         const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000C0Cu);
-        const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);
-        wd[c] = (o << 4) | e;
+        const uint32_t od = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);
+        wd[c] = (od << 4) | e;
       }
     };
     if (__builtin_amdgcn_ballot_w64(rq.exact || (!ROT && rq.wide)) == 0) {
@@ -209,16 +194,77 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
         return __builtin_fmaf(__builtin_fmaf(f, lo_inv, kMagic0) + __builtin_fmaf(f, hi_inv, kMagic0), 0.5f, zf);
       });
     }
-    if (valid) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(a.q + t * (a.gpr * (int64_t)(G / 2)) + (int64_t)gc * (G / 2)) + sub;
+    uint8_t *gq = o.q + t * (a.gpr * (int64_t)(G / 2)) + (int64_t)gc * (G / 2);
+    if (NC >= 4 && a.vec_store) {
+      // 4 x 4 transposes in the quad (lane s: dword s of chunks 4b..4b+3 ->
+      // the four dwords of chunk 4b + s), so each lane stores 16 contiguous
+      // bytes and a wavefront's 16 groups leave as whole lines
+      const bool o1 = sub & 1, o2 = sub & 2;
+#pragma unroll
+      for (int b = 0; b < NC / 4; ++b) {
+        uint32_t *u = wd + 4 * b;
+#pragma unroll
+        for (int c = 0; c < 4; c += 2) {
+          const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o1 ? u[c] : u[c + 1]), 0xB1, 0xF, 0xF, false);
+          if (o1) u[c] = r;
+          else u[c + 1] = r;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o2 ? u[c] : u[c + 2]), 0x4E, 0xF, 0xF, false);
+          if (o2) u[c] = r;
+          else u[c + 2] = r;
+        }
+        if (valid) store_nt(reinterpret_cast<uint4 *>(gq) + 4 * b + sub, make_uint4(u[0], u[1], u[2], u[3]));
+      }
+    } else if (valid) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(gq) + sub;
 #pragma unroll
       for (int c = 0; c < NC; ++c) store_nt(dst + 4 * c, wd[c]);
-      if (sub == 0) {
-        const int64_t gi = t * a.gpr + gc;
-        a.scale[gi] = rq.s;
-        a.zero[gi] = rq.zp;
-      }
     }
+    if (valid && sub == 0) {
+      const int64_t gi = t * a.gpr + gc;
+      o.scale[gi] = rq.s;
+      o.zero[gi] = rq.zp;
+    }
+  }
+};
+
+}  // namespace
+
+// One tensor: the next set is loaded before the current one is worked.
+template <int V, bool ROT>
+__global__ __launch_bounds__(256) void group_quant(KvArgs a) {
+  constexpr int NC = V / 8;
+  const KvLane<V> L(a);
+  const uint32_t w0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t gb = (int64_t)w0 * 16;  // first group of the current set
+  if (gb >= a.total) return;      // whole wavefront
+  int64_t t0 = (uint32_t)gb / (uint32_t)a.gpr;
+  int32_t c0 = (int32_t)(gb - t0 * a.gpr);
+
+  int64_t t;
+  int32_t gc;
+  bool valid = L.locate(a, gb, t0, c0, t, gc);
+  uint4 cur[NC];
+  L.load(cur, a.ten[0], t, gc);
+  for (;;) {
+    // the next set, or (past the end) the current one again, an L2 hit:
+    // unconditional, so that waiting for the current set never waits for it
+    const int64_t gbn = gb + a.step;
+    int64_t t0n = t0 + a.step_rows;
+    int32_t c0n = c0 + a.step_cols;
+    if (c0n >= a.gpr) {
+      c0n -= a.gpr;
+      ++t0n;
+    }
+    const bool more = gbn < a.total;
+    int64_t tn;
+    int32_t gcn;
+    const bool validn = more ? L.locate(a, gbn, t0n, c0n, tn, gcn) : (tn = t, gcn = gc, false);
+    uint4 nxt[NC];
+    L.load(nxt, a.ten[0], tn, gcn);
+    L.template quant<ROT>(a, cur, a.ten[0], t, gc, valid);
     if (!more) break;
 #pragma unroll
     for (int c = 0; c < NC; ++c) cur[c] = nxt[c];
@@ -231,30 +277,74 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
   }
 }
 
-// grid: two wavefronts per SIMD of the 256 compute units, each with one set
-// in flight ahead of the one in work
-constexpr int kKvWaves = 256 * 4 * 2;
+// Keys and values of the same tokens (same shape): per set both tensors'
+// loads are issued together and the tensor with the heavier arithmetic
+// (ten[0], the keys) is worked first while the other's data arrives.
+template <int V, bool R0, bool R1>
+__global__ __launch_bounds__(256) void group_quant_pair(KvArgs a) {
+  constexpr int NC = V / 8;
+  const KvLane<V> L(a);
+  const uint32_t w0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t gb = (int64_t)w0 * 16;
+  if (gb >= a.total) return;
+  int64_t t0 = (uint32_t)gb / (uint32_t)a.gpr;
+  int32_t c0 = (int32_t)(gb - t0 * a.gpr);
+  for (;;) {
+    int64_t t;
+    int32_t gc;
+    const bool valid = L.locate(a, gb, t0, c0, t, gc);
+    uint4 k[NC], v[NC];
+    L.load(k, a.ten[0], t, gc);
+    L.load(v, a.ten[1], t, gc);
+    L.template quant<R0>(a, k, a.ten[0], t, gc, valid);
+    L.template quant<R1>(a, v, a.ten[1], t, gc, valid);
+    gb += a.step;
+    if (gb >= a.total) break;
+    t0 += a.step_rows;
+    c0 += a.step_cols;
+    if (c0 >= a.gpr) {
+      c0 -= a.gpr;
+      ++t0;
+    }
+  }
+}
 
-hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int group, bool rotate,
-                              uint8_t *q, float *scale, int32_t *zero, hipStream_t st) {
-  KvArgs a;
-  a.x = (const __half *)x;
-  a.ldx = ldx;
-  a.q = q;
-  a.scale = scale;
-  a.zero = zero;
+namespace {
+// wavefronts per launch: four per SIMD of the 256 compute units (one set
+// each at the 2048 x 4096 shapes); larger inputs loop
+constexpr int kKvWaves = 256 * 4 * 4;
+
+KvArgs kv_args(int64_t T, int64_t K, int group, const KvTensor *ten, int nt) {
+  KvArgs a{};
+  for (int i = 0; i < nt; ++i) a.ten[i] = ten[i];
+  if (nt == 1) a.ten[1] = ten[0];
   a.T = T;
   a.gpr = (int32_t)(K / group);
   a.total = T * a.gpr;
   a.gpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)a.gpr) + 1u;
+  a.vec_store = 1;
+  for (int i = 0; i < nt; ++i)
+    if ((uintptr_t)ten[i].q % 16) a.vec_store = 0;
   a.norm = 1.0 / sqrt((double)group);
+  return a;
+}
+
+int64_t kv_grid(KvArgs &a) {
   const int64_t sets = (a.total + 15) / 16;
   const int64_t waves = std::min<int64_t>(sets, kKvWaves);
   const int64_t blocks = (waves + 3) / 4;
   a.step = blocks * 4 * 16;
   a.step_rows = a.step / a.gpr;
   a.step_cols = (int32_t)(a.step - a.step_rows * a.gpr);
-  const dim3 g((unsigned)blocks), b(256);
+  return blocks;
+}
+}  // namespace
+
+hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int group, bool rotate,
+                              uint8_t *q, float *scale, int32_t *zero, hipStream_t st) {
+  const KvTensor ten{(const __half *)x, ldx, q, scale, zero};
+  KvArgs a = kv_args(T, K, group, &ten, 1);
+  const dim3 g((unsigned)kv_grid(a)), b(256);
   switch (group * 2 + (rotate ? 1 : 0)) {
     case 64 * 2: group_quant<16, false><<<g, b, 0, st>>>(a); break;
     case 64 * 2 + 1: group_quant<16, true><<<g, b, 0, st>>>(a); break;
@@ -262,6 +352,31 @@ hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, 
     case 128 * 2 + 1: group_quant<32, true><<<g, b, 0, st>>>(a); break;
     case 256 * 2: group_quant<64, false><<<g, b, 0, st>>>(a); break;
     case 256 * 2 + 1: group_quant<64, true><<<g, b, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int V>
+static void launch_pair_v(const KvArgs &a, bool r0, bool r1, dim3 g, hipStream_t st) {
+  const dim3 b(256);
+  if (r1) group_quant_pair<V, true, true><<<g, b, 0, st>>>(a);  // r1 implies r0 (rotated tensor first)
+  else if (r0) group_quant_pair<V, true, false><<<g, b, 0, st>>>(a);
+  else group_quant_pair<V, false, false><<<g, b, 0, st>>>(a);
+}
+
+hipError_t launch_group_quant_pair(const KvTensor &k, bool rot_k, const KvTensor &v, bool rot_v, int64_t T,
+                                   int64_t K, int group, hipStream_t st) {
+  // the rotated tensor first: its arithmetic overlaps the other's loads
+  const bool swap = rot_v && !rot_k;
+  const KvTensor ten[2] = {swap ? v : k, swap ? k : v};
+  KvArgs a = kv_args(T, K, group, ten, 2);
+  const bool r0 = swap ? rot_v : rot_k, r1 = swap ? rot_k : rot_v;
+  const dim3 g((unsigned)kv_grid(a));
+  switch (group) {
+    case 64: launch_pair_v<16>(a, r0, r1, g, st); break;
+    case 128: launch_pair_v<32>(a, r0, r1, g, st); break;
+    case 256: launch_pair_v<64>(a, r0, r1, g, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -349,21 +349,55 @@ rq_status rq_rotate_quant_decode_linear(const void *x, int64_t T, int64_t K, int
   return hip_status(rq::launch_decode_fused_rot(p, f, (hipStream_t)stream), "rotated fused decode launch");
 }
 
-rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
-                             int32_t rotate, uint8_t *q, float *scale, int32_t *zero, void *stream) {
+static rq_status kv_check_shape(int64_t T, int64_t K, int32_t group) {
   if (T < 0 || K <= 0) return fail(RQ_EINVAL, "need T >= 0, K > 0");
   if (group != 64 && group != 128 && group != 256) return fail(RQ_ESHAPE, "group=%d must be 64, 128 or 256", group);
   if (K % group) return fail(RQ_ESHAPE, "K=%lld must be a multiple of group=%d", (long long)K, group);
   if (K > (int64_t(1) << 21)) return fail(RQ_ESHAPE, "K=%lld is above 2^21 channels", (long long)K);
   if (T > (int64_t(1) << 40) / (K / group)) return fail(RQ_ESHAPE, "T=%lld is too large", (long long)T);
+  return RQ_OK;
+}
+
+static rq_status kv_check_tensor(const char *what, const void *x, int64_t ldx, int64_t K, const uint8_t *q,
+                                 const float *scale, const int32_t *zero) {
+  if (!x || !aligned(x, 16)) return fail(RQ_EALIGN, "%sx is required, 16-byte aligned", what);
+  if (ldx < K || ldx % 8) return fail(RQ_EALIGN, "%sldx=%lld must be >= K and a multiple of 8", what, (long long)ldx);
+  if (!q || !aligned(q, 4)) return fail(RQ_EALIGN, "%sq is required, 4-byte aligned", what);
+  if (!scale || !aligned(scale, 4)) return fail(RQ_EALIGN, "%sscale is required, 4-byte aligned", what);
+  if (!zero || !aligned(zero, 4)) return fail(RQ_EALIGN, "%szero is required, 4-byte aligned", what);
+  return RQ_OK;
+}
+
+rq_status rq_kv_rotate_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int32_t group,
+                             int32_t rotate, uint8_t *q, float *scale, int32_t *zero, void *stream) {
+  if (rq_status st = kv_check_shape(T, K, group)) return st;
   if (T == 0) return ok();
-  if (!x || !aligned(x, 16)) return fail(RQ_EALIGN, "x is required, 16-byte aligned");
-  if (ldx < K || ldx % 8) return fail(RQ_EALIGN, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
-  if (!q || !aligned(q, 4)) return fail(RQ_EALIGN, "q is required, 4-byte aligned");
-  if (!scale || !aligned(scale, 4)) return fail(RQ_EALIGN, "scale is required, 4-byte aligned");
-  if (!zero || !aligned(zero, 4)) return fail(RQ_EALIGN, "zero is required, 4-byte aligned");
+  if (rq_status st = kv_check_tensor("", x, ldx, K, q, scale, zero)) return st;
   return hip_status(rq::launch_group_quant(x, T, K, ldx, group, rotate != 0, q, scale, zero, (hipStream_t)stream),
                     "kv quantizer launch");
+}
+
+rq_status rq_kv_cache_quant(const rq_kv_tensor *keys, const rq_kv_tensor *values, int64_t T, int64_t K,
+                            int32_t group, void *stream) {
+  if (!keys || !values) return fail(RQ_EINVAL, "keys and values descriptors are required");
+  if (rq_status st = kv_check_shape(T, K, group)) return st;
+  if (T == 0) return ok();
+  if (rq_status st = kv_check_tensor("keys: ", keys->x, keys->ldx, K, keys->q, keys->scale, keys->zero)) return st;
+  if (rq_status st = kv_check_tensor("values: ", values->x, values->ldx, K, values->q, values->scale, values->zero))
+    return st;
+  const int64_t G = T * (K / group);
+  const uintptr_t kb[3] = {(uintptr_t)keys->q, (uintptr_t)keys->scale, (uintptr_t)keys->zero};
+  const uintptr_t vb[3] = {(uintptr_t)values->q, (uintptr_t)values->scale, (uintptr_t)values->zero};
+  const uintptr_t len[3] = {(uintptr_t)(T * (K / 2)), (uintptr_t)(G * 4), (uintptr_t)(G * 4)};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (kb[i] < vb[j] + len[j] && vb[j] < kb[i] + len[i])
+        return fail(RQ_EINVAL, "keys' and values' output buffers overlap");
+  const rq::KvTensor k{(const __half *)keys->x, keys->ldx, keys->q, keys->scale, keys->zero};
+  const rq::KvTensor v{(const __half *)values->x, values->ldx, values->q, values->scale, values->zero};
+  return hip_status(rq::launch_group_quant_pair(k, keys->rotate != 0, v, values->rotate != 0, T, K, group,
+                                                (hipStream_t)stream),
+                    "kv cache quantizer launch");
 }
 
 rq_status rq_w8a8_linear(const uint8_t *qx, const float *sx, const int32_t *zx, int64_t T, int64_t K_int,

@@ -69,6 +69,17 @@ hipError_t launch_decode_fused_rot(const GemmArgs &p, const FuseArgs &f, hipStre
 // kv_quant.hip: per-group Walsh-Hadamard (optional) + group-wise asymmetric INT4
 hipError_t launch_group_quant(const void *x, int64_t T, int64_t K, int64_t ldx, int group, bool rotate,
                               uint8_t *q, float *scale, int32_t *zero, hipStream_t st);
+// one tensor of the KV quantizer: fp16 input rows and the three outputs
+struct KvTensor {
+  const __half *x;
+  int64_t ldx;
+  uint8_t *q;
+  float *scale;
+  int32_t *zero;
+};
+// keys and values of the same T tokens in one launch
+hipError_t launch_group_quant_pair(const KvTensor &k, bool rot_k, const KvTensor &v, bool rot_v, int64_t T,
+                                   int64_t K, int group, hipStream_t st);
 bool gemm_ra_fits(const GemmArgs &p);
 hipError_t launch_gemm_ra(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 // one-byte codes (Kb = K bytes per row); x_unsigned: codes in [0, 255], p.rowsum required;

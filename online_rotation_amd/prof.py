@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "kron64_mfma": ["csrc/kron.hip", "csrc/rq_device.h"],
     "kron_quant": _QUANT,
     "group_quant": ["csrc/kv_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"],
+    "group_quant_pair": ["csrc/kv_quant.hip", "csrc/rq_device.h", "csrc/split_common.h"],
     "split_quant8": ["csrc/quant8.hip", "csrc/rq_device.h"],
     "clip_search": ["csrc/clip_search.hip", "csrc/rq_device.h"],
 }

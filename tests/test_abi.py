@@ -168,6 +168,39 @@ def test_kv_rotate_quant_validation():
     assert ok(z=FAKE + 1) == rq.RQ_EALIGN
 
 
+def test_kv_cache_quant_validation():
+    L = rq.lib()
+    MB = 1 << 24
+    K_, V_ = FAKE, FAKE + 8 * MB   # keys' and values' buffers, far apart
+
+    def desc(base, x=None, ldx=4096, q=None, s=None, z=None, rot=1):
+        return rq._KvTensor(base if x is None else x, ldx, rot, base + MB if q is None else q,
+                            base + 2 * MB if s is None else s, base + 3 * MB if z is None else z)
+
+    def call(k=None, v=None, T=8, K=4096, g=128):
+        k = desc(K_) if k is None else k
+        v = desc(V_, rot=0) if v is None else v
+        return L.rq_kv_cache_quant(ctypes.byref(k), ctypes.byref(v), T, K, g, None)
+
+    assert L.rq_kv_cache_quant(None, ctypes.byref(desc(V_)), 8, 4096, 128, None) == rq.RQ_EINVAL
+    assert L.rq_kv_cache_quant(ctypes.byref(desc(K_)), None, 8, 4096, 128, None) == rq.RQ_EINVAL
+    assert call(T=-1) == rq.RQ_EINVAL
+    assert call(g=96) == rq.RQ_ESHAPE
+    assert call(K=4160) == rq.RQ_ESHAPE
+    assert call(k=desc(K_, ldx=4090)) == rq.RQ_EALIGN            # keys ldx < K
+    assert call(v=desc(V_, ldx=4100)) == rq.RQ_EALIGN            # values ldx % 8
+    assert call(k=desc(K_, x=FAKE + 2)) == rq.RQ_EALIGN
+    assert call(v=desc(V_, q=V_ + MB + 2)) == rq.RQ_EALIGN       # codes 4-byte aligned
+    assert call(v=desc(V_, s=0)) == rq.RQ_EALIGN                 # null scale
+    assert call(k=desc(K_, z=K_ + 3 * MB + 1)) == rq.RQ_EALIGN
+    # outputs shared or overlapping between keys and values
+    assert call(v=desc(V_, q=K_ + MB)) == rq.RQ_EINVAL
+    assert call(v=desc(V_, s=K_ + 3 * MB)) == rq.RQ_EINVAL          # values' scale on keys' zero points
+    assert call(v=desc(V_, q=K_ + MB + 8 * 2048 - 16)) == rq.RQ_EINVAL  # the last 16 bytes of keys' codes
+    # T == 0: nothing to check beyond the descriptors, nothing launched
+    assert call(T=0) == rq.RQ_OK
+
+
 def test_prepare_weights_validation_and_workspace():
     L = rq.lib()
     kron = _rot("kron", n1=64, n2=64, p1=FAKE, p2=FAKE)

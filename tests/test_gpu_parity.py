@@ -848,8 +848,8 @@ def _tie_inputs(g, s, rng):
 
 @pytest.mark.parametrize("g", [64, 256])
 def test_kv_rotate_quant_exact_ties(g):
-    """Every nonzero rotated value is a tie; the fp32 butterflies are exact on
-    these inputs, so the codes must round half to even exactly as the oracle."""
+    """Every nonzero rotated value is a tie; the transform is exact, so the
+    codes must round half to even exactly as the oracle."""
     note(f"[kv_rotate_quant] exact ties group={g}")
     rng = np.random.default_rng(g)
     x = _tie_inputs(g, 0.5 if g == 64 else 1.0, rng)
@@ -884,21 +884,118 @@ def test_kv_rotate_quant_full_size_sampled():
 
 
 def test_kv_rotate_quant_grid_stride():
-    """More groups than one grid step covers (2048 wavefronts x 16 groups):
+    """More groups than one grid step covers (4096 wavefronts x 16 groups):
     the grid-stride loop, rows that wrap inside a set (24 groups per row, a
-    step of 32768 groups is 1365 rows + 8 groups) and the clamped last set;
+    step of 65536 groups is 2730 rows + 16 groups) and the clamped last set;
     then 64 groups per row over 8200 rows."""
-    for T, K, g in ((1500, 3072, 128), (8200, 4096, 64)):
+    for T, K, g in ((3000, 3072, 128), (8200, 4096, 64)):
         note(f"[kv_rotate_quant] grid stride T={T} K={K} group={g}")
         x = workloads.make_inputs("kv", T=T, K=K, with_weights=False)["v"]
         q, s, z = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=False)
         torch.cuda.synchronize()
         check_kv_quant(host(q), host(s), host(z), o.kv_rotate_quant(x, group=g, rotate=False), x, g, False)
-        rows = np.r_[0:3, 1364:1368, T - 3:T]
+        rows = np.r_[0:3, 1023:1026, 2729:2733, T - 3:T]
         q, s, z = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=True)
         torch.cuda.synchronize()
         check_kv_quant(host(q)[rows], host(s)[rows], host(z)[rows], o.kv_rotate_quant(x[rows], group=g), x[rows],
                        g, True)
+
+
+def _offset_codes(T, K, off=4):
+    """A dense uint8 [T, K/2] view that starts `off` bytes into its buffer:
+    4-byte aligned, not 16-byte aligned."""
+    buf = torch.empty(T * (K // 2) + 16, dtype=torch.uint8, device="cuda")
+    return buf[off:off + T * (K // 2)].view(T, K // 2)
+
+
+def _kv_out(T, K, g, q=None):
+    return (q if q is not None else torch.empty((T, K // 2), dtype=torch.uint8, device="cuda"),
+            torch.empty((T, K // g), dtype=torch.float32, device="cuda"),
+            torch.empty((T, K // g), dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("g", [128, 256])
+def test_kv_rotate_quant_codes_at_4_byte_alignment(g):
+    """Codes buffers that are 4- but not 16-byte aligned take the dword
+    stores; the result is the same as with an aligned buffer."""
+    T, K = 45, 2048
+    note(f"[kv_rotate_quant] codes 4-byte aligned group={g}")
+    x = workloads.make_inputs("kv", T=T, K=K, with_weights=False)["x"]
+    for rot in (True, False):
+        a = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=rot)
+        b = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=rot, out=_kv_out(T, K, g, _offset_codes(T, K)))
+        torch.cuda.synchronize()
+        assert b[0].data_ptr() % 16 == 4
+        for u, w in zip(a, b):
+            assert torch.equal(u, w)
+        check_kv_quant(*(host(t) for t in b), o.kv_rotate_quant(x, group=g, rotate=rot), x, g, rot)
+
+
+KV_PAIR_CASES = [
+    # name, T, K, group, rotate keys, rotate values
+    ("g128-ragged", 301, 4096, 128, True, False),
+    ("g64-both-rotated", 37, 4096, 64, True, True),
+    ("g256", 37, 4096, 256, True, False),
+    ("g64-plain", 19, 1024, 64, False, False),
+    ("values-rotated-only", 41, 4096, 128, False, True),
+    ("one-group", 1, 128, 128, True, False),
+    ("24-groups-per-row", 77, 3072, 128, True, False),
+    ("grid-stride", 3000, 3072, 128, True, False),
+]
+
+
+@pytest.mark.parametrize("case", KV_PAIR_CASES, ids=[c[0] for c in KV_PAIR_CASES])
+def test_kv_cache_quant_pair(case):
+    """Keys and values in one launch: each tensor's outputs are those of its
+    own rq_kv_rotate_quant call, bit for bit, and match the oracle."""
+    name, T, K, g, rk, rv = case
+    note(f"[kv_cache_quant] {name} T={T} K={K} group={g} rotate_k={rk} rotate_v={rv}")
+    inp = workloads.make_inputs("kv", T=T, K=K, with_weights=False)
+    k, v = inp["x"], inp["v"]
+    ok_, ov = rq.rq_kv_cache_quant(dev(k), dev(v), group=g, rotate_k=rk, rotate_v=rv)
+    sk = rq.rq_kv_rotate_quant(dev(k), group=g, rotate=rk)
+    sv = rq.rq_kv_rotate_quant(dev(v), group=g, rotate=rv)
+    torch.cuda.synchronize()
+    for a, b in zip(ok_ + ov, sk + sv):
+        assert torch.equal(a, b)
+    rows = np.arange(T) if T <= 400 else np.r_[0:3, 1023:1026, 2729:2733, T - 3:T]
+    for x, out, rot in ((k, ok_, rk), (v, ov, rv)):
+        check_kv_quant(*(host(t)[rows] for t in out), o.kv_rotate_quant(x[rows], group=g, rotate=rot), x[rows],
+                       g, rot)
+
+
+def test_kv_cache_quant_strided_and_unaligned():
+    """Different leading dimensions for keys and values, and a values codes
+    buffer that is only 4-byte aligned (every tensor then takes the dword
+    stores)."""
+    T, K, g = 29, 1024, 128
+    note("[kv_cache_quant] strided rows, 4-byte aligned codes")
+    inp = workloads.make_inputs("kv", T=T, K=K, with_weights=False)
+    k, v = inp["x"], inp["v"]
+    kb = np.zeros((T, K + 64), np.float16)
+    kb[:, :K] = k
+    vb = np.zeros((T, K + 8), np.float16)
+    vb[:, :K] = v
+    kt, vt = dev(kb)[:, :K], dev(vb)[:, :K]
+    ok_, ov = rq.rq_kv_cache_quant(kt, vt, group=g, out_v=_kv_out(T, K, g, _offset_codes(T, K)))
+    torch.cuda.synchronize()
+    check_kv_quant(*(host(t) for t in ok_), o.kv_rotate_quant(k, group=g, rotate=True), k, g, True)
+    check_kv_quant(*(host(t) for t in ov), o.kv_rotate_quant(v, group=g, rotate=False), v, g, False)
+
+
+def test_kv_cache_quant_full_size_sampled():
+    """The kv workload at its full size (keys and values [2048, 4096], g=128)
+    in the one launch the benchmark times: sampled key rows against the
+    oracle, the values in full."""
+    inp = workloads.make_inputs("kv", with_weights=False)
+    k, v = inp["x"], inp["v"]
+    note(f"[kv_cache_quant] full size {k.shape}")
+    ok_, ov = rq.rq_kv_cache_quant(dev(k), dev(v), group=128)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, k.shape[0] - 1, np.random.default_rng(8).choice(k.shape[0], 125, replace=False)])
+    check_kv_quant(*(host(t)[rows] for t in ok_), o.kv_rotate_quant(k[rows], group=128, rotate=True), k[rows],
+                   128, True)
+    check_kv_quant(*(host(t) for t in ov), o.kv_rotate_quant(v, group=128, rotate=False), v, 128, False)
 
 
 # ----------------------------------------------------------------------------- 8-bit (QUIK-8B)
