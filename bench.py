@@ -96,7 +96,7 @@ def gemm_kernel(T, Kb, n_out=0, bits=4):
     return "gemm_w4a4"
 
 
-def quant_kernel(wl):
+def quant_kernel(wl, T):
     """The quantizer kernel the library dispatches to (run_quant's rules)."""
     if wl.bits == 8:
         return "split_quant8"
@@ -469,7 +469,8 @@ def quant_sweep(torch, rq, x0, rot, wl, idx, bits, Kqb, n_out, reps, stream):
             times.append(ev0.elapsed_time(ev1) / 1e3 / n)
         sec = float(np.median(times))
         nbytes = T * K * 2 + T * Kqb + T * 4 + (T * 4 + T * n_out * 2 if mixed else 0)
-        out.append({"T": T, "avg_launch_us": round(sec * 1e6, 2), "achieved_GBps": round(nbytes / sec / 1e9, 1),
+        out.append({"T": T, "kernel": quant_kernel(wl, T), "avg_launch_us": round(sec * 1e6, 2),
+                    "achieved_GBps": round(nbytes / sec / 1e9, 1),
                     "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "buffer_sets": S})
         del g, xs, qs
         torch.cuda.synchronize()
@@ -643,7 +644,7 @@ def main():
             step(i % sc)
         torch.cuda.synchronize()
         print(json.dumps({"counters": "done", "workload": wl.name, "calib_bytes": CALIB_BYTES,
-                          "gemm_kernel": gemm_kernel(T, Kqb, n_out, bits), "quant_kernel": quant_kernel(wl)}),
+                          "gemm_kernel": gemm_kernel(T, Kqb, n_out, bits), "quant_kernel": quant_kernel(wl, T)}),
               flush=True)
         return
 
@@ -712,7 +713,7 @@ def main():
     gemm_tops = ops / gemm_s / 1e12
     rq_gbs = rq_bytes / rot_s / 1e9
     gemm_bytes = w_bytes + T * Kqb + T * 8 + T * n_out * 2 + T * N * 2
-    gk, qk = gemm_kernel(T, Kqb, n_out, bits), quant_kernel(wl)
+    gk, qk = gemm_kernel(T, Kqb, n_out, bits), quant_kernel(wl, T)
     decode = gk.startswith("gemm_decode")
     traffic = prof.read_traffic(os.path.join(ROOT, "profiles", f"{gk}_{wl.name}_traffic.txt"), gk)
     if decode:
