@@ -5,9 +5,10 @@ marshals arguments: torch supplies device memory and the current HIP stream,
 every computation runs in the library's HIP kernels.  There is no fallback:
 if librq.so is missing or a tensor is not on the GPU, the call raises.
 
-Entry points carry the C names:
-    rq_rotate_quant, rq_prepare_weights, rq_w4a4_linear,
-    rq_mixed_outlier_linear, rq_w4a4_gemm_i32
+Entry points carry the C names of every function include/rq.h declares
+(EXPORTS below): the quantizer, weight prep and linear layers, the fused
+decode forms, the 8-bit (QUIK-8B) path, the KV-cache quantizer and the clip
+search.
 """
 from __future__ import annotations
 
