@@ -182,7 +182,7 @@ GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (1
                (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
                (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
                (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144),
-               (5, 300, 16384), (2, 40, 32768)]
+               (5, 300, 16384), (2, 40, 32768), (3, 70, 65536), (300, 130, 65536)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -901,6 +901,29 @@ def test_kv_rotate_quant_grid_stride():
                        g, True)
 
 
+@pytest.mark.parametrize("rot", [True, False])
+def test_kv_rotate_quant_widest_rows(rot):
+    """K = 2^21 channels (the largest the ABI takes), 16384 groups per row.
+    Groups are independent (an oracle pin), so the oracle runs on the rows cut
+    into one group each; the keys and values launch gets the same rows."""
+    T, K, g = 2, 1 << 21, 128
+    note(f"[kv_rotate_quant] widest rows T={T} K={K} group={g} rotate={rot}")
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((T, K)) * np.where(rng.random(K) < 0.01, 30.0, 1.0)).astype(np.float16)
+    ref = o.kv_rotate_quant(x.reshape(T * K // g, g), group=g, rotate=rot)
+    ref = {"q": ref["q"].reshape(T, K), "scale": ref["scale"].reshape(T, K // g),
+           "zero": ref["zero"].reshape(T, K // g), "pre": ref["pre"].reshape(T, K),
+           "zpre": ref["zpre"].reshape(T, K // g), "packed": ref["packed"].reshape(T, K // 2)}
+    out = rq.rq_kv_rotate_quant(dev(x), group=g, rotate=rot)
+    ok_, ov = rq.rq_kv_cache_quant(dev(x), dev(x[::-1].copy()), group=g, rotate_k=rot, rotate_v=rot)
+    torch.cuda.synchronize()
+    check_kv_quant(*(host(t) for t in out), ref, x, g, rot)
+    for a, b in zip(out, ok_):
+        assert torch.equal(a, b)
+    for a, b in zip(out, ov):   # the values were the same rows in reverse order
+        assert torch.equal(a, b.flip(0))
+
+
 def _offset_codes(T, K, off=4):
     """A dense uint8 [T, K/2] view that starts `off` bytes into its buffer:
     4-byte aligned, not 16-byte aligned."""
@@ -1051,7 +1074,8 @@ def test_prepare_weights_8bit_matches_oracle():
     assert np.array_equal(host(wq["w_out"]), ref["w_out"])
 
 
-GEMM8_SHAPES = [(300, 1024, 200), (5, 64, 33), (257, 27776, 130), (1, 128, 1), (513, 2048, 257)]
+GEMM8_SHAPES = [(300, 1024, 200), (5, 64, 33), (257, 27776, 130), (1, 128, 1), (513, 2048, 257),
+                (5, 32768, 70), (260, 32768, 129)]
 
 
 @pytest.mark.parametrize("shape", GEMM8_SHAPES, ids=[f"{t}x{k}x{n}" for t, k, n in GEMM8_SHAPES])
