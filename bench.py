@@ -35,8 +35,9 @@ that a kernel trace of the default run holds one launch shape per kernel.
 
 `--workload kv` measures the KV-cache quantizer instead: one step quantizes
 one attention layer's keys (R3, a 128-point Walsh-Hadamard per head) and
-values, group-wise asymmetric INT4 with groups of 128 channels; the line
-reports GB/s, with the keys launch as the roofline kernel.
+values, group-wise asymmetric INT4 with groups of 128 channels, in one
+rq_kv_cache_quant launch; the line reports GB/s with that launch as the
+roofline kernel, and the two single-tensor launches timed beside it.
 """
 from __future__ import annotations
 
