@@ -7,13 +7,14 @@
 // in [-127, 127]; one byte per code.
 //
 // One workgroup per row, grid-stride over rows.  At start the workgroup turns
-// the outlier list into a bit mask and, per 8-column chunk, the output offset
-// of its first kept column (a block prefix scan), both in LDS.  Per row, each
-// of the 1024 threads loads its (at most four) 8-column chunks with 16-byte
-// loads and keeps them for both passes: masked fp16 min / max (or |x| max)
-// and the block reduction, then codes written byte by byte into an LDS copy
-// of the packed row at their compacted positions, outlier values to x_out,
-// and the row stored with 16-byte writes.  Codes come from two magic-number
+// the outlier list into a bit mask, the ascending list of distinct outlier
+// columns and, per 8-column chunk, the output offset of its first kept column
+// (a block prefix scan), all in LDS.  Per row, each of the 1024 threads loads
+// its (at most four) 8-column chunks with 16-byte loads and keeps them for
+// both passes: masked fp16 min / max (or |x| max) and the block reduction,
+// then codes written byte by byte into an LDS copy of the packed row at their
+// compacted positions, and the row stored with 16-byte writes; one thread per
+// outlier column copies its value to x_out.  Codes come from two magic-number
 // products (recip_bracket below); the exact boundary test runs only where
 // they disagree.
 #include "rq_device.h"
@@ -51,6 +52,11 @@ __device__ __forceinline__ void recip_bracket(float s, float inv, float &lo, flo
   if (e < 0.0f) lo = __uint_as_float(__float_as_uint(inv) - 1u);
 }
 
+// a value every lane of the wavefront holds, into a scalar register
+__device__ __forceinline__ float q8_uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 constexpr float kQ8Magic = 12582912.0f;  // 1.5 * 2^23: fma(x, r, kQ8Magic) - kQ8Magic = rne(x * r)
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
@@ -80,12 +86,13 @@ struct Q8Args {
   __half *x_out;           // [T, n_out] or null
 };
 
-template <bool ASYM>
+template <bool ASYM, bool CSUM>
 __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8))) void split_quant8(Q8Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t *mask = reinterpret_cast<uint32_t *>(smem);           // [K / 32] outlier bits
   int32_t *cbase = reinterpret_cast<int32_t *>(smem + a.K / 8);  // [K / 8] first kept position per chunk
-  uint8_t *row = smem + ((a.K / 8 + a.K / 2 + 15) & ~15);       // [K] bytes: the packed row
+  uint8_t *row = smem + ((a.K / 8 + a.K / 2 + 15) & ~15);       // [K + 16] bytes: the packed row, a spare slot
+  uint16_t *ocol = reinterpret_cast<uint16_t *>(row + a.K + 16);  // [n_out] outlier columns, ascending
   __shared__ float red[2][kQ8Threads / 64];
   __shared__ int ired[kQ8Threads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -114,10 +121,20 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
   for (int i = 0; i < cpt; ++i) {
     const int c = tid * cpt + i;
     if (c < a.nch) {
+      const uint32_t m = cmask(c);
       cbase[c] = base;
-      base += 8 - __builtin_popcount(cmask(c));
+      // the chunk's outliers take ranks 8c - base, 8c - base + 1, ...
+      int orank = 8 * c - base;
+      for (uint32_t mm = m; mm; mm &= mm - 1u, ++orank)
+        if (orank < a.n_out) ocol[orank] = (uint16_t)(8 * c + __builtin_ctz(mm));
+      base += 8 - __builtin_popcount(m);
     }
   }
+  // distinct outlier columns (duplicates in the list count once)
+  int kept_total = 0;
+#pragma unroll
+  for (int w = 0; w < kQ8Threads / 64; ++w) kept_total += ired[w];
+  const int nset = min(a.n_out, a.K - kept_total);
   __syncthreads();
 
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -129,6 +146,10 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
 #pragma unroll
     for (int i = 0; i < kQ8MaxChunks; ++i)
       v[i] = load_nt(src + 8 * min(tid + kQ8Threads * i, a.nch - 1));
+    // the thread's first outlier column (rank tid in ascending order) is read
+    // with the row, an L2 hit once the row is in; column 0 stands in past
+    // the list
+    const uint16_t og = reinterpret_cast<const uint16_t *>(src)[tid < nset ? ocol[tid] : 0];
     // pass 1: masked min / max of the kept columns (outliers count as 0,
     // which the range [min(x, 0), max(x, 0)] already contains), or |x| max
     h2 mn2 = {0, 0}, mx2 = {0, 0};
@@ -140,8 +161,11 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = ((m >> (2 * e)) & 1u ? 0u : 0x0000FFFFu) | ((m >> (2 * e + 1)) & 1u ? 0u : 0xFFFF0000u);
-        const uint32_t d = w[e] & keep;
+        // bits 2e, 2e + 1 of m, each sign-extended to a full mask, select the
+        // halves that are zeroed
+        const uint32_t olo = (uint32_t)((int32_t)(m << (31 - 2 * e)) >> 31);
+        const uint32_t ohi = (uint32_t)((int32_t)(m << (30 - 2 * e)) >> 31);
+        const uint32_t d = w[e] & ~((olo & 0x0000FFFFu) | (ohi & 0xFFFF0000u));
         h2 h;
         __builtin_memcpy(&h, &d, 4);
         if (!ASYM) h = __builtin_elementwise_abs(h);
@@ -172,51 +196,80 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
       lo_c = -127.0f;
       hi_c = 127.0f;
     }
-    // pass 2: codes into the LDS row at their compacted positions; outlier
-    // values to x_out
+    // pass 2: codes into the LDS row at their compacted positions.  Per
+    // value: the two bracket products; where every lane of the wavefront
+    // agrees on all eight (all but about 1e-5 of values), the product is the
+    // code; else the lanes with a disagreement take the exact test.  The code
+    // plus zero point is clamped in the magic-number domain, kQ8Magic + code,
+    // whose low byte is the code byte (two's complement for negative
+    // symmetric codes), so the float bits go to the LDS row as they are.
+    // Outlier positions write their byte to a spare slot past the row
+    // instead of branching.  A zero scale needs no select: rlo = rhi = 0 and
+    // zf = 0 give code 0.
     float rlo = 0.0f, rhi = 0.0f;
     if (s > 0.0f) recip_bracket(s, inv, rlo, rhi);
-    // rne(x / s) + zero point, clamped; s == 0 (a zero range) gives 0
-    auto code_of = [&](float f) {
-      const float a = __builtin_fmaf(f, rlo, kQ8Magic), b = __builtin_fmaf(f, rhi, kQ8Magic);
-      float r = a - kQ8Magic;
-      if (a != b) r = rne_div(f, s, inv);
-      return (int)__builtin_amdgcn_fmed3f(s > 0.0f ? r + zf : 0.0f, lo_c, hi_c);
+    // the row's constants are the same in every lane: scalar registers
+    s = q8_uniform(s);
+    inv = q8_uniform(inv);
+    zf = q8_uniform(zf);
+    rlo = q8_uniform(rlo);
+    rhi = q8_uniform(rhi);
+    const float clo = kQ8Magic + lo_c, chi = kQ8Magic + hi_c;
+    auto code_bits = [&](float f) {
+      float cv = __builtin_fmaf(f, rlo, kQ8Magic);
+      if (cv != __builtin_fmaf(f, rhi, kQ8Magic)) cv = rne_div(f, s, inv) + kQ8Magic;
+      return __float_as_uint(__builtin_amdgcn_fmed3f(cv + zf, clo, chi));
     };
+    // the outliers, one thread per column in ascending order (the row is in
+    // L2 by now): fp16 bits to x_out, and their codes, which the chunks'
+    // code sums below include, for the code sum's correction
     int csum = 0;
+    for (int j = tid; j < nset; j += kQ8Threads) {
+      const uint16_t bits = j == tid ? og : reinterpret_cast<const uint16_t *>(src)[ocol[j]];
+      reinterpret_cast<uint16_t *>(a.x_out)[r * a.n_out + j] = bits;
+      if (CSUM) {
+        const uint32_t cb = code_bits(__half2float(__ushort_as_half(bits))) & 0xFFu;
+        csum -= ASYM ? (int)cb : (int)(int8_t)cb;
+      }
+    }
+    const int spare = a.K;
 #pragma unroll
     for (int i = 0; i < kQ8MaxChunks; ++i) {
       const int c = tid + kQ8Threads * i;
       if (c >= a.nch) continue;
       const uint32_t m = cmask(c);
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      int kpos = cbase[c];
-      if (m == 0u) {  // no outlier in the chunk: eight consecutive codes
+      auto val = [&](int e) {
+        const float2 f2 = __half22float2(*reinterpret_cast<const __half2 *>(&w[e >> 1]));
+        return (e & 1) ? f2.y : f2.x;
+      };
+      float cv[8];
+      bool split = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 f2 = __half22float2(*reinterpret_cast<const __half2 *>(&w[e >> 1]));
-          const int ci = code_of((e & 1) ? f2.y : f2.x);
-          csum += ci;
-          if (kpos + e < a.kint) row[kpos + e] = (uint8_t)ci;
-        }
-      } else {
-        int opos = 8 * c - kpos;
+      for (int e = 0; e < 8; ++e) {
+        cv[e] = __builtin_fmaf(val(e), rlo, kQ8Magic);
+        split |= cv[e] != __builtin_fmaf(val(e), rhi, kQ8Magic);
+      }
+      if (__builtin_amdgcn_ballot_w64(split) != 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
-          if ((m >> e) & 1u) {
-            if (opos < a.n_out) reinterpret_cast<uint16_t *>(a.x_out)[r * a.n_out + opos] = (uint16_t)bits;
-            ++opos;
-          } else {
-            const int ci = code_of(__half2float(__ushort_as_half((unsigned short)bits)));
-            csum += ci;
-            if (kpos < a.kint) row[kpos] = (uint8_t)ci;
-            ++kpos;
-          }
-        }
+        for (int e = 0; e < 8; ++e)
+          if (cv[e] != __builtin_fmaf(val(e), rhi, kQ8Magic)) cv[e] = rne_div(val(e), s, inv) + kQ8Magic;
+      }
+      // value e's byte goes to row[kpos + e - nout] (nout: outliers left of
+      // it), an outlier's to the spare slot
+      const int kpos = cbase[c];
+      int nout = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = __float_as_uint(__builtin_amdgcn_fmed3f(cv[e] + zf, clo, chi));
+        const int out = (int)((m >> e) & 1u);
+        row[out ? spare : kpos + e - nout] = (uint8_t)b;
+        nout += out;
+        // every column's code enters the sum; the outliers' leave it above
+        if (CSUM) csum += ASYM ? (int)(b & 0xFFu) : (int)(int8_t)(b & 0xFFu);
       }
     }
-    if (a.code_sum) {
+    if (CSUM) {
       const int cs = wave_sum(csum);
       if (lane == 0) ired[wave] = cs;
       __syncthreads();
@@ -241,7 +294,11 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
 
 }  // namespace
 
-size_t split8_smem_bytes(int64_t K) { return (((size_t)(K / 8) + (size_t)(K / 2) + 15) & ~(size_t)15) + (size_t)K; }
+// mask, chunk offsets, the packed row with 16 spare bytes (the slot that
+// outlier positions write to), then the outlier columns in ascending order
+size_t split8_smem_bytes(int64_t K, int n_out) {
+  return (((size_t)(K / 8) + (size_t)(K / 2) + 15) & ~(size_t)15) + (size_t)K + 16 + 2 * (size_t)n_out;
+}
 
 hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
                          const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
@@ -262,16 +319,16 @@ hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool 
   a.zero = zero;
   a.code_sum = code_sum;
   a.x_out = (__half *)x_out;
-  const size_t lds = split8_smem_bytes(K);
+  const size_t lds = split8_smem_bytes(K, n_out);
   const dim3 g((unsigned)(T < 1024 ? T : 1024)), b(kQ8Threads);
-  const void *k = asym ? reinterpret_cast<const void *>(split_quant8<true>)
-                       : reinterpret_cast<const void *>(split_quant8<false>);
+  void (*k)(Q8Args) = asym ? (code_sum ? split_quant8<true, true> : split_quant8<true, false>)
+                            : (code_sum ? split_quant8<false, true> : split_quant8<false, false>);
   if (lds > 48 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (asym) split_quant8<true><<<g, b, lds, st>>>(a);
-  else split_quant8<false><<<g, b, lds, st>>>(a);
+  k<<<g, b, lds, st>>>(a);
   return hipGetLastError();
 }
 

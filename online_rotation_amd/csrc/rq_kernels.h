@@ -88,7 +88,7 @@ hipError_t launch_gemm_ra8(const GemmArgs &p, bool x_unsigned, int mode, hipStre
 bool gemm_decode8_fits(const GemmArgs &p, int mode);
 hipError_t launch_gemm_decode8(const GemmArgs &p, bool x_unsigned, int mode, hipStream_t st);
 // quant8.hip: unrotated per-row INT8 with the outlier split
-size_t split8_smem_bytes(int64_t K);
+size_t split8_smem_bytes(int64_t K, int n_out);
 hipError_t launch_split8(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,
                          const float *row_clip, const int32_t *outlier_idx, int n_out, uint8_t *q,
                          float *scale, int32_t *zero, int32_t *code_sum, void *x_out, hipStream_t st);
