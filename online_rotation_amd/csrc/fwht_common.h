@@ -176,6 +176,28 @@ __device__ __forceinline__ void fwht_load_tables(uint4 (*ltab)[64], int blog2, i
   }
 }
 
+// The same tables in two halves for a 256-thread workgroup: the global
+// loads into registers (fwht_fetch_tables), then the LDS stores
+// (fwht_store_tables), so that a caller can issue other loads in between.
+template <bool GSR>
+__device__ __forceinline__ void fwht_fetch_tables(uint4 (&tv)[GSR ? 2 : 4], int blog2, int tid) {
+  const OpTab &t1 = GSR ? (blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8) : kHad1;
+#pragma unroll
+  for (int i = 0; i < (GSR ? 2 : 4); ++i) {
+    const int e = tid + 256 * i, op = e >> 6, l = e & 63;
+    tv[i] = op < 8 ? tab_load(t1, op, l) : tab_load(kHad2, op - 8, l);
+  }
+}
+
+template <bool GSR>
+__device__ __forceinline__ void fwht_store_tables(uint4 (*ltab)[64], const uint4 (&tv)[GSR ? 2 : 4], int tid) {
+#pragma unroll
+  for (int i = 0; i < (GSR ? 2 : 4); ++i) {
+    const int e = tid + 256 * i;
+    ltab[e >> 6][e & 63] = tv[i];
+  }
+}
+
 struct FwhtOut {
   v4w code[2];
   float s;
@@ -190,9 +212,9 @@ struct FwhtOut {
 template <bool GSR, bool CSUM, bool CLAMP>
 __device__ __forceinline__ FwhtOut fwht_token(const v4w (&raw)[8], v4w *st, const uint4 (*ltab)[64], float norm,
                                             float clip) {
-const int lane = threadIdx.x & 63, r32 = lane & 31, g = lane >> 5;
-FwhtOut out;
-out.csum = 0;
+  const int lane = threadIdx.x & 63, r32 = lane & 31, g = lane >> 5;
+  FwhtOut out;
+  out.csum = 0;
   uint4 mop[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void fwht4096_quant(const __half *__restrict__
 // (1 + 2^-22) and the rounded code never leaves [-7, 7], so the clamp is
 // dropped; non-finite inputs then leave byte-clean NaN patterns (nibble 0).
 template <bool GSR, bool CSUM, bool CLAMP>
-__global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ x, int64_t T,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwht4096_mfma(const __half *__restrict__ x, int64_t T,
                                                      int64_t ldx, uint8_t *__restrict__ q,
                                                      float *__restrict__ scale,
                                                      int32_t *__restrict__ code_sum, float clip,
@@ -184,9 +184,6 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
   // Constant operands, staged in LDS once per workgroup: read through
   // lgkmcnt, waiting for them never waits for a token prefetch in flight.
   __shared__ uint4 ltab[GSR ? 8 : 16][64];
-  fwht_load_tables<GSR>(ltab, blog2, threadIdx.x, 256);
-  __syncthreads();
-  if (t0 >= T) return;
 
   // Each token is read once and its codes written once: both go through
   // nontemporal accesses (measured 13% faster than cached ones on a plain
@@ -206,9 +203,12 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
     for (int c = 0; c < 8; ++c) raw[c] = __builtin_nontemporal_load(&row[64 * c + lane]);
   };
 
-  // transform, scale, quantize and store token t
+  // transform, scale, quantize and (for a wavefront inside the grid's
+  // tokens) store token t
+  const bool live = t0 < T;
   auto body = [&](const v4w (&raw)[8], int64_t t) {
     const FwhtOut o = fwht_token<GSR, CSUM, CLAMP>(raw, stage[wave], ltab, norm, clip);
+    if (!live) return;
     uint8_t *qrow = q + t * 2048;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -223,10 +223,21 @@ __global__ __launch_bounds__(256) void fwht4096_mfma(const __half *__restrict__ 
   // token's loads are in flight while the current one is computed; indices
   // past the end are clamped onto the last row (same inputs, same outputs),
   // so the loop holds no branch.
+  // The tables' global loads go out first, then the wavefront's first
+  // token, and only then are the tables stored to LDS and the workgroup
+  // meets: the token's memory latency runs under the table set-up.  A
+  // wavefront past the last token works on that token (a clamped index) and
+  // stores nothing; with no early exit here the compiler keeps the token's
+  // loads ahead of the barrier.
+  uint4 tv[GSR ? 2 : 4];
+  fwht_fetch_tables<GSR>(tv, blog2, threadIdx.x);
   v4w b0[8], b1[8];
-  load(b0, t0);
+  load(b0, min(t0, T - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  fwht_store_tables<GSR>(ltab, tv, threadIdx.x);
+  __syncthreads();
   if (tpw == 1) {
-    body(b0, t0);
+    body(b0, min(t0, T - 1));
     return;
   }
   for (int i = 0; i < tpw; i += 2) {
