@@ -56,33 +56,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(16) float imgS[kImg];   // v = 16bk + t:        s[64(16bk + i) + 16kg + t]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, l16 = lane & 15;
-  // all 48 loads of a thread first, then the LDS writes, so the loads are in
-  // flight together
+  // All 48 loads of a thread first, then the LDS writes, so the loads are in
+  // flight together.  Each image is a permutation of its source (4096
+  // entries each), so thread t reads source entries e = 256 it + t
+  // (coalesced: a wavefront's load covers 256 contiguous bytes) and writes
+  // each to its image slot (register v, lane l) from the inverse maps:
+  //   B[R][C]:  v = 4 (R % 16) + C / 16,           l = 16 (R / 16) + pi(C % 16)
+  //   A[R][C]:  v = 16 (R / 16) + 4 (R / 4 % 4) + C / 16,  l = 16 (R % 4) + C % 16
+  //   s[X]:     v = 16 (X / 1024) + X % 16,        l = 16 (X / 16 % 4) + X / 64 % 16
+  // (pi is its own inverse).  Gathered in image order instead, the channel
+  // scales alone touched 64 cache lines per load instruction, and every
+  // workgroup waited several microseconds on the tables.
   constexpr int kIt = kImg / 256;
   float vb[kIt], va[kIt], vs[kIt];
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int e = it * 256 + tid;
-    const int v = e >> 6, l = e & 63;  // register v of lane l
-    const int lk = l >> 4, li = l & 15;
-    vb[it] = fb[(16 * lk + (v >> 2)) * 64 + 16 * (v & 3) + 4 * (li & 3) + (li >> 2)];
-    va[it] = fa[(16 * (v >> 4) + 4 * ((v >> 2) & 3) + lk) * 64 + 16 * (v & 3) + li];
-    vs[it] = chan_scale ? chan_scale[64 * (16 * (v >> 4) + li) + 16 * lk + (v & 15)] : 1.0f;
+    vb[it] = fb[e];
+    va[it] = fa[e];
+    vs[it] = chan_scale ? chan_scale[e] : 1.0f;
   }
+  // The first row block of the wavefront's first token is requested right
+  // after the tables (loads complete in order, so the image writes below
+  // wait for the tables only), and its memory latency runs under the image
+  // set-up.  The index is clamped; a wavefront with no token never uses it.
+  const int64_t tfirst = (int64_t)blockIdx.x * 4 + wave;
+  uint4 xpre[2];
+  {
+    const __half *src = x + min(tfirst, T - 1) * ldx + 64 * l16 + 16 * kg;
+    xpre[0] = *reinterpret_cast<const uint4 *>(src);
+    xpre[1] = *reinterpret_cast<const uint4 *>(src + 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int e = it * 256 + tid;
-    const int v = e >> 6, l = e & 63;
-    imgB[(v >> 1) * 128 + 2 * l + (v & 1)] = (double)vb[it];  // B[16kg + t][16bj + pi(i)], v = 4t + bj
-    imgA[(v >> 1) * 128 + 2 * l + (v & 1)] = (double)va[it];  // A[16bk + 4r + kg][16bi + i], v = 16bk + 4r + bi
-    imgS[(v >> 2) * 256 + 4 * l + (v & 3)] = vs[it];          // s[64(16bk + i) + 16kg + t], v = 16bk + t
+    const int R = e >> 6, C = e & 63, c16 = C & 15;
+    {
+      const int v = 4 * (R & 15) + (C >> 4), l = 16 * (R >> 4) + 4 * (c16 & 3) + (c16 >> 2);
+      imgB[(v >> 1) * 128 + 2 * l + (v & 1)] = (double)vb[it];
+    }
+    {
+      const int v = 16 * (R >> 4) + 4 * ((R >> 2) & 3) + (C >> 4), l = 16 * (R & 3) + c16;
+      imgA[(v >> 1) * 128 + 2 * l + (v & 1)] = (double)va[it];
+    }
+    {
+      const int v = 16 * (e >> 10) + (e & 15), l = 16 * ((e >> 4) & 3) + ((e >> 6) & 15);
+      imgS[(v >> 2) * 256 + 4 * l + (v & 3)] = vs[it];
+    }
   }
   __syncthreads();
   const v2d *iB = reinterpret_cast<const v2d *>(imgB);
   const v2d *iA = reinterpret_cast<const v2d *>(imgA);
   const float4 *iS = reinterpret_cast<const float4 *>(imgS);
 
-  for (int64_t t0 = (int64_t)blockIdx.x * 4 + wave; t0 < T; t0 += (int64_t)gridDim.x * 4) {
+  // One token: t0 (in range), its first row block already in xpre when pre
+  // is set, stores only when live.
+  auto token = [&](int64_t t0, bool pre, bool live) {
     const __half *row = x + t0 * ldx;
     // lane (l16, kg) takes M[16bk + l16][16kg .. 16kg + 15]: two 16-byte loads
     // per row block, the next block's in flight while one is worked (the
@@ -106,7 +136,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int b = 0; b < 4; ++b) y[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
       uint4 xc[2], xn[2];
-      xload(0, xc);
+      if (h == 0 && pre) {
+        xc[0] = xpre[0];
+        xc[1] = xpre[1];
+      } else {
+        xload(0, xc);
+      }
 #pragma unroll 1
       for (int bk = 0; bk < 4; ++bk) {
         xload(min(bk + 1, 3), xn);
@@ -177,6 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     amax = wave_max(amax);
     float s, inv;
     sym_scale(amax, clip, s, inv);
+    if (!live) return;
     int csum = 0;
     uint8_t *qrow = q + t0 * 2048;
 #pragma unroll
@@ -201,7 +237,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       scale[t0] = s;
       if (code_sum) code_sum[t0] = csum;
     }
-  }
+  };
+  // The first token outside the loop, so that no branch stands between the
+  // prefetch above and its use (a guarded use lets the compiler sink the
+  // prefetch past the barrier); a wavefront past the last token works on
+  // that token and stores nothing.
+  token(min(tfirst, T - 1), true, tfirst < T);
+  for (int64_t t0 = tfirst + (int64_t)gridDim.x * 4; t0 < T; t0 += (int64_t)gridDim.x * 4) token(t0, false, true);
 }
 
 hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,
