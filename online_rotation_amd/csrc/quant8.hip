@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kQ8Threads) __attribute__((amdgpu_waves_per_eu(8, 8
   __syncthreads();
 
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const int nrows = (int)((a.T - 1 - blockIdx.x) / gridDim.x) + 1;  // for progress_prio
+  int done = 0;
   for (int64_t r = blockIdx.x; r < a.T; r += gridDim.x) {
+    progress_prio(done++, nrows);
     const __half *src = a.x + r * a.ldx;
     // the thread's chunks tid + 1024 i, loaded once (past the end: a clamped
     // reload, never used)

@@ -289,10 +289,36 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
   const int nw = K / 32;
   const int Kn = K - n_out;
 
+  // A row's 16-byte chunks; inactive words reload the thread's last active
+  // word (their keep masks are zero), so the loads hold no branch.  Cached
+  // loads: the outlier gather below re-reads the row from L2 (with
+  // nontemporal loads it went to HBM and the kernel ran 30% slower).
+  auto load_row = [&](uint4 (&u)[WPT][4], int64_t t) {
+    const __half *row = x + t * ldx;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const __half *src = row + 32 * min(tid * WPT + j, nw - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[j][i] = *reinterpret_cast<const uint4 *>(src + 8 * i);
+    }
+  };
+  // The outlier list's first entries and then the workgroup's first row are
+  // requested before the set-up below, so that the row's memory latency runs
+  // under it: loads complete in order, so the set-up waits for the list
+  // without waiting for the row.  The grid has at most T workgroups, so the
+  // row exists; the row loop runs at least once, which keeps the compiler
+  // from sinking these loads past the set-up's barriers.
+  const int oid0 = tid < n_out ? outlier_idx[tid] : -1;
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 cur[WPT][4];
+  load_row(cur, blockIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- per-workgroup setup
   for (int i = tid; i < NW; i += kSplitThreads) mask[i] = 0u;
   __syncthreads();
-  for (int j = tid; j < n_out; j += kSplitThreads) {
+  if (oid0 >= 0 && oid0 < K) atomicOr(&mask[oid0 >> 5], 1u << (oid0 & 31));
+  for (int j = tid + kSplitThreads; j < n_out; j += kSplitThreads) {
     const int c = outlier_idx[j];
     if (c >= 0 && c < K) atomicOr(&mask[c >> 5], 1u << (c & 31));
   }
@@ -344,29 +370,19 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
   for (int i = tid; i < NW * 4 + 1; i += kSplitThreads) packed[i] = 0u;
   __syncthreads();
 
-  // A row's 16-byte chunks; inactive words reload the thread's last active
-  // word (their keep masks are zero), so the loads hold no branch.  Cached
-  // loads: the outlier gather below re-reads the row from L2 (with
-  // nontemporal loads it went to HBM and the kernel ran 30% slower).
-  auto load_row = [&](uint4 (&u)[WPT][4], int64_t t) {
-    const __half *row = x + t * ldx;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const __half *src = row + 32 * min(tid * WPT + j, nw - 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[j][i] = *reinterpret_cast<const uint4 *>(src + 8 * i);
-    }
-  };
   // outlier values per thread gathered ahead of the codes: columns ogc
   // (past the list, or with none: column 0, loaded but not stored)
   constexpr int kOg = 4;
   int ogc[kOg];
 #pragma unroll
   for (int k = 0; k < kOg; ++k) ogc[k] = nset > 0 ? ocol[min(tid + kSplitThreads * k, nset - 1)] : 0;
-  uint4 cur[WPT][4], nxt[WPT][4];
-  load_row(cur, blockIdx.x);
-
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  uint4 nxt[WPT][4];
+  int64_t t = blockIdx.x;
+  // rows of this workgroup, for the issue priority (progress_prio)
+  const int nrows = (int)((T - 1 - blockIdx.x) / gridDim.x) + 1;
+  int done = 0;
+  do {
+    progress_prio(done++, nrows);
     const __half *row = x + t * ldx;
     // this row's first kOg * 256 outlier values (L2-resident by now), issued
     // before the next row's loads so that waiting for them leaves those in flight
@@ -440,7 +456,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_quant(
 #pragma unroll
       for (int i = 0; i < 4; ++i) cur[j][i] = nxt[j][i];
     __syncthreads();
-  }
+    t += gridDim.x;
+  } while (t < T);
 }
 
 hipError_t launch_split(const void *x, int64_t T, int64_t K, int64_t ldx, bool asym, float clip,

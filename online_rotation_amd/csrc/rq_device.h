@@ -85,6 +85,21 @@ __device__ __forceinline__ int wave_scan_dpp(int x) {
 #undef RQ_DPP
 
 // The wave's max / min / sum, in every lane (a scalar register).
+// Issue priority for the item done (of n) of a grid-stride loop: level 3
+// for the first quarter of the wavefront's items, down to 0 for the last.
+// Among waves of equal priority a SIMD issues oldest first, so the
+// workgroups placed last on it fall behind and, at equal priority
+// throughout, finish the launch alone with their latency exposed; lowering
+// the priority of waves that are ahead lets the late ones catch up.
+__device__ __forceinline__ void progress_prio(int done, int n) {
+  switch (3 - min(3, (4 * done) / max(n, 1))) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) { return wave_max_dpp(v); }
 __device__ __forceinline__ float wave_min(float v) { return wave_min_dpp(v); }
 __device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_scan_dpp(v), 63); }
