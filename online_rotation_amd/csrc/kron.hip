@@ -242,8 +242,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // prefetch above and its use (a guarded use lets the compiler sink the
   // prefetch past the barrier); a wavefront past the last token works on
   // that token and stores nothing.
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  const int ntok = tfirst < T ? (int)((T - 1 - tfirst) / stride) + 1 : 1;  // for progress_prio
+  progress_prio(0, ntok);
   token(min(tfirst, T - 1), true, tfirst < T);
-  for (int64_t t0 = tfirst + (int64_t)gridDim.x * 4; t0 < T; t0 += (int64_t)gridDim.x * 4) token(t0, false, true);
+  int done = 1;
+  for (int64_t t0 = tfirst + stride; t0 < T; t0 += stride) {
+    progress_prio(done++, ntok);
+    token(t0, false, true);
+  }
 }
 
 hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
   for (int i = 0; i < tpw; i += 2) {
+    progress_prio(i, tpw);
     const int64_t ta = min(t0 + i * nw, T - 1), tb = min(t0 + (i + 1) * nw, T - 1),
                   tc = min(t0 + (i + 2) * nw, T - 1);
     load(b1, tb);
