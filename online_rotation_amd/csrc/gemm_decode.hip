@@ -531,7 +531,30 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
   v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   v4f fo = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i0 = 0; i0 < L; i0 += kD16) {
+  // Whole ring groups of live INT4 steps first: no masks, no outlier
+  // operands (their zero products would leave fo at +0 unchanged) and no
+  // x_out reads, so a wavefront issues about half the instructions per step
+  // and two wavefronts sharing a SIMD keep pace with the weight stream.  The
+  // rest (the group holding the INT4 / outlier boundary, the outlier steps
+  // and steps past the end) takes the general step below.
+  const int qa = min(qs, nsteps - j0);  // this part's live INT4 steps
+  int i0 = 0;
+  for (; i0 + kD16 <= qa; i0 += kD16) {
+#pragma unroll
+    for (int u = 0; u < kD16; ++u) {
+      const int i = i0 + u;
+      const uint4 wq = rb[u];
+      const uint4 wa = *reinterpret_cast<const uint4 *>(xa + 64 * (j0 + i));
+      const v4i a0 = XU ? widen_unsigned(wa.x, wa.y) : widen_signed(wa.x, wa.y);
+      const v4i a1 = XU ? widen_unsigned(wa.z, wa.w) : widen_signed(wa.z, wa.w);
+      const v4i b0 = widen_signed(wq.x, wq.y), b1 = widen_signed(wq.z, wq.w);
+      __builtin_amdgcn_sched_barrier(0);
+      rb[u] = *reinterpret_cast<const uint4 *>(src(min(i + kD16, L - 1)));
+      acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc1, 0, 0, 0);
+    }
+  }
+  for (; i0 < L; i0 += kD16) {
 #pragma unroll
     for (int u = 0; u < kD16; ++u) {
       const int i = i0 + u;
