@@ -174,6 +174,13 @@ inline int64_t d16_chunks(int64_t T, int64_t Kb, int64_t n_out) { return T * (Kb
 inline bool d16_fits(int64_t T, int64_t Kb, int64_t n_out) {
   return T <= 16 && d16_chunks(T, Kb, n_out) <= 4096;
 }
+// 17 to 32 rows: two halves of 16 rows per wavefront against one weight
+// stream, the stage up to 152 KB of LDS (one workgroup per CU) loaded in at
+// most three groups of 8 chunks per thread
+constexpr size_t kD16MaxLds2 = 152 * 1024;
+inline bool d16_fits2(int64_t T, int64_t Kb, int64_t n_out, int nthr) {
+  return T > 16 && T <= 32 && d16_lds(T, Kb, n_out) <= kD16MaxLds2 && d16_chunks(T, Kb, n_out) <= 24 * (int64_t)nthr;
+}
 // floor(c / d) = umulhi(c, m) with m = ceil(2^32 / d) = floor((2^32 - 1) / d) + 1
 // (d >= 2): exact while c * d < 2^32
 __device__ inline uint32_t d16_magic(uint32_t d) { return 0xFFFFFFFFu / d + 1; }
@@ -416,11 +423,14 @@ __device__ __forceinline__ void stage_rotated(const FuseArgs &f, uint8_t *xs, ui
   }
 }
 
-template <bool XU, int MODE, int G, int RG = 0>
+// TH = 2 (17 to 32 rows, G = 1 .. 3): each wavefront also multiplies rows
+// 16 .. 31 (register r of lane (l16, kg) then token 16 + 4kg + r of the
+// second half) against the same weight fragments.
+template <bool XU, int MODE, int G, int RG = 0, int TH = 1>
 __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   extern __shared__ __align__(16) uint8_t xs[];
-  __shared__ float sxl[16];  // the rows' scales and zero points (G = 0: made here; else staged)
-  __shared__ int zxl[16];
+  __shared__ float sxl[16 * TH];  // the rows' scales and zero points (G = 0: made here; else staged)
+  __shared__ int zxl[16 * TH];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, l16 = lane & 15;
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     const int32_t *zxp = p.zx ? p.zx : reinterpret_cast<const int32_t *>(p.sx);
     const float vsx = MODE != 0 ? p.sx[tc] : 0.0f;
     const int32_t vzx = MODE == 2 ? zxp[tc] : 0;
-    v4u s0[8], s1[8];
+    v4u s0[8], s1[8], s2[8];
     auto sload = [&](v4u (&v)[8], int h) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -485,7 +495,8 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       }
     };
     sload(s0, 0);
-    if (G == 2) sload(s1, 1);
+    if (G >= 2) sload(s1, 1);
+    if (G >= 3) sload(s2, 2);
     // the weight ring's prologue goes out behind the staging loads, so waiting
     // for the latter below leaves it in flight
     __builtin_amdgcn_sched_barrier(0);
@@ -508,7 +519,8 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
         }
       };
       sstore(s0, 0);
-      if (G == 2) sstore(s1, 1);
+      if (G >= 2) sstore(s1, 1);
+      if (G >= 3) sstore(s2, 2);
     }
     if (tid < T) {
       sxl[tid] = vsx;
@@ -523,14 +535,18 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   const uint32_t arow = min((uint32_t)l16, T - 1);
   const uint8_t *xa = xs + arow * pa + 16 * kg;
   const uint8_t *xoa = nk ? xs + xo_base + arow * po + 16 * kg : xa;  // never read unmasked when nk == 0
+  // the second half's rows (TH = 2), clamped like the first
+  const uint32_t arow2 = min((uint32_t)(16 + l16), T - 1);
+  const uint8_t *xa2 = xs + arow2 * pa + 16 * kg;
+  const uint8_t *xoa2 = nk ? xs + xo_base + arow2 * po + 16 * kg : xa2;
   // the channel's scale and code sum go out before the weight stream, so the
   // epilogue does not wait on them
   const bool has_zx = G == 0 ? XU : p.zx != nullptr;
   const int64_t gnc = min(n0 + l16, p.N - 1);
   const float swn = MODE != 0 ? p.sw[gnc] : 0.0f;
   const int32_t rsn = (MODE == 2 && has_zx) ? p.rowsum[gnc] : 0;
-  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  v4f fo = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0}, acc3 = {0, 0, 0, 0};
+  v4f fo = {0.0f, 0.0f, 0.0f, 0.0f}, fo2 = {0.0f, 0.0f, 0.0f, 0.0f};
   // Whole ring groups of live INT4 steps first: no masks, no outlier
   // operands (their zero products would leave fo at +0 unchanged) and no
   // x_out reads, so a wavefront issues about half the instructions per step
@@ -548,10 +564,20 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       const v4i a0 = XU ? widen_unsigned(wa.x, wa.y) : widen_signed(wa.x, wa.y);
       const v4i a1 = XU ? widen_unsigned(wa.z, wa.w) : widen_signed(wa.z, wa.w);
       const v4i b0 = widen_signed(wq.x, wq.y), b1 = widen_signed(wq.z, wq.w);
+      v4i a2, a3;
+      if (TH == 2) {
+        const uint4 wa2 = *reinterpret_cast<const uint4 *>(xa2 + 64 * (j0 + i));
+        a2 = XU ? widen_unsigned(wa2.x, wa2.y) : widen_signed(wa2.x, wa2.y);
+        a3 = XU ? widen_unsigned(wa2.z, wa2.w) : widen_signed(wa2.z, wa2.w);
+      }
       __builtin_amdgcn_sched_barrier(0);
       rb[u] = *reinterpret_cast<const uint4 *>(src(min(i + kD16, L - 1)));
       acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc1, 0, 0, 0);
+      if (TH == 2) {
+        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b0, acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b1, acc3, 0, 0, 0);
+      }
     }
   }
   for (; i0 < L; i0 += kD16) {
@@ -564,7 +590,13 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       const v4i a0 = XU ? widen_unsigned(wa.x & l4, wa.y & l4) : widen_signed(wa.x & l4, wa.y & l4);
       const v4i a1 = XU ? widen_unsigned(wa.z & l4, wa.w & l4) : widen_signed(wa.z & l4, wa.w & l4);
       const v4i b0 = widen_signed(wq.x, wq.y), b1 = widen_signed(wq.z, wq.w);
-      v8h ao, bo;
+      v4i a2, a3;
+      if (TH == 2) {
+        const uint4 wa2 = *reinterpret_cast<const uint4 *>(xa2 + 64 * min(j0 + i, last));
+        a2 = XU ? widen_unsigned(wa2.x & l4, wa2.y & l4) : widen_signed(wa2.x & l4, wa2.y & l4);
+        a3 = XU ? widen_unsigned(wa2.z & l4, wa2.w & l4) : widen_signed(wa2.z & l4, wa2.w & l4);
+      }
+      v8h ao, bo, ao2;
       if (MODE == 2) {
         const int jo = o0 + i - qs;
         const uint32_t lo = (i >= qs && i < L && jo < nk) ? 0xFFFFFFFFu : 0u;
@@ -573,12 +605,22 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
         const uint4 bm = {wq.x & lo, wq.y & lo, wq.z & lo, wq.w & lo};
         __builtin_memcpy(&ao, &am, 16);
         __builtin_memcpy(&bo, &bm, 16);
+        if (TH == 2) {
+          const uint4 xv2 = *reinterpret_cast<const uint4 *>(xoa2 + 64 * max(min(jo, nk - 1), 0));
+          const uint4 am2 = {xv2.x & lo, xv2.y & lo, xv2.z & lo, xv2.w & lo};
+          __builtin_memcpy(&ao2, &am2, 16);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       rb[u] = *reinterpret_cast<const uint4 *>(src(min(i + kD16, L - 1)));
       acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc1, 0, 0, 0);
       if (MODE == 2) fo = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, fo, 0, 0, 0);
+      if (TH == 2) {
+        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b0, acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b1, acc3, 0, 0, 0);
+        if (MODE == 2) fo2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao2, bo, fo2, 0, 0, 0);
+      }
     }
   }
   if (ks > 1) {
@@ -586,12 +628,18 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     // wavefront is past its loop); part 0 adds them in part order
     __syncthreads();
     uint32_t *red = reinterpret_cast<uint32_t *>(xs);
+    constexpr int RS = 12 * TH;  // reduction slots per wavefront
     if (part > 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        red[(wave * 12 + r) * 64 + lane] = (uint32_t)acc0[r];
-        red[(wave * 12 + 4 + r) * 64 + lane] = (uint32_t)acc1[r];
-        red[(wave * 12 + 8 + r) * 64 + lane] = __float_as_uint(fo[r]);
+        red[(wave * RS + r) * 64 + lane] = (uint32_t)acc0[r];
+        red[(wave * RS + 4 + r) * 64 + lane] = (uint32_t)acc1[r];
+        red[(wave * RS + 8 + r) * 64 + lane] = __float_as_uint(fo[r]);
+        if (TH == 2) {
+          red[(wave * RS + 12 + r) * 64 + lane] = (uint32_t)acc2[r];
+          red[(wave * RS + 16 + r) * 64 + lane] = (uint32_t)acc3[r];
+          red[(wave * RS + 20 + r) * 64 + lane] = __float_as_uint(fo2[r]);
+        }
       }
     }
     __syncthreads();
@@ -600,9 +648,14 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       const int w2 = q * cb + cbk;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        acc0[r] += (int)red[(w2 * 12 + r) * 64 + lane];
-        acc1[r] += (int)red[(w2 * 12 + 4 + r) * 64 + lane];
-        fo[r] += __uint_as_float(red[(w2 * 12 + 8 + r) * 64 + lane]);
+        acc0[r] += (int)red[(w2 * RS + r) * 64 + lane];
+        acc1[r] += (int)red[(w2 * RS + 4 + r) * 64 + lane];
+        fo[r] += __uint_as_float(red[(w2 * RS + 8 + r) * 64 + lane]);
+        if (TH == 2) {
+          acc2[r] += (int)red[(w2 * RS + 12 + r) * 64 + lane];
+          acc3[r] += (int)red[(w2 * RS + 16 + r) * 64 + lane];
+          fo2[r] += __uint_as_float(red[(w2 * RS + 20 + r) * 64 + lane]);
+        }
       }
     }
   }
@@ -613,22 +666,27 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
   if (MODE == 0) {
     int32_t *out = reinterpret_cast<int32_t *>(p.out);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t gm = 4 * kg + r;
-      if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = (acc0[r] + acc1[r]) >> kShift;
-    }
+    for (int h = 0; h < TH; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gm = 16 * h + 4 * kg + r;
+        const int32_t a = h ? acc2[r] + acc3[r] : acc0[r] + acc1[r];
+        if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = a >> kShift;
+      }
     return;
   }
   __half *out = reinterpret_cast<__half *>(p.out);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t gm = 4 * kg + r;
-    const int64_t gmc = min(gm, p.T - 1);
-    int32_t v = (acc0[r] + acc1[r]) >> kShift;
-    if (MODE == 2 && has_zx) v -= zxl[gmc] * rsn;
-    const float y = (float)v * sxl[gmc] * swn + fo[r];
-    if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(y);
-  }
+  for (int h = 0; h < TH; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gm = 16 * h + 4 * kg + r;
+      const int64_t gmc = min(gm, p.T - 1);
+      int32_t v = (h ? acc2[r] + acc3[r] : acc0[r] + acc1[r]) >> kShift;
+      if (MODE == 2 && has_zx) v -= zxl[gmc] * rsn;
+      const float y = (float)v * sxl[gmc] * swn + (h ? fo2[r] : fo[r]);
+      if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(y);
+    }
 }
 
 // Waves per workgroup (w) and K parts (ks) for N channels of `steps` k-steps
@@ -649,6 +707,15 @@ static void d16_grid(int64_t N, int64_t steps, int &w, int &ks) {
   w = ks > 1 ? 8 : (int)std::min<int64_t>(8, std::max<int64_t>(4, (rb + 255) / 256));
 }
 constexpr size_t kD16Reduce = 8 * 12 * 64 * 4;  // LDS for adding the parts
+constexpr size_t kD16Reduce2 = 8 * 24 * 64 * 4;  // the same with two row halves
+
+// the two-half kernel for (mode, unsigned activations, staging groups)
+template <int G>
+static void (*d16_kernel2(int mode, bool xu))(GemmArgs, FuseArgs) {
+  return mode == 0   ? (xu ? gemm_decode16<true, 0, G, 0, 2> : gemm_decode16<false, 0, G, 0, 2>)
+         : mode == 1 ? gemm_decode16<false, 1, G, 0, 2>
+                     : (xu ? gemm_decode16<true, 2, G, 0, 2> : gemm_decode16<false, 2, G, 0, 2>);
+}
 
 bool gemm_decode_fits(const GemmArgs &p) { return p.T <= 32 && p.Kb % 64 == 0 && p.Kb >= 64; }
 
@@ -684,6 +751,31 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
     f.ks = ks;
     k<<<grid, block, lds, st>>>(p, f);
     return hipGetLastError();
+  }
+  {
+    // 17 to 32 rows: the same streams, each against two halves of 16 rows
+    const int64_t rb = (p.N + 15) / 16;
+    int w, ks;
+    d16_grid(p.N, p.Kb / 64 + n_out / 32, w, ks);
+    const int nthr = 64 * w;
+    if (d16_fits2(p.T, p.Kb, n_out, nthr)) {
+      const int cb = w / ks;
+      const dim3 grid((unsigned)((rb + cb - 1) / cb)), block((unsigned)nthr);
+      const int64_t ch = d16_chunks(p.T, p.Kb, n_out);
+      void (*k)(GemmArgs, FuseArgs) = ch <= 8 * (int64_t)nthr    ? d16_kernel2<1>(mode, x_unsigned)
+                                      : ch <= 16 * (int64_t)nthr ? d16_kernel2<2>(mode, x_unsigned)
+                                                                 : d16_kernel2<3>(mode, x_unsigned);
+      const size_t lds = std::max(d16_lds(p.T, p.Kb, n_out), ks > 1 ? kD16Reduce2 : 0);
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      FuseArgs f{};
+      f.ks = ks;
+      k<<<grid, block, lds, st>>>(p, f);
+      return hipGetLastError();
+    }
   }
   const dim3 grid((unsigned)((p.N + 127) / 128)), block(256);
   if (mode == 0) {

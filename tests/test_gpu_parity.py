@@ -178,11 +178,16 @@ def test_prepare_weights_matches_oracle(case):
 # with the stage loaded in one group of 8 chunks per thread, then in two).
 # Long rows at small N split each channel block's k-steps over 2 (K = 8192,
 # 8320: parts of 33 and 32 steps), 4 (K = 16384) and 8 (K = 32768) wavefronts.
+# 17 to 32 rows take the two-half form of the 16-channel kernel: staged in
+# one, two or three groups of 8 chunks per thread, K split over two parts
+# (T = 24, K = 8192), more than 16384 channels (T = 32, N = 16500); a stage
+# above its LDS bound (T = 30, K = 16384) keeps the 32-channel kernel.
 GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (129, 130, 7936),
                (8, 300, 8192), (300, 129, 4032), (513, 200, 192), (256, 128, 64),
                (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
                (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144),
-               (5, 300, 16384), (2, 40, 32768), (3, 70, 65536), (300, 130, 65536)]
+               (5, 300, 16384), (2, 40, 32768), (3, 70, 65536), (300, 130, 65536),
+               (24, 100, 8192), (32, 16500, 1024), (30, 300, 16384), (21, 2000, 7936)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -198,7 +203,7 @@ def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
 
 
 @pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032),
-                                   (7, 190, 3968)])
+                                   (7, 190, 3968), (24, 130, 3968), (32, 300, 8192)])
 def test_linear_epilogue_on_oracle_codes(T, N, K):
     note(f"[w4a4_linear] T={T} N={N} K={K}")
     rng = np.random.default_rng(K + T)
@@ -239,7 +244,8 @@ def test_large_gemm_output_layouts(N, pad, off):
                                             (300, 150, 256, True), (260, 70, 32, False),
                                             (8, 300, 256, True), (32, 64, 96, True), (1, 40, 32, False),
                                             (15, 64, 96, True), (12, 130, 64, False), (5, 77, 0, True),
-                                            (16, 200, 256, True)])
+                                            (16, 200, 256, True), (24, 300, 256, True), (17, 4500, 64, False),
+                                            (32, 1000, 256, True)])
 def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     note(f"[mixed_linear] T={T} N={N} n_out={n_out} asym={asym}")
     K = 7936
