@@ -25,7 +25,7 @@ typedef uint32_t v4w __attribute__((ext_vector_type(4)));  // a register vector,
 //     per-row power of two chosen from the exponent of max|x| (exact), which
 //     puts the largest intermediate just below 2^15; the quantizer divides
 //     it out again (exact).
-// Constant operands come from compile-time sign tables (16 bytes per lane),
+// Constant operands are +-1 sign images (16 bytes per lane) made in the kernel,
 // staged in LDS once per workgroup.  Up to 2048 tokens, one wavefront per
 // token; beyond, each wavefront takes an even number of tokens and loads the
 // next one while it computes the current one.
@@ -34,89 +34,6 @@ typedef uint32_t v4w __attribute__((ext_vector_type(4)));  // a register vector,
 // so four consecutive elements share a lane and a lane pair (l, l+32)
 // swaps halves (v_permlane32_swap) into 16 contiguous packed bytes.
 // ---------------------------------------------------------------------------
-constexpr int cpopc(uint32_t v) {
-  int c = 0;
-  while (v) {
-    c += (int)(v & 1u);
-    v >>= 1;
-  }
-  return c;
-}
-constexpr uint32_t cbitrev(uint32_t v, int bits) {
-  uint32_t r = 0;
-  for (int i = 0; i < bits; ++i) r |= ((v >> i) & 1u) << (bits - 1 - i);
-  return r;
-}
-
-struct OpTab {
-  uint32_t w[8][64][4];  // [operand][lane][dword]: 8 fp16 values per lane
-};
-
-// Step 1 of the Hadamard product, B = H_64: operand (cb, kc) of lane
-// (r32, g) is column b' = r32 + 32*cb, slot s is row b = 16*kc + 8*g + s.
-// Only the sign bits are stored; the kernel ORs in a per-row magnitude.
-constexpr OpTab make_had1() {
-  OpTab t{};
-  for (int cb = 0; cb < 2; ++cb)
-    for (int kc = 0; kc < 4; ++kc)
-      for (int l = 0; l < 64; ++l)
-        for (int s = 0; s < 8; ++s) {
-          const uint32_t col = (l & 31) + 32 * cb, b = 16 * kc + 8 * (l >> 5) + s;
-          const uint32_t sign = (uint32_t)(cpopc(b & col) & 1);
-          t.w[cb * 4 + kc][l][s / 2] |= (sign << 15) << (16 * (s & 1));
-        }
-  return t;
-}
-// Step 2, B = H_64 (+-1): operand (nb, rb, c) of lane (r32, g) is column
-// a' = r32 + 32*nb; slot s is row a = 32*rb + 16*c + 8*(s/4) + 4*g + s%4,
-// the row the step-1 accumulator register 8*c + s of that lane holds.
-constexpr OpTab make_had2() {
-  OpTab t{};
-  for (int nb = 0; nb < 2; ++nb)
-    for (int rb = 0; rb < 2; ++rb)
-      for (int c = 0; c < 2; ++c)
-        for (int l = 0; l < 64; ++l)
-          for (int s = 0; s < 8; ++s) {
-            const uint32_t col = (l & 31) + 32 * nb;
-            const uint32_t a = 32 * rb + 16 * c + 8 * (s >> 2) + 4 * (l >> 5) + (s & 3);
-            const uint32_t v = 0x3C00u | ((uint32_t)(cpopc(a & col) & 1) << 15);
-            t.w[(nb * 2 + rb) * 2 + c][l][s / 2] |= v << (16 * (s & 1));
-          }
-  return t;
-}
-// GSR, A = G^T with G = blockdiag(Wal_B): operand (mb, kc) of lane (r32, g)
-// is output j = r32 + 32*mb, slot s is input b = 16*kc + 8*g + s;
-// G[b][j] = H_B[sigma(b%B)][j%B] inside a block (sigma = bitrev o gray:
-// row sigma(s) of H_B is the one with s sign changes), 0 across blocks.
-constexpr OpTab make_gsr(int blog2) {
-  OpTab t{};
-  const uint32_t B = 1u << blog2, bm = B - 1;
-  for (int mb = 0; mb < 2; ++mb)
-    for (int kc = 0; kc < 4; ++kc)
-      for (int l = 0; l < 64; ++l)
-        for (int s = 0; s < 8; ++s) {
-          const uint32_t j = (l & 31) + 32 * mb, b = 16 * kc + 8 * (l >> 5) + s;
-          uint32_t v = 0;
-          if ((b >> blog2) == (j >> blog2)) {
-            const uint32_t bl = b & bm, sig = cbitrev(bl ^ (bl >> 1), blog2);
-            v = 0x3C00u | ((uint32_t)(cpopc(sig & (j & bm)) & 1) << 15);
-          }
-          t.w[mb * 4 + kc][l][s / 2] |= v << (16 * (s & 1));
-        }
-  return t;
-}
-
-static __device__ const OpTab kHad1 = make_had1();
-static __device__ const OpTab kHad2 = make_had2();
-static __device__ const OpTab kGsr8 = make_gsr(3);
-static __device__ const OpTab kGsr16 = make_gsr(4);
-static __device__ const OpTab kGsr32 = make_gsr(5);
-static __device__ const OpTab kGsr64 = make_gsr(6);
-
-__device__ __forceinline__ uint4 tab_load(const OpTab &t, int op, int lane) {
-  return *reinterpret_cast<const uint4 *>(&t.w[op][lane][0]);
-}
-
 __device__ __forceinline__ v8h as_h8(uint4 u) {
   v8h h;
   __builtin_memcpy(&h, &u, 16);
@@ -164,38 +81,55 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // Stage slot of row a, 16-byte column j (see fwht_token).
 __device__ __forceinline__ int fwht_swz(int a, int j) { return a * 8 + (j ^ ((a >> 1) & 7)); }
 
-// Operand tables into LDS (8 operands for GSR, 16 for the Hadamard), by the
-// nthreads threads of the workgroup (a multiple of 64).
+// Operand images (16 bytes per lane: 8 fp16 values), made in the kernel from
+// their formulas (no memory access, so a workgroup's set-up waits on
+// nothing; loaded from global tables at kernel start they queued behind the
+// tokens' loads and took 1.5 us at the median):
+//   Hadamard step 1, B = H_64, operand op = 4 cb + kc of lane (r32, g):
+//     column b' = r32 + 32 cb, slot s is row b = 16 kc + 8 g + s; only the
+//     sign bits (the kernel ORs in a per-row magnitude);
+//   Hadamard step 2, B = H_64 (+-1), operand 8 + (2 nb + rb) 2 + c: column
+//     a' = r32 + 32 nb, slot s is row a = 32 rb + 16 c + 8 (s / 4) + 4 g +
+//     s % 4, the row the step-1 accumulator register 8 c + s of that lane
+//     holds;
+//   GSR, A = G^T with G = blockdiag(Wal_B), operand op = 4 mb + kc: output
+//     j = r32 + 32 mb, slot s is input b = 16 kc + 8 g + s; G[b][j] =
+//     H_B[sigma(b % B)][j % B] inside a block (sigma = bitrev o gray: row
+//     sigma(s) of H_B has s sign changes), 0 across blocks.
+// H_64[x][y] = (-1)^popcount(x & y).
 template <bool GSR>
-__device__ __forceinline__ void fwht_load_tables(uint4 (*ltab)[64], int blog2, int tid, int nthreads) {
-  const OpTab &t1 = GSR ? (blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8) : kHad1;
+__device__ __forceinline__ uint4 tab_entry(int op, int l, int blog2) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint32_t v;
+    if (GSR) {
+      const uint32_t bm = (1u << blog2) - 1u;
+      const uint32_t j = (uint32_t)(l & 31) + 32u * (uint32_t)(op >> 2);
+      const uint32_t b = 16u * (uint32_t)(op & 3) + 8u * (uint32_t)(l >> 5) + (uint32_t)s;
+      const uint32_t bl = b & bm, sig = __builtin_bitreverse32(bl ^ (bl >> 1)) >> (32 - blog2);
+      v = (b >> blog2) == (j >> blog2) ? 0x3C00u | ((uint32_t)(__builtin_popcount(sig & j & bm) & 1) << 15) : 0u;
+    } else if (op < 8) {
+      const uint32_t col = (uint32_t)(l & 31) + 32u * (uint32_t)(op >> 2);
+      const uint32_t b = 16u * (uint32_t)(op & 3) + 8u * (uint32_t)(l >> 5) + (uint32_t)s;
+      v = (uint32_t)(__builtin_popcount(b & col) & 1) << 15;
+    } else {
+      const int o = op - 8, nb = o >> 2, rb = (o >> 1) & 1, c = o & 1;
+      const uint32_t col = (uint32_t)(l & 31) + 32u * (uint32_t)nb;
+      const uint32_t a = 32u * rb + 16u * c + 8u * (uint32_t)(s >> 2) + 4u * (uint32_t)(l >> 5) + (uint32_t)(s & 3);
+      v = 0x3C00u | ((uint32_t)(__builtin_popcount(a & col) & 1) << 15);
+    }
+    w[s >> 1] |= v << (16 * (s & 1));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// All operand images into LDS (8 operands for GSR, 16 for the Hadamard), by
+// the nthreads threads of the workgroup.
+template <bool GSR>
+__device__ __forceinline__ void fwht_make_tables(uint4 (*ltab)[64], int blog2, int tid, int nthreads) {
   constexpr int nop = GSR ? 8 : 16;
-  for (int e = tid; e < nop * 64; e += nthreads) {
-    const int op = e >> 6, l = e & 63;
-    ltab[op][l] = op < 8 ? tab_load(t1, op, l) : tab_load(kHad2, op - 8, l);
-  }
-}
-
-// The same tables in two halves for a 256-thread workgroup: the global
-// loads into registers (fwht_fetch_tables), then the LDS stores
-// (fwht_store_tables), so that a caller can issue other loads in between.
-template <bool GSR>
-__device__ __forceinline__ void fwht_fetch_tables(uint4 (&tv)[GSR ? 2 : 4], int blog2, int tid) {
-  const OpTab &t1 = GSR ? (blog2 == 6 ? kGsr64 : blog2 == 5 ? kGsr32 : blog2 == 4 ? kGsr16 : kGsr8) : kHad1;
-#pragma unroll
-  for (int i = 0; i < (GSR ? 2 : 4); ++i) {
-    const int e = tid + 256 * i, op = e >> 6, l = e & 63;
-    tv[i] = op < 8 ? tab_load(t1, op, l) : tab_load(kHad2, op - 8, l);
-  }
-}
-
-template <bool GSR>
-__device__ __forceinline__ void fwht_store_tables(uint4 (*ltab)[64], const uint4 (&tv)[GSR ? 2 : 4], int tid) {
-#pragma unroll
-  for (int i = 0; i < (GSR ? 2 : 4); ++i) {
-    const int e = tid + 256 * i;
-    ltab[e >> 6][e & 63] = tv[i];
-  }
+  for (int e = tid; e < nop * 64; e += nthreads) ltab[e >> 6][e & 63] = tab_entry<GSR>(e >> 6, e & 63, blog2);
 }
 
 struct FwhtOut {
@@ -206,7 +140,7 @@ struct FwhtOut {
 
 // One token through the transform and the quantizer: raw holds the token's
 // 8 KB as loaded (load c, lane l: bytes 1024c + 16l), st is the wavefront's
-// 4 KB LDS stage, ltab the operand tables (fwht_load_tables).  Returns the
+// 4 KB LDS stage, ltab the operand tables (fwht_make_tables).  Returns the
 // lane's 32 bytes of packed codes (code bytes 32 (r32 + 32 nb) + 16 g, nb =
 // 0, 1), the scale and, with CSUM, the token's code sum.
 template <bool GSR, bool CSUM, bool CLAMP>

@@ -174,12 +174,12 @@ inline int64_t d16_chunks(int64_t T, int64_t Kb, int64_t n_out) { return T * (Kb
 inline bool d16_fits(int64_t T, int64_t Kb, int64_t n_out) {
   return T <= 16 && d16_chunks(T, Kb, n_out) <= 4096;
 }
-// 17 to 32 rows: two halves of 16 rows per wavefront against one weight
-// stream, the stage up to 152 KB of LDS (one workgroup per CU) loaded in at
-// most three groups of 8 chunks per thread
+// larger stages (up to 32 rows, as two halves of 16 rows per wavefront
+// against one weight stream above 16): up to 152 KB of LDS (one workgroup per
+// CU), loaded in at most three groups of 8 chunks per thread
 constexpr size_t kD16MaxLds2 = 152 * 1024;
 inline bool d16_fits2(int64_t T, int64_t Kb, int64_t n_out, int nthr) {
-  return T > 16 && T <= 32 && d16_lds(T, Kb, n_out) <= kD16MaxLds2 && d16_chunks(T, Kb, n_out) <= 24 * (int64_t)nthr;
+  return T <= 32 && d16_lds(T, Kb, n_out) <= kD16MaxLds2 && d16_chunks(T, Kb, n_out) <= 24 * (int64_t)nthr;
 }
 // floor(c / d) = umulhi(c, m) with m = ceil(2^32 / d) = floor((2^32 - 1) / d) + 1
 // (d >= 2): exact while c * d < 2^32
@@ -411,7 +411,7 @@ __device__ __forceinline__ void stage_rotated(const FuseArgs &f, uint8_t *xs, ui
   __builtin_amdgcn_sched_barrier(0);
   prologue();
   __builtin_amdgcn_sched_barrier(0);
-  fwht_load_tables<GSR>(ltab, f.gsr_log2, tid, (int)nthr);
+  fwht_make_tables<GSR>(ltab, f.gsr_log2, tid, (int)nthr);
   __syncthreads();
   for (uint32_t t = wave; t < T; t += nwaves) {
     if (t != wave) load(raw, t);
@@ -423,7 +423,7 @@ __device__ __forceinline__ void stage_rotated(const FuseArgs &f, uint8_t *xs, ui
   }
 }
 
-// TH = 2 (17 to 32 rows, G = 1 .. 3): each wavefront also multiplies rows
+// TH = 2 (17 to 32 rows): each wavefront also multiplies rows
 // 16 .. 31 (register r of lane (l16, kg) then token 16 + 4kg + r of the
 // second half) against the same weight fragments.
 template <bool XU, int MODE, int G, int RG = 0, int TH = 1>
@@ -709,12 +709,13 @@ static void d16_grid(int64_t N, int64_t steps, int &w, int &ks) {
 constexpr size_t kD16Reduce = 8 * 12 * 64 * 4;  // LDS for adding the parts
 constexpr size_t kD16Reduce2 = 8 * 24 * 64 * 4;  // the same with two row halves
 
-// the two-half kernel for (mode, unsigned activations, staging groups)
-template <int G>
-static void (*d16_kernel2(int mode, bool xu))(GemmArgs, FuseArgs) {
-  return mode == 0   ? (xu ? gemm_decode16<true, 0, G, 0, 2> : gemm_decode16<false, 0, G, 0, 2>)
-         : mode == 1 ? gemm_decode16<false, 1, G, 0, 2>
-                     : (xu ? gemm_decode16<true, 2, G, 0, 2> : gemm_decode16<false, 2, G, 0, 2>);
+// the kernel for (mode, unsigned activations) with G staging groups and TH
+// row halves
+template <int G, int TH>
+static void (*d16_kernel(int mode, bool xu))(GemmArgs, FuseArgs) {
+  return mode == 0   ? (xu ? gemm_decode16<true, 0, G, 0, TH> : gemm_decode16<false, 0, G, 0, TH>)
+         : mode == 1 ? gemm_decode16<false, 1, G, 0, TH>
+                     : (xu ? gemm_decode16<true, 2, G, 0, TH> : gemm_decode16<false, 2, G, 0, TH>);
 }
 
 bool gemm_decode_fits(const GemmArgs &p) { return p.T <= 32 && p.Kb % 64 == 0 && p.Kb >= 64; }
@@ -753,7 +754,8 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
     return hipGetLastError();
   }
   {
-    // 17 to 32 rows: the same streams, each against two halves of 16 rows
+    // stages above 64 KB, and 17 to 32 rows (the same streams, each against
+    // two halves of 16 rows)
     const int64_t rb = (p.N + 15) / 16;
     int w, ks;
     d16_grid(p.N, p.Kb / 64 + n_out / 32, w, ks);
@@ -762,10 +764,15 @@ hipError_t launch_gemm_decode(const GemmArgs &p, bool x_unsigned, int mode, hipS
       const int cb = w / ks;
       const dim3 grid((unsigned)((rb + cb - 1) / cb)), block((unsigned)nthr);
       const int64_t ch = d16_chunks(p.T, p.Kb, n_out);
-      void (*k)(GemmArgs, FuseArgs) = ch <= 8 * (int64_t)nthr    ? d16_kernel2<1>(mode, x_unsigned)
-                                      : ch <= 16 * (int64_t)nthr ? d16_kernel2<2>(mode, x_unsigned)
-                                                                 : d16_kernel2<3>(mode, x_unsigned);
-      const size_t lds = std::max(d16_lds(p.T, p.Kb, n_out), ks > 1 ? kD16Reduce2 : 0);
+      const bool two = p.T > 16;
+      void (*k)(GemmArgs, FuseArgs) =
+          two ? (ch <= 8 * (int64_t)nthr    ? d16_kernel<1, 2>(mode, x_unsigned)
+                 : ch <= 16 * (int64_t)nthr ? d16_kernel<2, 2>(mode, x_unsigned)
+                                            : d16_kernel<3, 2>(mode, x_unsigned))
+              : (ch <= 8 * (int64_t)nthr    ? d16_kernel<1, 1>(mode, x_unsigned)
+                 : ch <= 16 * (int64_t)nthr ? d16_kernel<2, 1>(mode, x_unsigned)
+                                            : d16_kernel<3, 1>(mode, x_unsigned));
+      const size_t lds = std::max(d16_lds(p.T, p.Kb, n_out), ks > 1 ? (two ? kD16Reduce2 : kD16Reduce) : 0);
       if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

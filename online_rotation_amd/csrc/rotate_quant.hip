@@ -223,18 +223,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // token's loads are in flight while the current one is computed; indices
   // past the end are clamped onto the last row (same inputs, same outputs),
   // so the loop holds no branch.
-  // The tables' global loads go out first, then the wavefront's first
-  // token, and only then are the tables stored to LDS and the workgroup
-  // meets: the token's memory latency runs under the table set-up.  A
-  // wavefront past the last token works on that token (a clamped index) and
-  // stores nothing; with no early exit here the compiler keeps the token's
-  // loads ahead of the barrier.
-  uint4 tv[GSR ? 2 : 4];
-  fwht_fetch_tables<GSR>(tv, blog2, threadIdx.x);
+  // The wavefront's first token is requested first; the operand tables are
+  // then computed into LDS (no memory access) and the workgroup meets, so
+  // the token's latency runs under the set-up.  A wavefront past the last
+  // token works on that token (a clamped index) and stores nothing; with no
+  // early exit here the compiler keeps the token's loads ahead of the
+  // barrier.
   v4w b0[8], b1[8];
   load(b0, min(t0, T - 1));
   __builtin_amdgcn_sched_barrier(0);
-  fwht_store_tables<GSR>(ltab, tv, threadIdx.x);
+  fwht_make_tables<GSR>(ltab, blog2, threadIdx.x, 256);
   __syncthreads();
   if (tpw == 1) {
     body(b0, min(t0, T - 1));
