@@ -66,17 +66,30 @@ template <int V>
 struct KvLane {
   static constexpr int G = 4 * V;   // channels per group
   static constexpr int NC = V / 8;  // 16-byte chunks per lane
+  // Rotated groups of 128 or more channels leave the transform with each
+  // lane holding V contiguous output channels (see quant); smaller ones
+  // keep the loaded layout.
+  static constexpr bool kSwapOut = NC >= 4;
   int sub, quad;
   double c1, c2, fin;
   __device__ KvLane(const KvArgs &a) {
     const int lane = threadIdx.x & 63;
     sub = lane & 3;
     quad = lane >> 2;
-    // Cross-lane butterflies store sigma * value with sigma = (-1)^popcount(sub),
-    // each one fma with the partner; fin = sigma / sqrt(group) restores the value.
     c1 = (sub & 1) ? -1.0 : 1.0;
     c2 = (sub & 2) ? -1.0 : 1.0;
-    fin = c1 * c2 * a.norm;
+    // In the loaded layout the cross-lane butterflies store sigma * value
+    // with sigma = (-1)^popcount(sub), each one fma with the partner; fin =
+    // sigma / sqrt(group) restores the value.
+    fin = kSwapOut ? a.norm : c1 * c2 * a.norm;
+  }
+  // bit-reversed chunk index (log2(NC) bits): the output position of the
+  // lane's chunk c after the exchanging transform
+  static __device__ constexpr int chunk_out(int c) {
+    int r = 0;
+    for (int b = 1, rb = NC >> 1; b < NC; b <<= 1, rb >>= 1)
+      if (c & b) r |= rb;
+    return r;
   }
   // Row and group column of this quad's group in the set that starts at
   // group gset (row tr, column cc); false past the last group, where the
@@ -106,60 +119,130 @@ struct KvLane {
   template <bool ROT>
   __device__ void quant(const KvArgs &a, const uint4 *cur, const KvTensor &o, int64_t t, int32_t gc,
                         bool valid) const {
+    // the lane's values as loaded (fp16 pairs) and, rotated, the transform's
+    // fp32 results; unrotated values are widened where they are used (the
+    // min / max run on the fp16 pairs, the codes' fma takes fp16 operands)
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 hv[V / 2];
     float v[V];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint32_t w[4] = {cur[c].x, cur[c].y, cur[c].z, cur[c].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float2 f = __half22float2(*reinterpret_cast<const __half2 *>(&w[e]));
-        v[8 * c + 2 * e] = f.x;
-        v[8 * c + 2 * e + 1] = f.y;
-      }
+      for (int e = 0; e < 4; ++e) __builtin_memcpy(&hv[4 * c + e], &w[e], 4);
     }
+    auto val = [&](int i) -> float { return ROT ? v[i] : (float)hv[i >> 1][i & 1]; };
     if (ROT) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = (float)hv[i >> 1][i & 1];
       // y_j = sum_i x_i (-1)^popcount(i & j): one butterfly stage per index
       // bit, in fp64 (exact), then one rounding to fp32
       double d[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) d[i] = (double)v[i];
+      if (kSwapOut) {
+        // In-lane stages first, the two top chunk bits last (h = V/4 with
+        // c2, h = V/2 with c1).  In a lane whose quad bit is set, those two
+        // write the difference to the lower slot, negated, and the sum to the
+        // upper one.  Each cross-lane stage then sends only the upper slots
+        // of its bit (the partner's values of the half this lane keeps) and
+        // forms both outputs of the kept half, one fma each: half the
+        // exchanges of the loaded layout.  Afterwards quad bit 0 selects the
+        // top chunk bit of the output index and slot bit V/2 its bit 3;
+        // quad bit 1 selects the next chunk bit and slot bit V/4 index bit
+        // 4.  So lane sub ends with the V channels from
+        // V (2 (sub & 1) + (sub >> 1)) on, chunk c at chunk_out(c).
 #pragma unroll
-      for (int h = 1; h < V; h <<= 1)
+        for (int h = 1; h < V / 4; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            if (!(i & h)) {
+              const double p = d[i], r = d[i + h];
+              d[i] = p + r;
+              d[i + h] = p - r;
+            }
 #pragma unroll
         for (int i = 0; i < V; ++i)
-          if (!(i & h)) {
-            const double p = d[i], r = d[i + h];
-            d[i] = p + r;
-            d[i + h] = p - r;
+          if (!(i & (V / 4))) {
+            const double p = d[i], r = d[i + V / 4];
+            d[i] = __builtin_fma(c2, p, r);
+            d[i + V / 4] = __builtin_fma(-c2, r, p);
           }
 #pragma unroll
-      for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0xB1>(d[i]), c1, d[i]);  // quad_perm [1,0,3,2]
+        for (int i = 0; i < V / 2; ++i) {
+          const double p = d[i], r = d[i + V / 2];
+          d[i] = __builtin_fma(c1, p, r);
+          d[i + V / 2] = __builtin_fma(-c1, r, p);
+        }
 #pragma unroll
-      for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0x4E>(d[i]), c2, d[i]);  // quad_perm [2,3,0,1]
+        for (int i = 0; i < V / 2; ++i) {
+          const double p = d[i], r = quad_perm64<0xB1>(d[i + V / 2]);  // quad_perm [1,0,3,2]
+          d[i] = __builtin_fma(c1, p, r);
+          d[i + V / 2] = __builtin_fma(-c1, r, p);
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (!(i & (V / 4))) {
+            const double p = d[i], r = quad_perm64<0x4E>(d[i + V / 4]);  // quad_perm [2,3,0,1]
+            d[i] = __builtin_fma(c2, p, r);
+            d[i + V / 4] = __builtin_fma(-c2, r, p);
+          }
+      } else {
+#pragma unroll
+        for (int h = 1; h < V; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            if (!(i & h)) {
+              const double p = d[i], r = d[i + h];
+              d[i] = p + r;
+              d[i + h] = p - r;
+            }
+#pragma unroll
+        for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0xB1>(d[i]), c1, d[i]);  // quad_perm [1,0,3,2]
+#pragma unroll
+        for (int i = 0; i < V; ++i) d[i] = __builtin_fma(quad_perm64<0x4E>(d[i]), c2, d[i]);  // quad_perm [2,3,0,1]
+      }
 #pragma unroll
       for (int i = 0; i < V; ++i) v[i] = (float)(d[i] * fin);
     }
     // the group's min and max over the quad (0 included, as the quantizer's range)
     float mn = 0.0f, mx = 0.0f;
+    if (ROT) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
+      for (int i = 0; i < V; ++i) {
+        mn = fminf(mn, v[i]);
+        mx = fmaxf(mx, v[i]);
+      }
+    } else {
+      // three-input packed minimum / maximum (a NaN, which the loaded data
+      // never holds, would carry through to the group's scale)
+      h2 m0 = hv[0], m1 = hv[0];
+#pragma unroll
+      for (int i = 1; i < V / 2; ++i) {
+        m0 = __builtin_elementwise_minimum(m0, hv[i]);
+        m1 = __builtin_elementwise_maximum(m1, hv[i]);
+      }
+      mn = fminf(fminf((float)m0.x, (float)m0.y), 0.0f);
+      mx = fmaxf(fmaxf((float)m1.x, (float)m1.y), 0.0f);
     }
     mn = fminf(mn, quad_xor1(mn));
     mx = fmaxf(mx, quad_xor1(mx));
     mn = fminf(mn, quad_xor2(mn));
     mx = fmaxf(mx, quad_xor2(mx));
     const RowQuant rq = row_quant(true, 1.0f, mn, mx);
-    // codes eight to a dword, nibble e = channel 32c + 8 sub + e; the byte
-    // permutes gather the low bytes (the nibbles) of the magic-biased floats
+    // codes eight to a dword, nibble e = channel 32c + 8 sub + e (loaded
+    // layout) or V (2 (sub & 1) + (sub >> 1)) + 8c + e (exchanged layout,
+    // from the lane's chunk chunk_out(c)); the byte permutes gather the low
+    // bytes (the nibbles) of the magic-biased floats
+    constexpr bool SW = ROT && kSwapOut;
     uint32_t wd[NC];
     auto pack = [&](auto code) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        const int cs = SW ? chunk_out(c) : c;
         uint32_t b[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) b[k] = __float_as_uint(__builtin_amdgcn_fmed3f(code(v[8 * c + k]), rq.lo_c, rq.hi_c));
+        for (int k = 0; k < 8; ++k) b[k] = __float_as_uint(__builtin_amdgcn_fmed3f(code(val(8 * cs + k)), rq.lo_c, rq.hi_c));
         const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000C0Cu);
         const uint32_t od = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);
         wd[c] = (od << 4) | e;
@@ -195,7 +278,18 @@ struct KvLane {
       });
     }
     uint8_t *gq = o.q + t * (a.gpr * (int64_t)(G / 2)) + (int64_t)gc * (G / 2);
-    if (NC >= 4 && a.vec_store) {
+    if (SW) {
+      // the lane's V codes are contiguous: V/2 bytes from its position
+      uint8_t *lq = gq + (V / 2) * (2 * (sub & 1) + (sub >> 1));
+      if (a.vec_store) {
+#pragma unroll
+        for (int b = 0; b < NC / 4; ++b)
+          if (valid) store_nt(reinterpret_cast<uint4 *>(lq) + b, make_uint4(wd[4 * b], wd[4 * b + 1], wd[4 * b + 2], wd[4 * b + 3]));
+      } else if (valid) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) store_nt(reinterpret_cast<uint32_t *>(lq) + c, wd[c]);
+      }
+    } else if (NC >= 4 && a.vec_store) {
       // 4 x 4 transposes in the quad (lane s: dword s of chunks 4b..4b+3 ->
       // the four dwords of chunk 4b + s), so each lane stores 16 contiguous
       // bytes and a wavefront's 16 groups leave as whole lines
@@ -277,9 +371,11 @@ __global__ __launch_bounds__(256) void group_quant(KvArgs a) {
   }
 }
 
-// Keys and values of the same tokens (same shape): per set both tensors'
-// loads are issued together and the tensor with the heavier arithmetic
-// (ten[0], the keys) is worked first while the other's data arrives.
+// Keys and values of the same tokens (same shape): per set the tensor with
+// the heavier arithmetic (ten[0], the keys) is worked first while the
+// other's data arrives.  The compiler issues the second tensor's loads
+// partway through the first one's transform; pinned ahead of the transform
+// (a scheduling barrier after each load group) the launch was 6% slower.
 template <int V, bool R0, bool R1>
 __global__ __launch_bounds__(256) void group_quant_pair(KvArgs a) {
   constexpr int NC = V / 8;
