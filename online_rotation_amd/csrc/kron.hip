@@ -40,10 +40,13 @@ namespace {
 typedef double v4d __attribute__((ext_vector_type(4)));
 typedef double v2d __attribute__((ext_vector_type(2)));
 constexpr int kImg = 64 * 64;  // entries per image: 64 registers x 64 lanes
+// One workgroup of eight wavefronts per CU (two per SIMD): the images are
+// built once per CU, not once per four wavefronts.
+constexpr int kKronWaves = 8, kKronThreads = 64 * kKronWaves;
 }  // namespace
 
 template <bool DIVIDE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kron64_mfma(const __half *__restrict__ x, int64_t T, int64_t ldx,
+__global__ __launch_bounds__(kKronThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void kron64_mfma(const __half *__restrict__ x, int64_t T, int64_t ldx,
                                                    const float *__restrict__ fa,
                                                    const float *__restrict__ fb,
                                                    const float *__restrict__ chan_scale, float clip,
@@ -54,11 +57,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(16) double imgB[kImg];  // v = 4t + bj:         B[16kg + t][16bj + pi(i)]
   __shared__ __align__(16) double imgA[kImg];  // v = 16bk + 4r + bi:  A[16bk + 4r + kg][16bi + i]
   __shared__ __align__(16) float imgS[kImg];   // v = 16bk + t:        s[64(16bk + i) + 16kg + t]
+  __shared__ __align__(16) uint8_t qst[kKronWaves][2048];  // a token's packed codes, per wavefront
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, l16 = lane & 15;
   // All 48 loads of a thread first, then the LDS writes, so the loads are in
   // flight together.  Each image is a permutation of its source (4096
-  // entries each), so thread t reads source entries e = 256 it + t
+  // entries each), so thread t reads source entries e = 512 it + t
   // (coalesced: a wavefront's load covers 256 contiguous bytes) and writes
   // each to its image slot (register v, lane l) from the inverse maps:
   //   B[R][C]:  v = 4 (R % 16) + C / 16,           l = 16 (R / 16) + pi(C % 16)
@@ -67,11 +71,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (pi is its own inverse).  Gathered in image order instead, the channel
   // scales alone touched 64 cache lines per load instruction, and every
   // workgroup waited several microseconds on the tables.
-  constexpr int kIt = kImg / 256;
+  constexpr int kIt = kImg / kKronThreads;
   float vb[kIt], va[kIt], vs[kIt];
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
-    const int e = it * 256 + tid;
+    const int e = it * kKronThreads + tid;
     vb[it] = fb[e];
     va[it] = fa[e];
     vs[it] = chan_scale ? chan_scale[e] : 1.0f;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // after the tables (loads complete in order, so the image writes below
   // wait for the tables only), and its memory latency runs under the image
   // set-up.  The index is clamped; a wavefront with no token never uses it.
-  const int64_t tfirst = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t tfirst = (int64_t)blockIdx.x * kKronWaves + wave;
   uint4 xpre[2];
   {
     const __half *src = x + min(tfirst, T - 1) * ldx + 64 * l16 + 16 * kg;
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
-    const int e = it * 256 + tid;
+    const int e = it * kKronThreads + tid;
     const int R = e >> 6, C = e & 63, c16 = C & 15;
     {
       const int v = 4 * (R & 15) + (C >> 4), l = 16 * (R >> 4) + 4 * (c16 & 3) + (c16 >> 2);
@@ -214,7 +218,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sym_scale(amax, clip, s, inv);
     if (!live) return;
     int csum = 0;
-    uint8_t *qrow = q + t0 * 2048;
+    // the codes go through the wavefront's LDS row, then out in 16-byte stores
+    uint8_t *qs = qst[wave];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -230,8 +235,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             bits |= (uint32_t)(cd & 0xF) << (4 * r);
           }
           // Y[i][j0 .. j0+3], i = 16bi + l16, j0 = 16bj + 4kg: byte (64 i + j0) / 2
-          *reinterpret_cast<uint16_t *>(qrow + 32 * (16 * bi + l16) + 8 * bj + 2 * kg) = (uint16_t)bits;
+          *reinterpret_cast<uint16_t *>(qs + 32 * (16 * bi + l16) + 8 * bj + 2 * kg) = (uint16_t)bits;
         }
+    wave_lds_sync();
+    {
+      const uint4 *src = reinterpret_cast<const uint4 *>(qs);
+      uint4 *dst = reinterpret_cast<uint4 *>(q + t0 * 2048);
+      const uint4 c0 = src[lane], c1 = src[64 + lane];
+      dst[lane] = c0;
+      dst[64 + lane] = c1;
+    }
+    wave_lds_sync();  // the row is free again for the next token
     if (code_sum) csum = wave_sum(csum);
     if (lane == 0) {
       scale[t0] = s;
@@ -242,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // prefetch above and its use (a guarded use lets the compiler sink the
   // prefetch past the barrier); a wavefront past the last token works on
   // that token and stores nothing.
-  const int64_t stride = (int64_t)gridDim.x * 4;
+  const int64_t stride = (int64_t)gridDim.x * kKronWaves;
   const int ntok = tfirst < T ? (int)((T - 1 - tfirst) / stride) + 1 : 1;  // for progress_prio
   progress_prio(0, ntok);
   token(min(tfirst, T - 1), true, tfirst < T);
@@ -256,9 +270,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 hipError_t launch_kron64(const void *x, int64_t T, int64_t ldx, const float *fa, const float *fb,
                          const float *chan_scale, bool divide, float clip, uint8_t *q, float *scale,
                          int32_t *code_sum, hipStream_t st) {
-  // two workgroups of 4 wavefronts per CU, one token per wavefront at a time
-  const int64_t wgs = (T + 3) / 4;
-  const dim3 g((unsigned)(wgs < 512 ? wgs : 512)), b(256);
+  // one workgroup per CU, one token per wavefront at a time
+  const int64_t wgs = (T + kKronWaves - 1) / kKronWaves;
+  const dim3 g((unsigned)(wgs < 256 ? wgs : 256)), b(kKronThreads);
   const __half *xh = (const __half *)x;
   if (divide)
     kron64_mfma<true><<<g, b, 0, st>>>(xh, T, ldx, fa, fb, chan_scale, clip, q, scale, code_sum);
