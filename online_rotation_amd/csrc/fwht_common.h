@@ -47,9 +47,9 @@ __device__ __forceinline__ v16f mfma16(uint4 a, uint4 b, v16f c) {
 // Split eight fp32 values into fp16 hi (nearest) and lo (remainder) operands.
 // hi is one v_cvt_pk_f16_f32 per pair (round to nearest even); the remainder
 // f - hi is exact in fp32 and comes from one mixed-precision fma per value
-// (v_fma_mix_f32: the fp16 operand widened inside the fma), then one pair
-// conversion.  `neg1` is -1.0 held in a register the compiler cannot see
-// through: with a literal -1 the fma folds to a subtraction that needs a
+// (the fp16 operand widened inside the fma) that rounds it to fp16 in the
+// same instruction.  `neg1` is -1.0 held in a register the compiler cannot
+// see through: with a literal -1 the fma folds to a subtraction that needs a
 // separate fp16 -> fp32 conversion of hi.
 __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo, float neg1) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -58,9 +58,11 @@ __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo, flo
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const h2 ab = __builtin_convertvector((f2){f[2 * j], f[2 * j + 1]}, h2);
-    const float ra = __builtin_fmaf((float)ab.x, neg1, f[2 * j]);
-    const float rb = __builtin_fmaf((float)ab.y, neg1, f[2 * j + 1]);
-    const h2 lr = __builtin_convertvector((f2){ra, rb}, h2);
+    // each remainder rounded to fp16 straight from the fma (v_fma_mixlo /
+    // v_fma_mixhi write the two halves of one register)
+    h2 lr;
+    lr.x = (_Float16)__builtin_fmaf((float)ab.x, neg1, f[2 * j]);
+    lr.y = (_Float16)__builtin_fmaf((float)ab.y, neg1, f[2 * j + 1]);
     __builtin_memcpy(&h[j], &ab, 4);
     __builtin_memcpy(&l[j], &lr, 4);
   }
@@ -68,8 +70,7 @@ __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo, flo
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// max over the wave of values below 2^24 (exact as floats)
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return (uint32_t)wave_max((float)v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_max_bits(v); }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -186,21 +187,32 @@ __device__ __forceinline__ FwhtOut fwht_token(const v4w (&raw)[8], v4w *st, cons
     // with e the fp16 exponent field of max|x|, so |P * 2^sx| < 2^15.
     uint32_t mx = 0;
     {
-      u16x2 m2 = {0, 0};
+      // max |x| as max(max x, -min x): three-input packed fp16 maximum /
+      // minimum over the raw pairs, two chains each (a NaN carries through
+      // and, like an infinity, gives exponent field 31)
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      h2 v[32];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint32_t d[4] = {mop[rb][kc].x, mop[rb][kc].y, mop[rb][kc].z, mop[rb][kc].w};
+        for (int kc = 0; kc < 4; ++kc) __builtin_memcpy(&v[16 * rb + 4 * kc], &mop[rb][kc], 16);
+      h2 hx[2], hn[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u16x2 v;
-            const uint32_t dm = d[i] & 0x7FFF7FFFu;
-            __builtin_memcpy(&v, &dm, 4);
-            m2 = __builtin_elementwise_max(m2, v);
-          }
+      for (int c = 0; c < 2; ++c) {
+        hx[c] = hn[c] = v[16 * c];
+#pragma unroll
+        for (int i = 1; i < 16; i += 2) {
+          const int j = 16 * c + i;
+          const int k = i + 1 < 16 ? j + 1 : j;
+          hx[c] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(hx[c], v[j]), v[k]);
+          hn[c] = __builtin_elementwise_minimum(__builtin_elementwise_minimum(hn[c], v[j]), v[k]);
         }
-      mx = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+      }
+      const h2 m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(hx[0], hx[1]),
+                                                 -__builtin_elementwise_minimum(hn[0], hn[1]));
+      uint32_t mb;
+      __builtin_memcpy(&mb, &m, 4);
+      mx = wave_max_u32(max(mb & 0x7FFFu, (mb >> 16) & 0x7FFFu));
     }
     float neg1 = -1.0f;
     asm volatile("" : "+v"(neg1));
@@ -259,7 +271,7 @@ __device__ __forceinline__ FwhtOut fwht_token(const v4w (&raw)[8], v4w *st, cons
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][j][r]));
-  amax = wave_max(amax) * nrm;
+  amax = __uint_as_float(wave_max_bits(__float_as_uint(amax))) * nrm;  // amax >= 0
   float s, inv;
   sym_scale(amax, clip, s, inv);
   const float invn = inv * nrm;

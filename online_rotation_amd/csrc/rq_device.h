@@ -82,6 +82,19 @@ __device__ __forceinline__ int wave_scan_dpp(int x) {
   x += RQ_DPP(0, x, 0x143, 0xC);  // row_bcast:31 into rows 2, 3
   return x;
 }
+// max over the wave of 32-bit patterns compared as unsigned (for floats
+// that are >= 0 this is their max: a NaN, the largest pattern, would
+// win); each stage is one DPP max (the identity 0 fills lanes without a
+// source), where the float form needs a move and two max per stage
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0xB1, 0xF));
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0x4E, 0xF));
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0x141, 0xF));
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0x140, 0xF));
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0x142, 0xA));
+  x = max(x, (uint32_t)RQ_DPP(0, (int)x, 0x143, 0xC));
+  return __builtin_amdgcn_readlane(x, 63);
+}
 #undef RQ_DPP
 
 // The wave's max / min / sum, in every lane (a scalar register).
