@@ -497,11 +497,15 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
     sload(s0, 0);
     if (G >= 2) sload(s1, 1);
     if (G >= 3) sload(s2, 2);
-    // the weight ring's prologue goes out behind the staging loads, so waiting
-    // for the latter below leaves it in flight
+    // Half the weight ring's prologue goes out behind the staging loads, so
+    // waiting for the latter below leaves it in flight; the other half once
+    // the stage is written.  With the whole ring ahead, the staging loads
+    // came back behind more of the launch's first burst of weight requests
+    // (whole ring 28.4-29.2 us at the QUIK decode shape, half 27.9-28.9,
+    // a quarter or three quarters no better than whole).
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
+    for (int s = 0; s < kD16 / 2; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     __builtin_amdgcn_sched_barrier(0);
     {
       const uint32_t ma = d16_magic(ka), mo = nk ? d16_magic(ko) : 0;
@@ -522,6 +526,8 @@ __global__ __launch_bounds__(512) void gemm_decode16(GemmArgs p, FuseArgs f) {
       if (G >= 2) sstore(s1, 1);
       if (G >= 3) sstore(s2, 2);
     }
+#pragma unroll
+    for (int s = kD16 / 2; s < kD16; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     if (tid < T) {
       sxl[tid] = vsx;
       zxl[tid] = p.zx ? vzx : 0;
