@@ -107,11 +107,15 @@ __global__ __launch_bounds__(512) void gemm_decode8(GemmArgs p, D8Args d) {
   {
     uint4 sv[4];
     sload(sv, 0);
+    // half the weight ring's prologue ahead of the staging wait, half after
+    // the stage is written (as in gemm_decode16)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < kD8Ring; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
+    for (int s = 0; s < kD8Ring / 2; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     __builtin_amdgcn_sched_barrier(0);
     sstore(sv, 0);
+#pragma unroll
+    for (int s = kD8Ring / 2; s < kD8Ring; ++s) rb[s] = *reinterpret_cast<const uint4 *>(src(min(s, L - 1)));
     // x_out rows, once (the outlier steps read them)
     if (d.nk) {
       const uint32_t ko = (uint32_t)p.n_out / 8, no = T * ko;
