@@ -329,7 +329,9 @@ rq_status rq_w8a8_linear(const uint8_t *qx, const float *sx, const int32_t *zx, 
                          const void *w_out, int32_t n_out, void *y, int64_t ldy, void *stream);
 
 /* rq_w8a8_gemm_i32 -- the raw INT32 accumulator of one-byte codes,
- * acc[t][n] = sum_k qx[t][k]*qw[n][k], for bit-exact tests.  x_unsigned != 0:
+ * acc[t][n] = sum_k qx[t][k]*qw[n][k] (the integer product of QUIK-8B's
+ * layers: QUIK blog, experiments part 2, on the kernels of "QUIK量化" part 4),
+ * for bit-exact tests.  x_unsigned != 0:
  * qx codes are unsigned [0, 255] and w_rowsum (int32 [N], the row sums of qw)
  * is required; otherwise signed.  acc int32 [T, ldacc], ldacc >= N;
  * K % 64 == 0, K <= 32768. */
@@ -337,9 +339,12 @@ rq_status rq_w8a8_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int
                            const uint8_t *qw, const int32_t *w_rowsum, int64_t N, int32_t *acc,
                            int64_t ldacc, void *stream);
 
-/* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k],
- * for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
- * otherwise signed.  acc int32 [T, ldacc], ldacc >= N. */
+/* rq_w4a4_gemm_i32 -- the raw INT32 accumulator acc[t][n] = sum_k qx[t][k]*qw[n][k]
+ * (the INT4 x INT4 product with INT32 accumulation: QUIK blog, "QUIK量化"
+ * part 4), for bit-exact tests.  x_unsigned != 0: qx codes are unsigned [0, 15];
+ * otherwise signed.  qx uint8 [T, K/2], qw uint8 [N, K/2] (both 16-byte
+ * aligned), acc int32 [T, ldacc], ldacc >= N.  K % 64 == 0, 0 < K <= 65536,
+ * N >= 1; the same status codes as rq_w4a4_linear.  T == 0 is a no-op. */
 rq_status rq_w4a4_gemm_i32(const uint8_t *qx, int32_t x_unsigned, int64_t T, int64_t K,
                            const uint8_t *qw, int64_t N, int32_t *acc, int64_t ldacc,
                            void *stream);
