@@ -23,8 +23,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# MFMA accumulators in VGPRs (no AGPR copies) where a kernel fits in 256
-# VGPRs; gemm_ra and kron64_mfma keep their accumulators in AGPRs instead.
+# MFMA accumulators in VGPRs (no AGPR copies) for the kernels listed here.
+# gemm_ra.hip and kron.hip are built without the flag; held to 256 registers
+# by their two-wavefronts-per-SIMD bound, they get VGPR accumulators from the
+# compiler as well (their code uses no AGPRs).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {"rotate_quant.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM, "gemm_decode.hip": VGPR_FORM,
                "gemm_decode8.hip": VGPR_FORM}
