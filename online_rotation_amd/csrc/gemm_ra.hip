@@ -21,10 +21,10 @@
 //     as int8, and the wavefronts read MFMA-ready fragments: 16 KB of reads
 //     and 4 KB of writes per k slice and CU, about half the LDS rate.
 // A k-step is 128 codes (64 bytes per row), four groups of 8 MFMAs.  Global
-// loads run kRaD steps ahead in a register ring; the B tile in LDS is
-// triple-buffered with one barrier per step, placed so that no fragment
-// read waits on it: every MFMA group's fragments are read one group ahead,
-// across step boundaries too.  Every step issues the same loads and stores
+// loads run ahead in register rings and the B tile goes through 3 or 4 LDS
+// buffers, with a barrier every step or every other step (the two schedules
+// below), placed so that no fragment read waits on it: every MFMA group's
+// fragments are read one group ahead, across step boundaries too.  Every step issues the same loads and stores
 // with no branch around them (row indices are clamped into the matrices,
 // and steps past the end re-load the last one), so the compiler waits only
 // for the load group it needs next.
@@ -38,12 +38,18 @@ namespace rq {
 namespace {
 
 constexpr int kRaBM = 256, kRaBN = 128;
-constexpr int kRaD = 3;                   // global load ring depth (k-steps)
-constexpr int kRaNB = 3;                  // B buffers in LDS
-constexpr int kRaU = kRaD % kRaNB == 0 ? kRaD : kRaD * kRaNB;  // unroll: slot and buffer indices static
+// Two schedules.  Barrier every other step (int4 codes without zero points
+// or outliers): A ring 2 steps deep, B ring 4, B in 4 LDS buffers.  Barrier
+// every step (8-bit codes, and the QUIK form, where the other schedule
+// measured slower): one ring of 3 steps for both, 3 buffers.  The unroll
+// keeps every slot and buffer index static.
+constexpr int kRaDA = 2, kRaDB = 4, kRaNB = 4, kRaU4 = 4;
+constexpr int kRaD3 = 3, kRaNB3 = 3, kRaU3 = 3;
 constexpr int kRaRow = 128;               // LDS bytes per B row and k-step (int8)
 constexpr int kRaBuf = kRaBN * kRaRow;    // one buffer: 16 KB
-static_assert(kRaNB * kRaBuf >= (kRaBM + kRaBN) * 128, "outlier tiles must fit the B buffers");
+static_assert(kRaNB3 * kRaBuf >= (kRaBM + kRaBN) * 128, "outlier tiles must fit the B buffers");
+static_assert(kRaU4 % kRaDA == 0 && kRaU4 % kRaDB == 0 && kRaU4 % kRaNB == 0, "unroll");
+static_assert(kRaU3 % kRaD3 == 0 && kRaU3 % kRaNB3 == 0, "unroll");
 
 // Widened slot s (16 bytes) of LDS row r sits at s ^ ((r >> 1) & 7): the 16
 // rows that a group of 16 lanes reads (one row per lane) or writes (four
@@ -86,7 +92,11 @@ template <bool XU, int MODE, int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   constexpr int kGroups = BITS == 8 ? 2 : 4;  // MFMA groups per k-step
-  __shared__ __align__(16) uint8_t Bs[kRaNB * kRaBuf];
+  constexpr bool kHalf = BITS == 4 && MODE != 2;  // a barrier every other step
+  constexpr int kNB = kHalf ? kRaNB : kRaNB3;
+  constexpr int kDA = kHalf ? kRaDA : kRaD3, kDB = kHalf ? kRaDB : kRaD3;
+  constexpr int kRaU = kHalf ? kRaU4 : kRaU3;
+  __shared__ __align__(16) uint8_t Bs[kNB * kRaBuf];
   // The tile's dequantization vectors (sx, zx per row; sw, rowsum per
   // column), staged in LDS at the start so that the epilogue does not wait on
   // global loads after the k loop (modes 1 and 2).
@@ -119,20 +129,23 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) rs[c] = l32 * kRaRow + (((kGroups * g + c) ^ ((l32 >> 1) & 7)) << 4);
 
-  uint4 ra[kRaD][4], rb[kRaD][2];
-  auto gload = [&](int s, int kb) {
-    const int64_t o = (int64_t)kb * 64;
+  // A(k) in A slot k % kDA, B(k) in B slot k % kDB
+  uint4 ra[kDA][4], rb[kDB][2];
+  auto gload_a = [&](int s, int k) {
+    const int64_t o = (int64_t)k * 64;
     ra[s][0] = ldg16(ap0 + o);
     ra[s][1] = ldg16(ap0 + o + 16);
     ra[s][2] = ldg16(ap1 + o);
     ra[s][3] = ldg16(ap1 + o + 16);
+  };
+  auto gload_b = [&](int s, int k) {
+    const int64_t o = (int64_t)k * 64;
     rb[s][0] = ldg16(bp0 + o);
     rb[s][1] = ldg16(bp1 + o);
   };
-  // half h of the B staging of slot s, widened, into LDS buffer buf
-  auto bstore = [&](int buf, int s, int h) {
+  // half h of a B staging chunk w, widened, into LDS buffer buf
+  auto bstore_w = [&](int buf, const uint4 &w, int h) {
     uint8_t *B = Bs + buf * kRaBuf;
-    const uint4 &w = rb[s][h];
     if (BITS == 8) {
       *reinterpret_cast<uint4 *>(B + (h ? ws2 : ws0)) = w;
     } else {
@@ -140,6 +153,7 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       *reinterpret_cast<v4i *>(B + (h ? ws3 : ws1)) = widen_signed(w.z, w.w);
     }
   };
+  auto bstore = [&](int buf, int s, int h) { bstore_w(buf, rb[s][h], h); };
   v4i bf[2][4];  // B fragments, double-buffered across MFMA groups
   auto bread = [&](int f, int buf, int c) {
     const uint8_t *B = Bs + buf * kRaBuf;
@@ -199,11 +213,30 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     vsw = p.sw[sc];
     vrs = rsp[sc];
   }
-  // prologue: steps 0 .. kRaD-1 in flight, B(0) into buffer 0, its first fragments
+  // prologue.  Every other step: B(0 .. 3) and A(0 .. 1) in flight; B(0),
+  // B(1) into buffers 0, 1 and their slots refilled with B(4), B(5).  Every
+  // step: steps 0 .. 2 in flight, B(0) into buffer 0.  Then B(0)'s first
+  // fragments.
+  if (kHalf) {
 #pragma unroll
-  for (int s = 0; s < kRaD; ++s) gload(s, min(s, last));
-  bstore(0, 0, 0);
-  bstore(0, 0, 1);
+    for (int s = 0; s < kDB; ++s) gload_b(s, min(s, last));
+#pragma unroll
+    for (int s = 0; s < kDA; ++s) gload_a(s, min(s, last));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      bstore(k, k, 0);
+      bstore(k, k, 1);
+      gload_b(k, min(k + kDB, last));
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < kDA; ++s) {
+      gload_a(s, min(s, last));
+      gload_b(s, min(s, last));
+    }
+    bstore(0, 0, 0);
+    bstore(0, 0, 1);
+  }
   if (MODE != 0) {
     s_sx[tid] = vsx;
     s_zx[tid] = need_zx ? vzx : 0;
@@ -215,20 +248,33 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   __syncthreads();
   bread(0, 0, 0);
 
-  // Step kb: A(kb) in load slot kb % kRaD, B(kb) in LDS buffer kb % kRaNB
-  // with MFMA group 0's fragments already in registers, B(kb+1) in load slot
-  // (kb+1) % kRaD.  Each of the four MFMA groups reads the next group's
-  // fragments first.  B(kb+1) is stored into buffer (kb+1) % kRaNB during
-  // groups 0 and 1 (8-bit: group 0), the barrier follows, before step kb+1's
-  // first fragments are read in the last group.  With three buffers, buffer
-  // (kb+1) % 3 was last read in step kb-2, before every wave passed step
+  // Barrier every other step.  Step kb: A(kb) in A slot kb % 2, B(kb+2) in B slot
+  // (kb+2) % 4 (refilled with B(kb+6) once stored), B(kb) in
+  // LDS buffer kb % 4 with MFMA group 0's fragments already in registers,
+  // B(kb+1) in buffer (kb+1) % 4.  Each of the four MFMA groups reads the
+  // next group's fragments first.  B(kb+2) is stored into buffer (kb+2) % 4
+  // during groups 0 and 1, and only odd steps end with a barrier (in group
+  // 3, before step kb+1's first fragments are read):
+  //   - B(kb+1) is read from step kb's group 3 on; it was stored in step
+  //     kb-1, and one of steps kb-1, kb holds a barrier after that store and
+  //     before group 3 (kb-1 odd: its own; kb odd: step kb's, ahead of the
+  //     read);
+  //   - buffer (kb+2) % 4 last held B(kb-2), whose last read is in step
+  //     kb-2's group 2; one of steps kb-2, kb-1 ends with a barrier.
+  // A barrier every other step lets the wavefronts drift apart for two steps
+  // between meetings.  A(kb+2) is requested in step kb's group 3.
+  // Barrier every step: A(kb) and B(kb) in load slot kb % 3; B(kb+1), from
+  // slot (kb+1) % 3, is stored into buffer (kb+1) % 3 during groups 0 and 1
+  // (8-bit: group 0), and every step's group 3 (8-bit: group 1) holds a
+  // barrier; buffer (kb+1) % 3 was last read in step kb-2, before step
   // kb-1's barrier.
   auto steps = [&](int kb0, auto tail) {
 #pragma unroll
     for (int v = 0; v < kRaU; ++v) {
       const int kb = kb0 + v;
-      const int u = v % kRaD, us = (v + 1) % kRaD;     // load slots of steps kb, kb+1
-      const int ub = v % kRaNB, nb = (v + 1) % kRaNB;  // LDS buffers of steps kb, kb+1
+      const int u = v % kDA, us = (v + 1) % kDB;       // A slot of kb; (8-bit) B slot of kb+1
+      const int ub = v % kNB, nb = (v + 1) % kNB;      // LDS buffers of steps kb, kb+1
+      const int nb2 = (v + 2) % kNB, ub2 = (v + 2) % kDB;  // int4: buffer and B slot of B(kb+2)
       const bool live = !decltype(tail)::value || kb < nsteps;
       v4i aw[2];
       if (BITS == 8) {
@@ -243,11 +289,13 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
         __syncthreads();
         awiden(u, 1, aw);
         __builtin_amdgcn_sched_barrier(0);
-        gload(u, min(kb + kRaD, last));
+        gload_a(u, min(kb + kDA, last));
+        gload_b(u, min(kb + kDA, last));
         bread(0, nb, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (live) mfma8(aw, 1);
         __builtin_amdgcn_sched_barrier(0);
+        if (decltype(tail)::value && kb + 1 >= nsteps) break;
         continue;
       }
       // (sched_barrier: keep each group's fragment reads ahead of its MFMAs;
@@ -257,14 +305,20 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       __builtin_amdgcn_sched_barrier(0);
       awiden(u, 0, aw);
       if (live) mfma8(aw, 0);
-      bstore(nb, us, 0);
+      if (kHalf) bstore(nb2, ub2, 0);
+      else bstore(nb, us, 0);
       __builtin_amdgcn_sched_barrier(0);
       // group 1
       bread(0, ub, 2);
       __builtin_amdgcn_sched_barrier(0);
       awiden(u, 1, aw);
       if (live) mfma8(aw, 1);
-      bstore(nb, us, 1);
+      if (kHalf) {
+        bstore(nb2, ub2, 1);
+        gload_b(ub2, min(kb + 2 + kDB, last));
+      } else {
+        bstore(nb, us, 1);
+      }
       // group 2
       bread(1, ub, 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -272,24 +326,28 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       if (live) mfma8(aw, 0);
       __builtin_amdgcn_sched_barrier(0);
       // group 3: A(kb) is fully widened after this, so its slot is refilled.
-      // The barrier sits here, a whole MFMA group after the last LDS stores
-      // of B(kb+1): placed before group 2 it waited for those stores to
-      // land with the matrix pipe idle (measured 1-2 us more at T = 2048,
-      // K = N = 4096).
+      // The barrier (odd steps) sits here, a whole MFMA group after the last
+      // LDS stores of B(kb+2): placed before group 2 it waited for those
+      // stores to land with the matrix pipe idle (measured 1-2 us more at
+      // T = 2048, K = N = 4096).
       awiden(u, 3, aw);
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      gload(u, min(kb + kRaD, last));
+      if (!kHalf || (v & 1)) __syncthreads();
+      gload_a(u, min(kb + kDA, last));
+      if (!kHalf) gload_b(u, min(kb + kDA, last));
       bread(0, nb, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (live) mfma8(aw, 1);
       __builtin_amdgcn_sched_barrier(0);
+      // the tail group stops after the last step (a uniform exit, so every
+      // wavefront meets the same barriers)
+      if (decltype(tail)::value && kb + 1 >= nsteps) break;
     }
   };
-  // Whole groups of kRaU steps in the loop; a final partial group (steps
-  // past the end only load and store) outside it, so that no branch sits
-  // inside the loop (a branch there makes the compiler copy the load ring
-  // at the back edge, waiting for every load in flight).
+  // Whole groups of kRaU steps in the loop; a final partial group outside
+  // it, so that no branch sits inside the loop (a branch there makes the
+  // compiler copy the load ring at the back edge, waiting for every load in
+  // flight).
   int kb0 = 0;
   for (; kb0 + kRaU <= nsteps; kb0 += kRaU) steps(kb0, std::false_type());
   if (kb0 < nsteps) steps(kb0, std::true_type());
