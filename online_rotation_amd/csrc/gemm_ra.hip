@@ -102,7 +102,8 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   // global loads after the k loop (modes 1 and 2).
   __shared__ float s_sx[kRaBM], s_sw[kRaBN];
   __shared__ int32_t s_zx[kRaBM], s_rs[kRaBN];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5, l32 = lane & 31;
   int tm, tn;
   ra_map_tile(blockIdx.x, nt_m, nt_n, tm, tn);
@@ -352,6 +353,11 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   for (; kb0 + kRaU <= nsteps; kb0 += kRaU) steps(kb0, std::false_type());
   if (kb0 < nsteps) steps(kb0, std::true_type());
 
+  // The epilogue's lane indices are made again here (the lane id from
+  // mbcnt) rather than carried across the k loop, where they would hold
+  // registers (spilled to scratch when the loop fills the register file).
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int etid = wave * 64 + elane, eg = elane >> 5, el32 = elane & 31;
   // Epilogue.  32x32 accumulator layout: lane l, register r holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
   constexpr int kShift = BITS == 8 ? 0 : (XU ? 4 : 8);
@@ -364,11 +370,11 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t gn = col0 + 32 * j + l32;
+        const int64_t gn = col0 + 32 * j + el32;
         const int32_t rsj = kZoff ? p.rowsum[min(gn, p.N - 1)] : 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * eg + (r & 3);
           if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = (acc[i][j][r] >> kShift) + kZoff * rsj;
         }
       }
@@ -378,15 +384,15 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   int32_t rsn[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    swn[j] = s_sw[32 * j + l32];
-    rsn[j] = s_rs[32 * j + l32];
+    swn[j] = s_sw[32 * j + el32];
+    rsn[j] = s_rs[32 * j + el32];
   }
   v16f f[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int lr = wave * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int lr = wave * 64 + 32 * i + 8 * (r >> 2) + 4 * eg + (r & 3);
       const float sxm = s_sx[lr];
       const int32_t zxm = s_zx[lr] - kZoff;
 #pragma unroll
@@ -413,24 +419,24 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     auto cload = [&](int c) {  // columns past n_out are clamped and never multiplied
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
+        const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
         px[i] = *reinterpret_cast<const uint4 *>(p.xo + min(m0 + row, p.T - 1) * p.n_out + col);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
+        const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
         pw[i] = *reinterpret_cast<const uint4 *>(p.wo + min(n0 + row, p.N - 1) * p.n_out + col);
       }
     };
     auto cstore = [&]() {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 2, sg = idx & 3;
+        const int idx = etid + 256 * i, row = idx >> 2, sg = idx & 3;
         *reinterpret_cast<uint4 *>(Xs + row * 128 + ((sg ^ (row & 7)) << 4)) = px[i];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 2, sg = idx & 3;
+        const int idx = etid + 256 * i, row = idx >> 2, sg = idx & 3;
         *reinterpret_cast<uint4 *>(Ws + row * 128 + ((sg ^ (row & 7)) << 4)) = pw[i];
       }
     };
@@ -445,14 +451,14 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
         v8h av[2], bv[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int r = wave * 64 + 32 * i + l32;
-          const uint4 t = *reinterpret_cast<const uint4 *>(Xs + r * 128 + (((2 * kk + g) ^ (r & 7)) << 4));
+          const int r = wave * 64 + 32 * i + el32;
+          const uint4 t = *reinterpret_cast<const uint4 *>(Xs + r * 128 + (((2 * kk + eg) ^ (r & 7)) << 4));
           __builtin_memcpy(&av[i], &t, 16);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = 32 * j + l32;
-          const uint4 t = *reinterpret_cast<const uint4 *>(Ws + r * 128 + (((2 * kk + g) ^ (r & 7)) << 4));
+          const int r = 32 * j + el32;
+          const uint4 t = *reinterpret_cast<const uint4 *>(Ws + r * 128 + (((2 * kk + eg) ^ (r & 7)) << 4));
           __builtin_memcpy(&bv[j], &t, 16);
         }
 #pragma unroll
@@ -481,13 +487,13 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rr = 8 * (r >> 2) + 4 * g + (r & 3);
-          *reinterpret_cast<__half *>(W + rr * kP + 2 * (32 * j + l32)) = __float2half_rn(f[i][j][r]);
+          const int rr = 8 * (r >> 2) + 4 * eg + (r & 3);
+          *reinterpret_cast<__half *>(W + rr * kP + 2 * (32 * j + el32)) = __float2half_rn(f[i][j][r]);
         }
       wave_lds_sync();
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int rr = 4 * it + (lane >> 4), cc = lane & 15;
+        const int rr = 4 * it + (elane >> 4), cc = elane & 15;
         const uint4 v = *reinterpret_cast<const uint4 *>(W + rr * kP + 16 * cc);
         const int64_t gm = row0 + 32 * i + rr, gn = col0 + 8 * cc;
         if (gm < p.T) {
@@ -510,10 +516,10 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t gn = col0 + 32 * j + l32;
+      const int64_t gn = col0 + 32 * j + el32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int64_t gm = row0 + 32 * i + 8 * (r >> 2) + 4 * eg + (r & 3);
         if (gm < p.T && gn < p.N) out[gm * p.ldo + gn] = __float2half_rn(f[i][j][r]);
       }
     }
