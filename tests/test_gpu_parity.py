@@ -187,7 +187,11 @@ GEMM_SHAPES = [(1, 1, 64), (16, 256, 256), (200, 130, 192), (300, 257, 4096), (1
                (32, 513, 4096), (3, 1000, 7936), (17, 96, 128), (31, 33, 384),
                (16, 100, 8192), (16, 70, 8320), (9, 65, 4608), (4, 16500, 128), (16, 16400, 6144),
                (5, 300, 16384), (2, 40, 32768), (3, 70, 65536), (300, 130, 65536),
-               (24, 100, 8192), (32, 16500, 1024), (30, 300, 16384), (21, 2000, 7936)]
+               (24, 100, 8192), (32, 16500, 1024), (30, 300, 16384), (21, 2000, 7936),
+               # the 256-row kernel's k-step counts of 1, 2, 3, 5, 6, 7 and 9 (K / 128): partial
+               # last groups of its 4-step schedule, an odd last step without its barrier
+               (256, 130, 128), (300, 200, 256), (257, 129, 384), (300, 257, 640), (260, 64, 768),
+               (512, 300, 896), (270, 100, 1152)]
 
 
 @pytest.mark.parametrize("unsigned_x", [False, True])
@@ -203,7 +207,8 @@ def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
 
 
 @pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032),
-                                   (7, 190, 3968), (24, 130, 3968), (32, 300, 8192)])
+                                   (7, 190, 3968), (24, 130, 3968), (32, 300, 8192),
+                                   (256, 128, 128), (300, 257, 384), (260, 130, 640), (513, 100, 896)])
 def test_linear_epilogue_on_oracle_codes(T, N, K):
     note(f"[w4a4_linear] T={T} N={N} K={K}")
     rng = np.random.default_rng(K + T)
@@ -264,6 +269,24 @@ def test_mixed_epilogue_on_oracle_codes(T, N, n_out, asym):
     ref = o.dequant_mixed(o.int_gemm(qx, qw), sx, zx if asym else np.zeros(T, np.int32), sw, rowsum,
                           xo, wo)
     check_y(host(y), ref)
+
+
+@pytest.mark.parametrize("K", [128, 384, 1152, 1280])
+def test_mixed_epilogue_step_counts(K):
+    """The QUIK form of the 256-row kernel (a barrier every step, groups of 3
+    steps) at k-step counts of 1, 3, 9 and 10: whole and partial last groups."""
+    T, N, n_out = 300, 200, 32
+    note(f"[mixed_linear steps] T={T} N={N} K={K} n_out={n_out}")
+    rng = np.random.default_rng(K)
+    qx = rng.integers(0, 16, (T, K)); zx = rng.integers(0, 16, T).astype(np.int32)
+    qw = rng.integers(-7, 8, (N, K)); rowsum = qw.sum(axis=1).astype(np.int32)
+    sx = rng.uniform(0.01, 2, T).astype(np.float32); sw = rng.uniform(1e-4, 5e-3, N).astype(np.float32)
+    xo = (rng.standard_normal((T, n_out)) * 40).astype(np.float16)
+    wo = (rng.standard_normal((N, n_out)) * 0.02).astype(np.float16)
+    y = rq.rq_mixed_outlier_linear(dev(o.pack_int4(qx)), dev(sx), dev(zx), dev(o.pack_int4(qw)), dev(sw),
+                                   dev(rowsum), dev(xo), dev(wo))
+    torch.cuda.synchronize()
+    check_y(host(y), o.dequant_mixed(o.int_gemm(qx, qw), sx, zx, sw, rowsum, xo, wo))
 
 
 # ----------------------------------------------------------------------------- fused decode
