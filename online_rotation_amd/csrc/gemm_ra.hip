@@ -24,10 +24,11 @@
 // loads run ahead in register rings and the B tile goes through 3 or 4 LDS
 // buffers, with a barrier every step or every other step (the two schedules
 // below), placed so that no fragment read waits on it: every MFMA group's
-// fragments are read one group ahead, across step boundaries too.  Every step issues the same loads and stores
-// with no branch around them (row indices are clamped into the matrices,
-// and steps past the end re-load the last one), so the compiler waits only
-// for the load group it needs next.
+// fragments are read one group ahead, across step boundaries too.  Every
+// step issues the same loads and stores with no branch around them (row
+// indices are clamped into the matrices, and loads past the end re-load
+// the last step), so the compiler waits only for the load group it needs
+// next.
 #include "gemm_common.h"
 #include "rq_kernels.h"
 
@@ -249,9 +250,9 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
   __syncthreads();
   bread(0, 0, 0);
 
-  // Barrier every other step.  Step kb: A(kb) in A slot kb % 2, B(kb+2) in B slot
-  // (kb+2) % 4 (refilled with B(kb+6) once stored), B(kb) in
-  // LDS buffer kb % 4 with MFMA group 0's fragments already in registers,
+  // Barrier every other step.  Step kb: A(kb) in A slot kb % 2, B(kb+2) in
+  // B slot (kb+2) % 4 (refilled with B(kb+6) once stored), B(kb) in LDS
+  // buffer kb % 4 with MFMA group 0's fragments already in registers,
   // B(kb+1) in buffer (kb+1) % 4.  Each of the four MFMA groups reads the
   // next group's fragments first.  B(kb+2) is stored into buffer (kb+2) % 4
   // during groups 0 and 1, and only odd steps end with a barrier (in group
