@@ -206,6 +206,25 @@ def test_gemm_int32_bit_exact(T, N, K, unsigned_x):
     assert np.array_equal(host(acc), o.int_gemm(qx, qw))
 
 
+@pytest.mark.parametrize("K", [128, 384, 640, 896, 4096])
+def test_gemm_more_tiles_than_cus(K):
+    """264 tiles of the 256-row kernel, more than the 256 CUs (two workgroups
+    on some CUs), at 1, 3, 5, 7 and 32 k-steps: raw accumulators and the
+    symmetric epilogue."""
+    T, N = 2048, 4224
+    note(f"[gemm_i32 + w4a4_linear, 264 tiles] T={T} N={N} K={K}")
+    rng = np.random.default_rng(K + 1)
+    qx = rng.integers(-8, 8, (T, K)); qw = rng.integers(-8, 8, (N, K))
+    ref = o.int_gemm(qx, qw)
+    acc = rq.rq_w4a4_gemm_i32(dev(o.pack_int4(qx)), dev(o.pack_int4(qw)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), ref)
+    sx = rng.uniform(0.01, 0.1, T).astype(np.float32); sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    y = rq.rq_w4a4_linear(dev(o.pack_int4(qx)), dev(sx), dev(o.pack_int4(qw)), dev(sw))
+    torch.cuda.synchronize()
+    check_y(host(y), o.dequant_sym(ref, sx, sw))
+
+
 @pytest.mark.parametrize("T,N,K", [(16, 256, 256), (300, 257, 4096), (77, 130, 3968), (270, 100, 4032),
                                    (7, 190, 3968), (24, 130, 3968), (32, 300, 8192),
                                    (256, 128, 128), (300, 257, 384), (260, 130, 640), (513, 100, 896)])
