@@ -416,30 +416,37 @@ void gemm_ra(GemmArgs p, int nt_m, int nt_n) {
     // row in lane group g: segment 2kk + g.
     uint8_t *Xs = Bs, *Ws = Bs + kRaBM * 128;
     const int nch = (p.n_out + 31) / 32;
-    uint4 px[4], pw[2];
-    auto cload = [&](int c) {  // columns past n_out are clamped and never multiplied
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
-        px[i] = *reinterpret_cast<const uint4 *>(p.xo + min(m0 + row, p.T - 1) * p.n_out + col);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
-        pw[i] = *reinterpret_cast<const uint4 *>(p.wo + min(n0 + row, p.N - 1) * p.n_out + col);
-      }
+    // The staging values are named one by one (literal indices): as arrays
+    // filled in loops, the compiler moved them into LDS (24 KB per
+    // workgroup) before the loops were unrolled.
+    auto xo_at = [&](int c, int i) {  // columns past n_out are clamped and never multiplied
+      const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
+      return *reinterpret_cast<const uint4 *>(p.xo + min(m0 + row, p.T - 1) * p.n_out + col);
+    };
+    auto wo_at = [&](int c, int i) {
+      const int idx = etid + 256 * i, row = idx >> 2, col = min(32 * c + 8 * (idx & 3), p.n_out - 8);
+      return *reinterpret_cast<const uint4 *>(p.wo + min(n0 + row, p.N - 1) * p.n_out + col);
+    };
+    auto put = [&](uint8_t *base, int i, const uint4 &v) {
+      const int idx = etid + 256 * i, row = idx >> 2, sg = idx & 3;
+      *reinterpret_cast<uint4 *>(base + row * 128 + ((sg ^ (row & 7)) << 4)) = v;
+    };
+    uint4 px0, px1, px2, px3, pw0, pw1;
+    auto cload = [&](int c) {
+      px0 = xo_at(c, 0);
+      px1 = xo_at(c, 1);
+      px2 = xo_at(c, 2);
+      px3 = xo_at(c, 3);
+      pw0 = wo_at(c, 0);
+      pw1 = wo_at(c, 1);
     };
     auto cstore = [&]() {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = etid + 256 * i, row = idx >> 2, sg = idx & 3;
-        *reinterpret_cast<uint4 *>(Xs + row * 128 + ((sg ^ (row & 7)) << 4)) = px[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int idx = etid + 256 * i, row = idx >> 2, sg = idx & 3;
-        *reinterpret_cast<uint4 *>(Ws + row * 128 + ((sg ^ (row & 7)) << 4)) = pw[i];
-      }
+      put(Xs, 0, px0);
+      put(Xs, 1, px1);
+      put(Xs, 2, px2);
+      put(Xs, 3, px3);
+      put(Ws, 0, pw0);
+      put(Ws, 1, pw1);
     };
     cload(0);
     __syncthreads();  // every wave is done with the B buffers
